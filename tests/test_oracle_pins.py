@@ -1,0 +1,362 @@
+"""Pins for the CPU oracle: each test checks the oracle against something other
+than itself (values the pages print, closed forms, exact-rational
+arithmetic, brute force, library routines, invariants)."""
+import itertools
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import kvq_oracle as O
+from mixed_precision_kv_amd import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    rows = []
+    with open(os.path.join(GOLD, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+# ----------------------------------------------------------------- grids ---
+def test_code_bits_match_printed_values():
+    for L, printed, decimals in _golden("code_bits.txt"):
+        assert round(O.code_bits(int(L)), int(decimals)) == float(printed)
+
+
+def test_codes_per_word_table():
+    for L, n, W in _golden("codes_per_word.txt"):
+        L, n, W = int(L), int(n), int(W)
+        assert O.codes_per_word(L) == n
+        assert O.words_per_row(L, 128) == W
+    for L in range(3, 17):
+        n = O.codes_per_word(L)
+        assert L ** n <= 2 ** 32 < L ** (n + 1)
+
+
+# --------------------------------------------------------------- packing ---
+@pytest.mark.parametrize("L", [3, 4, 5, 6, 8])
+def test_pack_exhaustive_small(L):
+    """Every code triple: the word equals Python's own base-L parse of the
+    digit string (most significant digit first), and unpacks back."""
+    codes = np.array(list(itertools.product(range(L), repeat=3)), dtype=np.uint8)
+    w = O.pack_digits(codes, L)
+    ref = [int("".join(str(d) for d in row[::-1]), L) for row in codes]
+    assert w.tolist() == ref
+    assert np.array_equal(O.unpack_digits(w, L, 3), codes)
+
+
+@pytest.mark.parametrize("L", [3, 4, 5, 6, 8])
+def test_pack_full_word_and_rows(L):
+    rng = np.random.default_rng(L)
+    n = O.codes_per_word(L)
+    codes = rng.integers(0, L, size=(500, n), dtype=np.uint8)
+    codes[0] = L - 1                                 # largest word L^n - 1
+    w = O.pack_digits(codes, L)
+    assert int(w[0]) == L ** n - 1
+    ref = [sum(int(c) * L ** j for j, c in enumerate(row)) for row in codes]
+    assert w.tolist() == ref
+    # rows pack along D, columns along the slot axis: transposes of each other
+    c2 = rng.integers(0, L, size=(2 * n + 3, 2 * n + 3), dtype=np.uint8)
+    assert np.array_equal(O.pack_rows(c2, L), O.pack_cols(c2.T.copy(), L).T)
+    # padding digits are zero: the last row word only holds the tail codes
+    row = O.pack_rows(c2[:1], L)[0]
+    tail = c2[0, (len(row) - 1) * n:]
+    assert int(row[-1]) == sum(int(c) * L ** j for j, c in enumerate(tail))
+
+
+# ------------------------------------------------------------- quantizer ---
+def _f16_groups(rng, shape, scale=1.0):
+    return (rng.standard_normal(shape).astype(np.float32) * np.float32(scale)).astype(np.float16)
+
+
+def _rne(fr: Fraction) -> int:
+    fl = math.floor(fr)
+    rem = fr - fl
+    if rem > Fraction(1, 2):
+        return fl + 1
+    if rem < Fraction(1, 2):
+        return fl
+    return fl if fl % 2 == 0 else fl + 1
+
+
+@pytest.mark.parametrize("L,G", [(5, 32), (6, 32), (8, 64), (4, 128), (3, 32)])
+def test_quantizer_against_exact_rational(L, G):
+    """Codes equal exact-rational round-half-even of (x - z)/s clamped to the
+    grid, z is the exact group minimum, s is within one fp16 ulp of the exact
+    range/(L-1) (equal to its nearest fp16 in nearly all groups)."""
+    rng = np.random.default_rng(100 + L)
+    x = _f16_groups(rng, (400, G), scale=3.0)
+    x[0] = x[0, 0]                                   # constant group
+    x[1, 5] = np.float16(-0.0); x[1, 6] = np.float16(0.0)
+    codes, s16, z16 = O.quantize_groups(x, L)
+    exact_nearest = 0
+    for g in range(x.shape[0]):
+        xs = [Fraction(float(v)) for v in x[g]]
+        mn, mx = min(xs), max(xs)
+        assert Fraction(float(z16[g])) == mn
+        s = Fraction(float(s16[g]))
+        target = (mx - mn) / (L - 1)
+        ulp = Fraction(2) ** (math.frexp(float(max(s, target)) or 1.0)[1] - 11) if target else 0
+        assert abs(s - target) <= ulp
+        if float(np.float16(float(target))) == float(s16[g]):
+            exact_nearest += 1
+        for i, xv in enumerate(xs):
+            want = 0 if s == 0 else min(max(_rne((xv - mn) / s), 0), L - 1)
+            assert codes[g, i] == want, (g, i)
+    assert exact_nearest >= x.shape[0] - 2
+
+
+def test_signed_zero_total_order():
+    """-0 sorts below +0 (IEEE total order), whichever comes first."""
+    x = np.abs(np.linspace(0.5, 3.0, 32)).astype(np.float16)
+    x[3] = np.float16(0.0); x[9] = np.float16(-0.0)
+    _, _, z = O.quantize_groups(x[None], 6)
+    assert z.view(np.uint16)[0] == 0x8000
+    y = -x
+    y[3] = np.float16(0.0); y[9] = np.float16(-0.0)
+    codes, s, z = O.quantize_groups(y[None], 6)
+    assert codes[0, 3] == codes[0, 9] == 5                   # both zeros sit at the top code
+
+
+def test_top_code_saturates_when_scale_rounds_down():
+    """A subnormal fp16 scale can round far below range/(L-1); the top code is
+    then clamped to L-1 (the grid has L levels)."""
+    x = np.zeros((1, 32), np.float16)
+    x[0, 1] = np.float16(7 * 2.0 ** -24)                  # range 7 ulp, s32 = 1.4 ulp -> s = 1 ulp
+    codes, s16, z16 = O.quantize_groups(x, 6)
+    assert s16.view(np.uint16)[0] == 1
+    assert codes[0, 1] == 5 and codes[0, 0] == 0
+
+
+def _fp16_int(x16):
+    """fp16 values as exact integers in units of 2**-24 (every fp16 is one)."""
+    b = x16.view(np.uint16).astype(np.int64)
+    mag = b & 0x7FFF
+    e, m = mag >> 10, mag & 0x3FF
+    val = np.where(e == 0, m, (m | 0x400) << np.maximum(e - 1, 0))
+    return np.where(b & 0x8000, -val, val)
+
+
+@pytest.mark.parametrize("L,G", [(5, 32), (6, 32), (8, 64), (3, 32)])
+def test_quantizer_codes_exact_integer_bulk(L, G):
+    """Millions of values: codes equal round-half-even of the exact quotient
+    (x - z)/s computed in integers (all fp16 values are integer multiples of
+    2**-24), clamped to the grid."""
+    rng = np.random.default_rng(1000 + L)
+    x = _f16_groups(rng, ((1 << 22) // G, G))
+    x[:, :4] *= np.float16(10)
+    codes, s16, z16 = O.quantize_groups(x, L)
+    X, Z, S = _fp16_int(x), _fp16_int(z16)[:, None], _fp16_int(s16)[:, None]
+    num = X - Z
+    assert np.all(num >= 0) and np.all(S > 0)
+    q = num // S
+    r = num - q * S
+    up = (2 * r > S) | ((2 * r == S) & (q % 2 == 1))
+    want = np.minimum(q + up, L - 1)
+    assert np.array_equal(codes.astype(np.int64), want)
+
+
+@pytest.mark.parametrize("L,G", [(5, 32), (6, 32), (8, 64), (4, 128), (3, 32)])
+def test_quantizer_half_step(L, G):
+    """Round-trip error is at most half a step (plus the top-code saturation
+    when the fp16 scale rounded down)."""
+    rng = np.random.default_rng(7 + L)
+    x = _f16_groups(rng, (3000, G))
+    x[:, :4] *= np.float16(10)
+    codes, s16, z16 = O.quantize_groups(x, L)
+    xh = O.dequantize_groups(codes, s16, z16)
+    xf = x.astype(np.float64)
+    s = s16.astype(np.float64)[:, None]
+    rng_ = (xf.max(1) - xf.min(1))[:, None]
+    sat = np.maximum(0.0, rng_ - (L - 1) * s)
+    assert np.all(np.abs(xh - xf) <= np.maximum(s / 2 * (1 + 2 ** -20), sat + 1e-12))
+    assert np.all(sat <= (L - 1) * s * 2 ** -11 + 1e-12)
+    assert codes.max() <= L - 1
+
+
+def test_quantizer_grid_points_and_constant_group():
+    for L in (3, 4, 5, 6, 8):
+        c = np.arange(L, dtype=np.float32)
+        x = (np.float32(-1.0) + c * np.float32(0.25)).astype(np.float16)[None, :]
+        codes, s16, z16 = O.quantize_groups(x, L)
+        assert float(s16[0]) == 0.25 and float(z16[0]) == -1.0
+        assert codes[0].tolist() == list(range(L))
+        assert np.array_equal(O.dequantize_groups(codes, s16, z16)[0], x[0].astype(np.float64))
+    x = np.full((1, 32), np.float16(1.375))
+    codes, s16, z16 = O.quantize_groups(x, 6)
+    assert float(s16[0]) == 0.0 and codes.max() == 0
+    assert np.all(O.dequantize_groups(codes, s16, z16) == 1.375)
+
+
+def test_two_bit_textbook_quantizer():
+    """L = 4 is the textbook asymmetric 2-bit min/max quantizer: codes
+    round((x - min) / ((max - min)/3)) in {0,1,2,3}, min -> 0, max -> 3."""
+    rng = np.random.default_rng(3)
+    x = _f16_groups(rng, (2000, 32))
+    codes, s16, z16 = O.quantize_groups(x, 4)
+    xf = x.astype(np.float64)
+    assert np.all(codes[np.arange(2000), xf.argmin(1)] == 0)
+    assert np.all(codes[np.arange(2000), xf.argmax(1)] == 3)
+    ref = np.rint((xf - xf.min(1, keepdims=True)) / ((xf.max(1) - xf.min(1)) / 3)[:, None])
+    assert np.mean(codes == ref) > 0.999
+
+
+# ------------------------------------------------------------------ rank ---
+def test_rank_brute_force_with_ties():
+    rng = np.random.default_rng(11)
+    for T in (1, 2, 17, 300, 2048):
+        s = np.exp(rng.standard_normal((2, T)).astype(np.float32)).astype(np.float32)
+        if T > 10:
+            s[0, 3] = s[0, 7] = s[0, 9]              # ties
+            s[1, 1] = np.float32(0.0); s[1, 2] = np.float32(-0.0)   # equal values
+            s[1, 4] = s[1, 1]
+        r = O.rank_desc(s)
+        for b in range(2):
+            sb = s[b].astype(np.float64)
+            for t in range(T):
+                want = int(np.sum(sb > sb[t]) + np.sum(sb[:t] == sb[t]))
+                assert r[b, t] == want
+            assert sorted(r[b].tolist()) == list(range(T))
+
+
+def test_tiers_preserve_every_token():
+    rng = np.random.default_rng(5)
+    B, T, n_hi = 3, 1000, 371
+    s = rng.standard_normal((B, T)).astype(np.float32)
+    rank = O.rank_desc(s)
+    tokmap, counts, inv = O.tiers_and_slots(rank, n_hi)
+    for b in range(B):
+        assert tuple(counts[b]) == (n_hi, T - n_hi)
+        tier = tokmap[b] >> 31
+        slot = tokmap[b] & 0x7FFFFFFF
+        for p in (0, 1):
+            toks = np.nonzero(tier == p)[0]
+            assert np.array_equal(slot[toks], np.arange(len(toks)))   # token order
+            assert np.array_equal(inv[b][p], toks)
+        # the high tier holds exactly the n_hi best scores
+        assert s[b][tier == 0].min() >= s[b][tier == 1].max()
+
+
+# --------------------------------------------------------- running median ---
+def test_running_median_against_resort():
+    rng = np.random.default_rng(9)
+    for n0 in (1, 2, 5, 64):
+        pre = np.exp(rng.standard_normal(n0).astype(np.float32))
+        rm = O.RunningMedian(pre)
+        hist = [float(x) for x in pre]
+        for _ in range(40):
+            snew = float(np.exp(np.float32(rng.standard_normal())))
+            if rng.random() < 0.2:
+                snew = hist[rng.integers(len(hist))]          # exact tie with a prior score
+            med = float(np.median(np.array(hist, dtype=np.float64)))
+            tier = rm.decide_and_insert(snew)
+            assert tier == (0 if snew > med else 1)
+            hist.append(float(np.float32(snew)))
+
+
+# ------------------------------------------------------------- attention ---
+def _naive_attention(q, k, v, scale):
+    out = []
+    for qh in q:
+        sc = [scale * math.fsum(float(a) * float(b) for a, b in zip(qh, kt)) for kt in k]
+        m = max(sc)
+        w = [math.exp(x - m) for x in sc]
+        den = math.fsum(w)
+        out.append([math.fsum(wi * float(vt[d]) for wi, vt in zip(w, v)) / den for d in range(len(v[0]))])
+    return np.array(out)
+
+
+def test_attention_brute_force_and_closed_forms():
+    rng = np.random.default_rng(21)
+    Hg, N, D = 4, 9, 16
+    q = rng.standard_normal((Hg, D))
+    k = rng.standard_normal((N, D))
+    v = rng.standard_normal((N, D))
+    o = O.attention_fp64(q, k, v, 0.25)
+    assert np.allclose(o, _naive_attention(q, k, v, 0.25), rtol=1e-12, atol=1e-13)
+    # a single token: output is that token's value
+    assert np.allclose(O.attention_fp64(q, k[:1], v[:1], 0.3), np.repeat(v[:1], Hg, 0), rtol=0, atol=1e-15)
+    # identical keys: the mean of the values
+    kk = np.repeat(k[:1], N, 0)
+    assert np.allclose(O.attention_fp64(q, kk, v, 0.3), np.repeat(v.mean(0, keepdims=True), Hg, 0), atol=1e-14)
+    # token order does not matter
+    perm = rng.permutation(N)
+    assert np.allclose(O.attention_fp64(q, k[perm], v[perm], 0.25), o, atol=1e-14)
+    # one dominant score selects its row
+    k2 = k.copy(); k2[4] = q[0] * 50
+    assert np.allclose(O.attention_fp64(q[:1], k2, v, 1.0)[0], v[4], atol=1e-9)
+
+
+def test_row_rel_err_definition():
+    r = np.array([[1.0, -2.0, 0.5]])
+    o = np.array([[1.0, -2.002, 0.5]])
+    assert abs(O.row_rel_err(o, r) - 0.001) < 1e-12
+
+
+# ------------------------------------------------------------ tiered unit ---
+def test_tiered_unit_roundtrip_small():
+    w = synth.CONFIGS[0].shrink(tokens=300, name="tiny")
+    inp = synth.make_inputs(w)
+    rank = O.rank_desc(inp.scores)
+    tokmap, counts, inv = O.tiers_and_slots(rank, w.n_hi)
+    hi, lo = O.quantize_tiered_unit(inp.k[0, :, 0], inp.v[0, :, 0], inv[0], 6, 5, 32)
+    assert hi.n + lo.n == 300 and hi.n == 150
+    # pool rows are the tier's tokens in token order, within half a step
+    for pool, toks in ((hi, inv[0][0]), (lo, inv[0][1])):
+        kh = pool.k_hat()
+        ks = np.repeat(pool.k_scale.astype(np.float64), 32, axis=1)
+        assert np.all(np.abs(kh - inp.k[0, toks, 0].astype(np.float64)) <= ks / 2 * (1 + 1e-6) + 1e-12)
+        vw = pool.v_words()
+        n = O.codes_per_word(pool.L)
+        assert vw.shape == (-(-pool.n // n), 128)
+        assert np.array_equal(O.unpack_digits(vw, pool.L, n).transpose(0, 2, 1).reshape(-1, 128)[:pool.n],
+                              pool.v_codes)
+
+
+# ----------------------------------------------------------------- kchan ---
+def test_kchan_unit_structure():
+    w = synth.CONFIGS[4].shrink(tokens=128 * 3 + 50, batch=1, kv_heads=1, q_heads=4, name="tiny5")
+    inp = synth.make_inputs(w)
+    k, v = inp.k[0, :, 0], inp.v[0, :, 0]
+    u = O.KChanUnit(k, v, w)
+    assert u.n_q == 256 and u.k_win.shape[0] == 178            # 2 blocks + window of 178
+    assert np.array_equal(u.k_win, k[256:]) and np.array_equal(u.v_win, v[256:])
+    mag = np.abs(k[:256].astype(np.float64))
+    for t in range(256):
+        top = sorted(range(128), key=lambda d: (-mag[t, d], d))[:2]
+        assert u.sp_ch[t].tolist() == sorted(top)
+        assert np.array_equal(u.sp_val[t], k[t, sorted(top)])
+    kh = u.k_hat()[:256]
+    step = np.repeat(u.k_scale.astype(np.float64)[:, None, :], 128, axis=1).reshape(256, 128)
+    assert np.all(np.abs(kh - k[:256].astype(np.float64)) <= step / 2 * (1 + 1e-6) + 1e-12)
+    # outlier channels are mostly taken by the sparse list
+    assert np.mean(u.sp_ch < 4) > 0.9
+    vh = u.v_hat()
+    assert np.array_equal(vh[256:], v[256:].astype(np.float64))
+
+
+# --------------------------------------------------------------- storage ---
+def test_storage_ratio_closed_forms():
+    """Layout bytes per (sequence, KV head), worked by hand for the 32768-token
+    6/5-level G=32 unit and the 65536-token kchan unit."""
+    D = 128
+    # 16384 hi tokens: 11 key words (44 B), ceil(16384/12) = 1366 value word rows
+    # of 128 words, 4 groups x 4 B (scale, zero) for K and for V.
+    hi = 16384 * 44 + 1366 * 512 + 2 * 16384 * 16
+    lo = 16384 * 40 + 1261 * 512 + 2 * 16384 * 16
+    assert O.tiered_unit_bytes(16384, 16384, 6, 5, 32, D) == hi + lo
+    fp16 = 32768 * 128 * 2 * 2
+    assert abs(O.storage_ratio(fp16, hi + lo) - 16777216 / 3769856) < 1e-12
+    w = synth.CONFIGS[4]
+    nq = 65408
+    b = nq * 32 + 511 * 512 + nq * 8 + (-(-nq // 20)) * 512 + nq * 16 + 128 * 512
+    assert O.kchan_unit_bytes(65536, w, D) == b
+    assert 5.5 < O.storage_ratio(65536 * 512, b) < 6.0
