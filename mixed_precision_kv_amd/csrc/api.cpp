@@ -1,0 +1,201 @@
+// Host side of the C ABI: layout, workspace sizing, argument validation and
+// dispatch to the kernel launchers.  Nothing here touches the GPU except the
+// launchers, which run only after every argument has been checked.
+#include <string.h>
+
+#include "common.h"
+#include "internal.h"
+
+namespace kvq {
+
+static int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
+static bool levels_ok(int L) { return L >= 3 && L <= 16; }
+static bool group_ok(int G) { return G == 32 || G == 64 || G == 128; }
+
+int decode_chunks(const kvq_layout* L, int max_len, int* nch0, int* nch1) {
+  if (L->cfg.mode == KVQ_MODE_TIERED) {
+    int c0 = L->cap[0] < max_len ? L->cap[0] : max_len;
+    int c1 = L->cap[1] < max_len ? L->cap[1] : max_len;
+    *nch0 = ceil_div(c0, decode_chunk_tiered(L->nv[0]));
+    *nch1 = ceil_div(c1, decode_chunk_tiered(L->nv[1]));
+  } else {
+    int nq = kchan_nq(L, max_len);
+    *nch0 = ceil_div(nq, decode_chunk_kchan(L));
+    *nch1 = 1;  // the fp16 window
+  }
+  return *nch0 + *nch1;
+}
+
+QuantWs quant_ws_plan(const kvq_layout* L, int T) {
+  QuantWs p;
+  memset(&p, 0, sizeof(p));
+  const int64_t B = L->cfg.batch;
+  int64_t off = 0;
+  if (L->cfg.mode == KVQ_MODE_TIERED) {
+    const int64_t nblk = ceil_div(T, kSortTile);
+    for (int i = 0; i < 2; ++i) { p.keys[i] = off; off = align256(off + B * T * 4); }
+    for (int i = 0; i < 2; ++i) { p.idx[i] = off; off = align256(off + B * T * 4); }
+    p.hist = off;   off = align256(off + B * 256 * nblk * 4);
+    p.ranks = off;  off = align256(off + B * T * 4);
+    for (int i = 0; i < 2; ++i) { p.inv[i] = off; off = align256(off + B * (int64_t)L->cap[i] * 4); }
+    p.bcount = off; off = align256(off + B * nblk * 4);
+  }
+  p.total = (size_t)(off > 256 ? off : 256);
+  return p;
+}
+
+}  // namespace kvq
+
+using namespace kvq;
+
+extern "C" const char* kvq_status_str(kvq_status s) {
+  switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_ARG: return "invalid argument";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KVQ_ERR_CAPACITY: return "capacity exceeded";
+    case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case KVQ_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+extern "C" kvq_status kvq_layout_init(const kvq_config* cfg, kvq_layout* out) {
+  if (!cfg || !out) return KVQ_ERR_ARG;
+  const kvq_config c = *cfg;
+  if (c.batch < 1 || c.kv_heads < 1 || c.q_heads < 1 || c.head_dim < 1 || c.capacity < 1)
+    return KVQ_ERR_ARG;
+  if (c.head_dim != kD || c.q_heads != kGqa * c.kv_heads) return KVQ_ERR_UNSUPPORTED;
+  if ((int64_t)c.batch * c.kv_heads > (1 << 20) || c.capacity > (1 << 24)) return KVQ_ERR_UNSUPPORTED;
+  kvq_layout L;
+  memset(&L, 0, sizeof(L));
+  L.cfg = c;
+  const int64_t B = c.batch, U = (int64_t)c.batch * c.kv_heads, D = kD;
+  int64_t off = 0;
+  if (c.mode == KVQ_MODE_TIERED) {
+    if (!levels_ok(c.levels_hi) || !levels_ok(c.levels_lo) || !group_ok(c.group))
+      return KVQ_ERR_UNSUPPORTED;
+    if (c.cap_hi < 0 || c.cap_lo < 0) return KVQ_ERR_ARG;
+    L.cap[0] = c.cap_hi ? c.cap_hi : c.capacity;
+    L.cap[1] = c.cap_lo ? c.cap_lo : c.capacity;
+    if (L.cap[0] > c.capacity || L.cap[1] > c.capacity) return KVQ_ERR_ARG;
+    if ((int64_t)L.cap[0] + L.cap[1] < c.capacity) return KVQ_ERR_ARG;
+    const int lv[2] = {c.levels_hi, c.levels_lo};
+    L.counters = off; off = align256(off + B * 16);
+    L.tokmap = off;   off = align256(off + B * c.capacity * 4);
+    L.sorted = off;   off = align256(off + B * c.capacity * 4);
+    for (int p = 0; p < 2; ++p) {
+      L.nv[p] = codes_per_word(lv[p]);
+      L.kw[p] = ceil_div(kD, L.nv[p]);
+      L.tiles[p] = ceil_div(L.cap[p], kTile);
+      L.vrows[p] = ceil_div(L.cap[p], L.nv[p]);
+      const int64_t ng = kD / c.group;
+      L.k_words[p] = off; off = align256(off + U * L.tiles[p] * L.kw[p] * kTile * 4);
+      L.k_meta[p] = off;  off = align256(off + U * L.tiles[p] * ng * kTile * 4);
+      L.v_words[p] = off; off = align256(off + U * L.vrows[p] * D * 4);
+      L.v_meta[p] = off;  off = align256(off + U * L.tiles[p] * ng * kTile * 4);
+    }
+  } else if (c.mode == KVQ_MODE_KCHAN) {
+    if (!levels_ok(c.k_levels) || !levels_ok(c.v_levels) || !group_ok(c.v_group))
+      return KVQ_ERR_UNSUPPORTED;
+    if (c.k_block != 128 || c.window < 0 || c.sparse_per_vec < 0 || c.sparse_per_vec > 8)
+      return KVQ_ERR_UNSUPPORTED;
+    L.cap[0] = c.capacity;
+    L.nv[0] = codes_per_word(c.k_levels);
+    L.nv[1] = codes_per_word(c.v_levels);
+    L.vnv = L.nv[1];
+    // decode chunks hold whole key blocks, key tiles and value word rows
+    if (lcm_i(lcm_i(c.k_block, kTile), L.vnv) > 640) return KVQ_ERR_UNSUPPORTED;
+    if (c.window + c.k_block - 1 > 640) return KVQ_ERR_UNSUPPORTED;
+    L.kw[0] = ceil_div(kD, L.nv[0]);
+    L.tiles[0] = ceil_div(c.capacity, kTile);
+    L.vrows[0] = ceil_div(c.capacity, L.vnv);
+    L.kblocks = ceil_div(c.capacity, c.k_block);
+    L.win_cap = c.window + c.k_block - 1;
+    if (L.win_cap > c.capacity) L.win_cap = c.capacity;
+    const int64_t ng = kD / c.v_group;
+    L.counters = off; off = align256(off + B * 16);
+    L.k_words[0] = off; off = align256(off + U * L.tiles[0] * L.kw[0] * kTile * 4);
+    L.k_meta[0] = off;  off = align256(off + U * L.kblocks * D * 4);
+    L.sparse = off;     off = align256(off + U * (int64_t)c.capacity * c.sparse_per_vec * 4);
+    L.v_words[0] = off; off = align256(off + U * L.vrows[0] * D * 4);
+    L.v_meta[0] = off;  off = align256(off + U * L.tiles[0] * ng * kTile * 4);
+    L.k_win = off;      off = align256(off + U * L.win_cap * D * 2);
+    L.v_win = off;      off = align256(off + U * L.win_cap * D * 2);
+  } else {
+    return KVQ_ERR_ARG;
+  }
+  L.total_bytes = off;
+  *out = L;
+  return KVQ_OK;
+}
+
+extern "C" size_t kvq_workspace_bytes(const kvq_layout* lay, int32_t op, int32_t max_len) {
+  if (!lay || max_len < 1 || max_len > lay->cfg.capacity) return 0;
+  if (op == KVQ_OP_QUANTIZE) return quant_ws_plan(lay, max_len).total;
+  if (op == KVQ_OP_DECODE) {
+    int a, b;
+    int n = decode_chunks(lay, max_len, &a, &b);
+    const int64_t U = (int64_t)lay->cfg.batch * lay->cfg.kv_heads;
+    return (size_t)(U * n * kGqa * (4 + kD) * 4);
+  }
+  return 0;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+extern "C" kvq_status kvq_quantize(const kvq_layout* lay, void* cache, const void* k, const void* v,
+                                   int64_t stride_b, int64_t stride_t, int64_t stride_h,
+                                   const float* scores, int32_t T, int32_t n_hi, int32_t* ranks_out,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  if (!lay || !cache || !k || !v) return KVQ_ERR_ARG;
+  if (!aligned16(cache) || !aligned16(k) || !aligned16(v)) return KVQ_ERR_ARG;
+  const kvq_config& c = lay->cfg;
+  if (T < 1) return KVQ_ERR_ARG;
+  if (T > c.capacity) return KVQ_ERR_CAPACITY;
+  if (stride_b < 0 || stride_t < 0 || stride_h < 0) return KVQ_ERR_ARG;
+  if ((stride_b | stride_t | stride_h) & 7) return KVQ_ERR_ARG;
+  if (c.mode == KVQ_MODE_TIERED) {
+    if (!scores || !aligned16(scores)) return KVQ_ERR_ARG;
+    if (ranks_out && !aligned16(ranks_out)) return KVQ_ERR_ARG;
+    if (n_hi < 0 || n_hi > T) return KVQ_ERR_ARG;
+    if (n_hi > lay->cap[0] || T - n_hi > lay->cap[1]) return KVQ_ERR_CAPACITY;
+    QuantWs plan = quant_ws_plan(lay, T);
+    if (!ws || !aligned16(ws) || ws_bytes < plan.total) return KVQ_ERR_WORKSPACE;
+    if (!launch_rank_tiers(lay, (uint8_t*)cache, scores, T, n_hi, ranks_out, (uint8_t*)ws, plan, stream))
+      return KVQ_ERR_LAUNCH;
+    if (!launch_quantize_tiered(lay, (uint8_t*)cache, k, v, stride_b, stride_t, stride_h, T, n_hi,
+                                (const uint8_t*)ws, plan, stream))
+      return KVQ_ERR_LAUNCH;
+    return KVQ_OK;
+  }
+  if (!launch_quantize_kchan(lay, (uint8_t*)cache, k, v, stride_b, stride_t, stride_h, T, stream))
+    return KVQ_ERR_LAUNCH;
+  return KVQ_OK;
+}
+
+extern "C" kvq_status kvq_append(const kvq_layout* lay, void* cache, const void* k_new,
+                                 const void* v_new, const float* score_new, void* stream) {
+  if (!lay || !cache || !k_new || !v_new || !score_new) return KVQ_ERR_ARG;
+  if (!aligned16(cache) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(score_new))
+    return KVQ_ERR_ARG;
+  if (lay->cfg.mode != KVQ_MODE_TIERED) return KVQ_ERR_UNSUPPORTED;
+  if (!launch_append(lay, (uint8_t*)cache, k_new, v_new, score_new, stream)) return KVQ_ERR_LAUNCH;
+  return KVQ_OK;
+}
+
+extern "C" kvq_status kvq_decode_attn(const kvq_layout* lay, const void* cache, const void* q,
+                                      float softmax_scale, int32_t max_len, void* out, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  if (!lay || !cache || !q || !out) return KVQ_ERR_ARG;
+  if (!aligned16(cache) || !aligned16(q) || !aligned16(out)) return KVQ_ERR_ARG;
+  if (!(softmax_scale > 0.0f) || softmax_scale > 1e30f) return KVQ_ERR_ARG;
+  if (max_len < 1) return KVQ_ERR_ARG;
+  if (max_len > lay->cfg.capacity) return KVQ_ERR_CAPACITY;
+  size_t need = kvq_workspace_bytes(lay, KVQ_OP_DECODE, max_len);
+  if (!ws || !aligned16(ws) || ws_bytes < need) return KVQ_ERR_WORKSPACE;
+  if (!launch_decode(lay, (const uint8_t*)cache, q, softmax_scale, max_len, out, (uint8_t*)ws, stream))
+    return KVQ_ERR_LAUNCH;
+  return KVQ_OK;
+}

@@ -1,0 +1,88 @@
+// Internal helpers shared by the library's HIP sources (not part of the ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#include "../../include/kvq.h"
+
+namespace kvq {
+
+constexpr int kD = 128;          // head_dim supported by the kernels
+constexpr int kGqa = 4;          // query heads per KV head
+constexpr int kTile = 16;        // slots per key tile
+
+// Base-L digits per 32-bit word: max{n : L^n <= 2^32}.
+__host__ __device__ inline int codes_per_word(int L) {
+  uint64_t p = 1;
+  int n = 0;
+  while (p * (uint64_t)L <= (1ull << 32)) {
+    p *= (uint64_t)L;
+    ++n;
+  }
+  return n;
+}
+
+__host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// fp16 bits -> integer key in IEEE total order (-0 below +0).
+__device__ inline int f16_order_key(uint32_t b) {
+  return (b & 0x8000u) ? -(int)(b & 0x7FFFu) - 1 : (int)b;
+}
+__device__ inline uint32_t f16_from_order_key(int k) {
+  return k < 0 ? (uint32_t)((-(k + 1)) | 0x8000) : (uint32_t)k;
+}
+
+__device__ inline float h2f(uint32_t bits16) {
+  return __half2float(__ushort_as_half((unsigned short)bits16));
+}
+__device__ inline uint32_t f2h_rne(float x) {
+  return (uint32_t)__half_as_ushort(__float2half_rn(x));
+}
+
+// Quantize one group given its fp16 min/max (bits).  Produces the fp16 scale
+// bits and the fp32 values the per-value step needs.  The per-value code is
+//   c = clamp(rint(fl32(x - z) / s), 0, L-1)
+// where the quotient is computed as q0 = a*r, rho = fma(-q0, s, a),
+// q = fma(rho, r, q0) with r = RN(1/s): Markstein's correction, which returns
+// the correctly rounded fp32 quotient when r is the correctly rounded
+// reciprocal (no overflow/underflow for fp16-range operands).
+struct GroupQ {
+  float z, s, r;
+  uint32_t s_bits;
+  float top;
+};
+
+__device__ inline GroupQ group_setup(uint32_t mn_bits, uint32_t mx_bits, int L) {
+  GroupQ g;
+  g.z = h2f(mn_bits);
+  float range = h2f(mx_bits) - g.z;               // fp32, round to nearest even
+  float s32 = range / (float)(L - 1);             // IEEE division
+  g.s_bits = f2h_rne(s32);
+  g.s = h2f(g.s_bits);
+  g.r = (g.s != 0.0f) ? 1.0f / g.s : 0.0f;        // correctly rounded reciprocal
+  g.top = (float)(L - 1);
+  return g;
+}
+
+__device__ inline uint32_t quant_value(float x, const GroupQ& g) {
+  if (g.s == 0.0f) return 0u;
+  float a = x - g.z;
+  float q0 = a * g.r;
+  float rho = __builtin_fmaf(-q0, g.s, a);
+  float q = __builtin_fmaf(rho, g.r, q0);
+  float c = __builtin_rintf(q);
+  c = fminf(fmaxf(c, 0.0f), g.top);
+  return (uint32_t)c;
+}
+
+// Order-preserving u32 key of an fp32 score for a DESCENDING sort expressed
+// as an ascending one; -0 is folded onto +0 so equal scores tie.
+__device__ inline uint32_t score_desc_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if (u == 0x80000000u) u = 0u;
+  uint32_t asc = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ~asc;
+}
+
+}  // namespace kvq

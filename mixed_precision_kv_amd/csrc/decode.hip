@@ -1,0 +1,368 @@
+// Decode attention over the packed cache, split over the context
+// (SemKV, Abstract: attention reads every kept token of the compressed cache;
+// KVQuant summary: small-batch decode is bound by memory bandwidth, so the
+// packed words are read once and dequantized in registers).
+//
+// Grid: one workgroup per (context chunk, unit, pool).  Each computes, for the
+// four query heads of its KV head, the chunk's running max m (log2 domain),
+// the sum l of exp2(score - m) and the unnormalized sum of exp2(score - m) * v^,
+// then a merge kernel combines every chunk of both pools (log-sum-exp).
+//
+// Scores use the group identity
+//   q . k^ = sum_g ( s_g * sum_{d in g} q_d c_d  +  z_g * sum_{d in g} q_d )
+// so keys are never dequantized value by value.
+#include <string.h>
+
+#include "common.h"
+#include "internal.h"
+
+namespace kvq {
+
+constexpr int kDecThreads = 256;
+constexpr int kPartStride = 4 + kD;        // floats per head: m, l, pad, pad, acc[128]
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct DecodeArgs {
+  const int32_t* counters;
+  const uint16_t* q;
+  float* part;
+  int Hkv, nch_total, nch0;
+  float scale_log2;
+  // tiered pools / kchan quantized part
+  const uint32_t* kwords[2];
+  const uint32_t* kmeta[2];
+  const uint32_t* vwords[2];
+  const uint32_t* vmeta[2];
+  int L[2], nv[2], kw[2], tiles[2], vrows[2], chunk[2];
+  int group;
+  // kchan extras
+  const uint32_t* sparse;
+  const uint16_t* kwin;
+  const uint16_t* vwin;
+  int vL, vnv, vgroup, spv, cap, kblocks, win_cap;
+};
+
+__device__ inline float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ inline float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Softmax of the chunk's scores (sc[4][n], log2-scaled) in place -> p; returns
+// per-head m, l in sm[4], sl[4].  Wave w handles head w.
+__device__ inline void chunk_softmax(float (*sc)[640], int n, float* sm, float* sl) {
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  float m = -INFINITY;
+  for (int i = lane; i < n; i += 64) m = fmaxf(m, sc[w][i]);
+  m = wave_max(m);
+  float l = 0.f;
+  for (int i = lane; i < n; i += 64) {
+    float p = exp2f(sc[w][i] - m);
+    sc[w][i] = p;
+    l += p;
+  }
+  l = wave_sum(l);
+  if (lane == 0) { sm[w] = m; sl[w] = l; }
+}
+
+__device__ inline void write_empty(float* part) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kGqa * kPartStride; i += kDecThreads) {
+    const int j = i % kPartStride;
+    part[i] = (j == 0) ? -INFINITY : 0.0f;
+  }
+}
+
+// Value pass shared by every quantized layout: column words of nv slots,
+// per-slot (scale, zero) in 16-slot tiles with groups of G along head_dim.
+__device__ inline void value_pass(const uint32_t* __restrict__ vw, const uint32_t* __restrict__ vm,
+                                  int u, int vrows, int tiles, int L, int nv, int G, int s_begin,
+                                  int s_end, float (*p)[640], float* red, float* acc_out) {
+  const int tid = threadIdx.x, d = tid & (kD - 1), half = tid >> 7;
+  const int NG = kD / G, g = d / G;
+  float acc[kGqa] = {0.f, 0.f, 0.f, 0.f};
+  const int r_begin = s_begin / nv, r_end = ceil_div(s_end, nv);
+  for (int r = r_begin + half; r < r_end; r += 2) {
+    uint32_t word = vw[((size_t)u * vrows + r) * kD + d];
+    for (int j = 0; j < nv; ++j) {
+      const int s = r * nv + j;
+      if (s >= s_end) break;
+      const uint32_t c = word % (uint32_t)L;
+      word /= (uint32_t)L;
+      const uint32_t meta = vm[(((size_t)u * tiles + s / kTile) * NG + g) * kTile + (s % kTile)];
+      const float v = __builtin_fmaf((float)c, h2f(meta & 0xFFFFu), h2f(meta >> 16));
+      const int i = s - s_begin;
+#pragma unroll
+      for (int hh = 0; hh < kGqa; ++hh) acc[hh] = __builtin_fmaf(p[hh][i], v, acc[hh]);
+    }
+  }
+  if (half == 1)
+    for (int hh = 0; hh < kGqa; ++hh) red[hh * kD + d] = acc[hh];
+  __syncthreads();
+  if (half == 0)
+    for (int hh = 0; hh < kGqa; ++hh) acc_out[hh * kD + d] = acc[hh] + red[hh * kD + d];
+}
+
+__device__ inline void finish_partial(float* part, const float* sm, const float* sl,
+                                      const float* acc) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kGqa * kD; i += kDecThreads) {
+    const int hh = i / kD, d = i % kD;
+    part[hh * kPartStride + 4 + d] = acc[hh * kD + d];
+  }
+  if (tid < kGqa) {
+    part[tid * kPartStride + 0] = sm[tid];
+    part[tid * kPartStride + 1] = sl[tid];
+  }
+}
+
+__device__ inline void load_q(const uint16_t* q, int b, int hk, int Hkv, float (*qf)[kD]) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kGqa * kD; i += kDecThreads) {
+    const int hh = i / kD, d = i % kD;
+    qf[hh][d] = h2f(q[((size_t)b * Hkv * kGqa + hk * kGqa + hh) * kD + d]);
+  }
+}
+
+__global__ __launch_bounds__(kDecThreads) void k_decode_tiered(DecodeArgs a) {
+  __shared__ float qf[kGqa][kD];
+  __shared__ float qsum[kGqa][4];
+  __shared__ float sc[kGqa][640];
+  __shared__ float red[kGqa * kD];
+  __shared__ float accs[kGqa * kD];
+  __shared__ float sm[kGqa], sl[kGqa];
+  const int tid = threadIdx.x;
+  const int c = blockIdx.x, u = blockIdx.y, p = blockIdx.z;
+  const int b = u / a.Hkv, hk = u % a.Hkv;
+  const int nchp = p ? (a.nch_total - a.nch0) : a.nch0;
+  if (c >= nchp) return;
+  float* part = a.part + ((size_t)u * a.nch_total + (p ? a.nch0 : 0) + c) * kGqa * kPartStride;
+  const int n = a.counters[b * 4 + 1 + p];
+  const int CH = a.chunk[p];
+  const int s_begin = c * CH, s_end = min(n, s_begin + CH);
+  if (s_begin >= s_end) { write_empty(part); return; }
+  const int L = a.L[p], nv = a.nv[p], kw = a.kw[p], tiles = a.tiles[p];
+  const int G = a.group, NG = kD / G;
+  load_q(a.q, b, hk, a.Hkv, qf);
+  __syncthreads();
+  if (tid < kGqa * NG) {
+    const int hh = tid / NG, g = tid % NG;
+    float s = 0.f;
+    for (int d = g * G; d < (g + 1) * G; ++d) s += qf[hh][d];
+    qsum[hh][g] = s;
+  }
+  __syncthreads();
+  // scores: one thread per slot
+  for (int s = s_begin + tid; s < s_end; s += kDecThreads) {
+    float part_g[kGqa][4];
+    for (int hh = 0; hh < kGqa; ++hh)
+      for (int g = 0; g < 4; ++g) part_g[hh][g] = 0.f;
+    const uint32_t* kp = a.kwords[p] + ((size_t)u * tiles + s / kTile) * kw * kTile + (s % kTile);
+    for (int w = 0; w < kw; ++w) {
+      uint32_t word = kp[w * kTile];
+      for (int j = 0; j < nv; ++j) {
+        const int d = w * nv + j;
+        if (d >= kD) break;
+        const float cf = (float)(word % (uint32_t)L);
+        word /= (uint32_t)L;
+        const int g = d / G;
+        for (int hh = 0; hh < kGqa; ++hh) part_g[hh][g] = __builtin_fmaf(qf[hh][d], cf, part_g[hh][g]);
+      }
+    }
+    const uint32_t* mp = a.kmeta[p] + ((size_t)u * tiles + s / kTile) * NG * kTile + (s % kTile);
+    float sco[kGqa] = {0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < NG; ++g) {
+      const uint32_t meta = mp[g * kTile];
+      const float sg = h2f(meta & 0xFFFFu), zg = h2f(meta >> 16);
+      for (int hh = 0; hh < kGqa; ++hh)
+        sco[hh] += __builtin_fmaf(sg, part_g[hh][g], zg * qsum[hh][g]);
+    }
+    for (int hh = 0; hh < kGqa; ++hh) sc[hh][s - s_begin] = sco[hh] * a.scale_log2;
+  }
+  __syncthreads();
+  chunk_softmax(sc, s_end - s_begin, sm, sl);
+  __syncthreads();
+  value_pass(a.vwords[p], a.vmeta[p], u, a.vrows[p], tiles, L, nv, G, s_begin, s_end, sc, red, accs);
+  __syncthreads();
+  finish_partial(part, sm, sl, accs);
+}
+
+// kchan: blockIdx.z == 0 -> quantized tokens (per-channel keys + sparse),
+// blockIdx.z == 1 -> the fp16 window (a single chunk).
+__global__ __launch_bounds__(kDecThreads) void k_decode_kchan(DecodeArgs a) {
+  __shared__ float qf[kGqa][kD];
+  __shared__ float qs[kGqa][kD];            // q * per-channel scale of the current key block
+  __shared__ float qz[kGqa];
+  __shared__ float sc[kGqa][640];
+  __shared__ float red[kGqa * kD];
+  __shared__ float accs[kGqa * kD];
+  __shared__ float sm[kGqa], sl[kGqa];
+  const int tid = threadIdx.x;
+  const int c = blockIdx.x, u = blockIdx.y, z = blockIdx.z;
+  const int b = u / a.Hkv, hk = u % a.Hkv;
+  const int nchp = z ? 1 : a.nch0;
+  if (c >= nchp) return;
+  float* part = a.part + ((size_t)u * a.nch_total + (z ? a.nch0 : 0) + c) * kGqa * kPartStride;
+  const int nq = a.counters[b * 4 + 1];
+  const int nwin = a.counters[b * 4 + 2];
+  load_q(a.q, b, hk, a.Hkv, qf);
+  __syncthreads();
+  if (z == 1) {
+    if (nwin <= 0) { write_empty(part); return; }
+    const uint16_t* kwp = a.kwin + (size_t)u * a.win_cap * kD;
+    const uint16_t* vwp = a.vwin + (size_t)u * a.win_cap * kD;
+    for (int i = tid; i < nwin; i += kDecThreads) {
+      float sco[kGqa] = {0.f, 0.f, 0.f, 0.f};
+      for (int d = 0; d < kD; ++d) {
+        const float kv = h2f(kwp[(size_t)i * kD + d]);
+        for (int hh = 0; hh < kGqa; ++hh) sco[hh] = __builtin_fmaf(qf[hh][d], kv, sco[hh]);
+      }
+      for (int hh = 0; hh < kGqa; ++hh) sc[hh][i] = sco[hh] * a.scale_log2;
+    }
+    __syncthreads();
+    chunk_softmax(sc, nwin, sm, sl);
+    __syncthreads();
+    const int d = tid & (kD - 1), half = tid >> 7;
+    float acc[kGqa] = {0.f, 0.f, 0.f, 0.f};
+    for (int i = half; i < nwin; i += 2) {
+      const float vv = h2f(vwp[(size_t)i * kD + d]);
+      for (int hh = 0; hh < kGqa; ++hh) acc[hh] = __builtin_fmaf(sc[hh][i], vv, acc[hh]);
+    }
+    if (half == 1)
+      for (int hh = 0; hh < kGqa; ++hh) red[hh * kD + d] = acc[hh];
+    __syncthreads();
+    if (half == 0)
+      for (int hh = 0; hh < kGqa; ++hh) accs[hh * kD + d] = acc[hh] + red[hh * kD + d];
+    __syncthreads();
+    finish_partial(part, sm, sl, accs);
+    return;
+  }
+  const int CH = a.chunk[0];
+  const int s_begin = c * CH, s_end = min(nq, s_begin + CH);
+  if (s_begin >= s_end) { write_empty(part); return; }
+  const int L = a.L[0], nv = a.nv[0], kw = a.kw[0], tiles = a.tiles[0];
+  for (int blk0 = s_begin; blk0 < s_end; blk0 += 128) {
+    const int kb = blk0 / 128;
+    for (int i = tid; i < kGqa * kD; i += kDecThreads) {
+      const int hh = i / kD, d = i % kD;
+      const uint32_t meta = a.kmeta[0][((size_t)u * a.kblocks + kb) * kD + d];
+      qs[hh][d] = qf[hh][d] * h2f(meta & 0xFFFFu);
+      red[i] = qf[hh][d] * h2f(meta >> 16);
+    }
+    __syncthreads();
+    if (tid < kGqa) {
+      float sz = 0.f;
+      for (int d = 0; d < kD; ++d) sz += red[tid * kD + d];
+      qz[tid] = sz;
+    }
+    __syncthreads();
+    if (tid < 128) {
+      const int s = blk0 + tid;
+      float sco[kGqa] = {0.f, 0.f, 0.f, 0.f};
+      const uint32_t* kp = a.kwords[0] + ((size_t)u * tiles + s / kTile) * kw * kTile + (s % kTile);
+      for (int w = 0; w < kw; ++w) {
+        uint32_t word = kp[w * kTile];
+        for (int j = 0; j < nv; ++j) {
+          const int d = w * nv + j;
+          if (d >= kD) break;
+          const float cf = (float)(word % (uint32_t)L);
+          word /= (uint32_t)L;
+          for (int hh = 0; hh < kGqa; ++hh) sco[hh] = __builtin_fmaf(qs[hh][d], cf, sco[hh]);
+        }
+      }
+      for (int e = 0; e < a.spv; ++e) {
+        const uint32_t ent = a.sparse[((size_t)u * a.cap + s) * a.spv + e];
+        const int ch = ent >> 16;
+        const float val = h2f(ent & 0xFFFFu);
+        for (int hh = 0; hh < kGqa; ++hh) sco[hh] = __builtin_fmaf(qf[hh][ch], val, sco[hh]);
+      }
+      for (int hh = 0; hh < kGqa; ++hh) sc[hh][s - s_begin] = (sco[hh] + qz[hh]) * a.scale_log2;
+    }
+    __syncthreads();
+  }
+  chunk_softmax(sc, s_end - s_begin, sm, sl);
+  __syncthreads();
+  value_pass(a.vwords[0], a.vmeta[0], u, a.vrows[0], tiles, a.vL, a.vnv, a.vgroup, s_begin, s_end,
+             sc, red, accs);
+  __syncthreads();
+  finish_partial(part, sm, sl, accs);
+}
+
+// Log-sum-exp merge of every chunk partial of one unit -> fp16 output.
+__global__ __launch_bounds__(kGqa * kD) void k_merge(const float* __restrict__ part,
+                                                     uint16_t* __restrict__ out, int nch_total,
+                                                     int Hkv) {
+  const int u = blockIdx.x, tid = threadIdx.x;
+  const int hh = tid / kD, d = tid % kD;
+  const int b = u / Hkv, hk = u % Hkv;
+  const float* pu = part + (size_t)u * nch_total * kGqa * kPartStride + hh * kPartStride;
+  float M = -INFINITY;
+  for (int c = 0; c < nch_total; ++c) M = fmaxf(M, pu[(size_t)c * kGqa * kPartStride]);
+  float l = 0.f, o = 0.f;
+  for (int c = 0; c < nch_total; ++c) {
+    const float* pc = pu + (size_t)c * kGqa * kPartStride;
+    const float m = pc[0];
+    if (m == -INFINITY) continue;
+    const float w = exp2f(m - M);
+    l = __builtin_fmaf(pc[1], w, l);
+    o = __builtin_fmaf(pc[4 + d], w, o);
+  }
+  out[((size_t)b * Hkv * kGqa + hk * kGqa + hh) * kD + d] = f2h_rne(o / l);
+}
+
+bool launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, float scale,
+                   int max_len, void* out, uint8_t* ws, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  const kvq_config& c = L->cfg;
+  const int U = c.batch * c.kv_heads;
+  int nch0, nch1;
+  const int nch = decode_chunks(L, max_len, &nch0, &nch1);
+  DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.counters = (const int32_t*)(cache + L->counters);
+  a.q = (const uint16_t*)q;
+  a.part = (float*)ws;
+  a.Hkv = c.kv_heads;
+  a.nch_total = nch;
+  a.nch0 = nch0;
+  a.scale_log2 = scale * kLog2e;
+  if (c.mode == KVQ_MODE_TIERED) {
+    const int lv[2] = {c.levels_hi, c.levels_lo};
+    for (int p = 0; p < 2; ++p) {
+      a.kwords[p] = (const uint32_t*)(cache + L->k_words[p]);
+      a.kmeta[p] = (const uint32_t*)(cache + L->k_meta[p]);
+      a.vwords[p] = (const uint32_t*)(cache + L->v_words[p]);
+      a.vmeta[p] = (const uint32_t*)(cache + L->v_meta[p]);
+      a.L[p] = lv[p]; a.nv[p] = L->nv[p]; a.kw[p] = L->kw[p]; a.tiles[p] = L->tiles[p];
+      a.vrows[p] = L->vrows[p];
+      a.chunk[p] = decode_chunk_tiered(L->nv[p]);
+    }
+    a.group = c.group;
+    const int gx = nch0 > nch1 ? nch0 : nch1;
+    k_decode_tiered<<<dim3(gx, U, 2), kDecThreads, 0, s>>>(a);
+  } else {
+    a.kwords[0] = (const uint32_t*)(cache + L->k_words[0]);
+    a.kmeta[0] = (const uint32_t*)(cache + L->k_meta[0]);
+    a.vwords[0] = (const uint32_t*)(cache + L->v_words[0]);
+    a.vmeta[0] = (const uint32_t*)(cache + L->v_meta[0]);
+    a.L[0] = c.k_levels; a.nv[0] = L->nv[0]; a.kw[0] = L->kw[0]; a.tiles[0] = L->tiles[0];
+    a.vrows[0] = L->vrows[0];
+    a.chunk[0] = decode_chunk_kchan(L);
+    if (a.chunk[0] > 640) return false;
+    a.vL = c.v_levels; a.vnv = L->vnv; a.vgroup = c.v_group; a.spv = c.sparse_per_vec;
+    a.cap = c.capacity; a.kblocks = L->kblocks; a.win_cap = L->win_cap;
+    a.sparse = (const uint32_t*)(cache + L->sparse);
+    a.kwin = (const uint16_t*)(cache + L->k_win);
+    a.vwin = (const uint16_t*)(cache + L->v_win);
+    if (L->win_cap > 640) return false;
+    const int gx = nch0 > 1 ? nch0 : 1;
+    k_decode_kchan<<<dim3(gx, U, 2), kDecThreads, 0, s>>>(a);
+  }
+  k_merge<<<U, kGqa * kD, 0, s>>>((const float*)ws, (uint16_t*)out, nch, c.kv_heads);
+  return hipGetLastError() == hipSuccess;
+}
+
+}  // namespace kvq

@@ -1,0 +1,51 @@
+// Internal declarations shared by the host entry points and the kernels.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/kvq.h"
+
+namespace kvq {
+
+constexpr int kSortTile = 4096;   // keys per radix-sort block (256 threads x 16)
+
+// Decode chunking: slots per split-K chunk for a pool with nv codes per value
+// word (a whole number of 16-slot key tiles and of value word rows).
+inline int decode_chunk_tiered(int nv) {
+  int unit = 16 * nv;
+  int m = 640 / unit;
+  return unit * (m < 1 ? 1 : m);
+}
+inline int gcd_i(int a, int b) { while (b) { int t = a % b; a = b; b = t; } return a; }
+inline int lcm_i(int a, int b) { return a / gcd_i(a, b) * b; }
+inline int decode_chunk_kchan(const kvq_layout* L) {
+  return lcm_i(lcm_i(L->cfg.k_block, 16), L->vnv);
+}
+inline int kchan_nq(const kvq_layout* L, int T) {
+  int kb = L->cfg.k_block;
+  int n = (T - L->cfg.window) / kb;
+  return n > 0 ? n * kb : 0;
+}
+
+// Number of decode chunks per unit for sequences of at most max_len tokens.
+int decode_chunks(const kvq_layout* L, int max_len, int* nch0, int* nch1);
+
+struct QuantWs {           // byte offsets inside the quantize workspace
+  size_t keys[2], idx[2], hist, ranks, inv[2], bcount, total;
+};
+QuantWs quant_ws_plan(const kvq_layout* L, int T);
+
+// Kernel launchers (return false when a launch failed).
+bool launch_rank_tiers(const kvq_layout* L, uint8_t* cache, const float* scores, int T, int n_hi,
+                       int32_t* ranks_out, uint8_t* ws, const QuantWs& plan, void* stream);
+bool launch_quantize_tiered(const kvq_layout* L, uint8_t* cache, const void* k, const void* v,
+                            int64_t sb, int64_t st, int64_t sh, int T, int n_hi,
+                            const uint8_t* ws, const QuantWs& plan, void* stream);
+bool launch_quantize_kchan(const kvq_layout* L, uint8_t* cache, const void* k, const void* v,
+                           int64_t sb, int64_t st, int64_t sh, int T, void* stream);
+bool launch_append(const kvq_layout* L, uint8_t* cache, const void* k_new, const void* v_new,
+                   const float* score_new, void* stream);
+bool launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, float scale,
+                   int max_len, void* out, uint8_t* ws, void* stream);
+
+}  // namespace kvq

@@ -1,0 +1,438 @@
+// Quantize-on-write (SemKV, Abstract: affine quantizer on an L-level
+// fractional-bit grid, two adjacent grids chosen by rank, every token kept,
+// also at generation time) and the per-channel-key / dense-and-sparse /
+// fp16-window variant (KVQuant summary, "techniques"; SKVQ, Abstract).
+//
+// A workgroup owns a whole number of value word rows (nv slots each, at most
+// 256 slots) of one pool of one (sequence, KV head), so every packed word it
+// writes is complete.  Codes are staged in LDS as bytes,
+// then packed twice: along head_dim for keys (row words) and along slots for
+// values (column words).
+#include "common.h"
+#include "internal.h"
+
+namespace kvq {
+
+constexpr int kQThreads = 256;
+
+__host__ __device__ inline int rows_per_wg(int nv) { return nv >= 256 ? 1 : 256 / nv; }
+
+struct QuantArgs {
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t sb, st, sh;
+  const int32_t* inv;      // [B][cap] slot -> token, or null for identity
+  int inv_cap;
+  int n;                   // valid slots per unit (same for every sequence)
+  int L, nv, kw, tiles, vrows, Hkv;
+  uint32_t* kwords;        // null: values only
+  uint32_t* kmeta;
+  uint32_t* vwords;
+  uint32_t* vmeta;
+};
+
+// Quantize one group of G fp16 values at src (16-byte aligned); codes to LDS.
+template <int G>
+__device__ inline uint32_t quant_group(const uint16_t* __restrict__ src, int L, uint8_t* codes) {
+  uint4 raw[G / 8];
+#pragma unroll
+  for (int i = 0; i < G / 8; ++i) raw[i] = *reinterpret_cast<const uint4*>(src + i * 8);
+  const uint16_t* x = reinterpret_cast<const uint16_t*>(raw);
+  int kmn = f16_order_key(x[0]), kmx = kmn;
+#pragma unroll
+  for (int i = 1; i < G; ++i) {
+    int kk = f16_order_key(x[i]);
+    kmn = min(kmn, kk);
+    kmx = max(kmx, kk);
+  }
+  const uint32_t mn = f16_from_order_key(kmn), mx = f16_from_order_key(kmx);
+  GroupQ g = group_setup(mn, mx, L);
+#pragma unroll
+  for (int i = 0; i < G; ++i) codes[i] = (uint8_t)quant_value(h2f(x[i]), g);
+  return g.s_bits | (mn << 16);
+}
+
+template <int G>
+__global__ __launch_bounds__(kQThreads) void k_quant_pool(QuantArgs a) {
+  extern __shared__ uint8_t lds[];
+  constexpr int NG = kD / G;
+  const int rows = rows_per_wg(a.nv);
+  const int SL = rows * a.nv;
+  uint8_t* ck = lds;                 // [SL][128] key codes
+  uint8_t* cv = lds + SL * kD;       // [SL][128] value codes
+  const int tid = threadIdx.x;
+  const int u = blockIdx.y;
+  const int b = u / a.Hkv, h = u % a.Hkv;
+  const int s0 = blockIdx.x * SL;
+  const int kv_lo = a.kwords ? 0 : 1;
+  // phase 1: groups -> codes (LDS) and (scale, zero) (global)
+  const int ntask = SL * NG * 2;
+  for (int task = tid; task < ntask; task += kQThreads) {
+    const int kv = task / (SL * NG);
+    if (kv < kv_lo) continue;
+    const int rem = task - kv * SL * NG;
+    const int i = rem / NG, g = rem - (rem / NG) * NG;
+    const int s = s0 + i;
+    uint8_t* dst = (kv ? cv : ck) + i * kD + g * G;
+    uint32_t meta = 0;
+    if (s < a.n) {
+      const int t = a.inv ? a.inv[(size_t)b * a.inv_cap + s] : s;
+      const uint16_t* src = (kv ? a.v : a.k) + b * a.sb + (int64_t)t * a.st + h * a.sh + g * G;
+      meta = quant_group<G>(src, a.L, dst);
+    } else {
+#pragma unroll
+      for (int i2 = 0; i2 < G; ++i2) dst[i2] = 0;
+    }
+    if (s < a.tiles * kTile) {
+      uint32_t* mp = kv ? a.vmeta : a.kmeta;
+      mp[(((size_t)u * a.tiles + s / kTile) * NG + g) * kTile + (s % kTile)] = meta;
+    }
+  }
+  __syncthreads();
+  // phase 2: key row words
+  if (a.kwords) {
+    for (int task = tid; task < SL * a.kw; task += kQThreads) {
+      const int i = task / a.kw, w = task - (task / a.kw) * a.kw;
+      const int s = s0 + i;
+      if (s >= a.tiles * kTile) continue;
+      const int d0 = w * a.nv;
+      const int d1 = min(kD, d0 + a.nv);
+      uint32_t word = 0;
+      for (int d = d1 - 1; d >= d0; --d) word = word * (uint32_t)a.L + ck[i * kD + d];
+      a.kwords[(((size_t)u * a.tiles + s / kTile) * a.kw + w) * kTile + (s % kTile)] = word;
+    }
+  }
+  // phase 3: value column words (rows of nv slots)
+  const int r0 = s0 / a.nv;
+  for (int task = tid; task < rows * kD; task += kQThreads) {
+    const int r = task / kD, d = task % kD;
+    if (r0 + r >= a.vrows) continue;
+    uint32_t word = 0;
+    for (int j = a.nv - 1; j >= 0; --j) word = word * (uint32_t)a.L + cv[(r * a.nv + j) * kD + d];
+    a.vwords[((size_t)u * a.vrows + r0 + r) * kD + d] = word;
+  }
+}
+
+static bool launch_pool(const QuantArgs& a, int G, int U, hipStream_t s) {
+  const int SL = rows_per_wg(a.nv) * a.nv;
+  const int cover = max(a.tiles * kTile, a.vrows * a.nv);
+  dim3 grid(ceil_div(cover, SL), U);
+  size_t lds = (size_t)2 * SL * kD;
+  switch (G) {
+    case 32: k_quant_pool<32><<<grid, kQThreads, lds, s>>>(a); break;
+    case 64: k_quant_pool<64><<<grid, kQThreads, lds, s>>>(a); break;
+    case 128: k_quant_pool<128><<<grid, kQThreads, lds, s>>>(a); break;
+    default: return false;
+  }
+  return true;
+}
+
+bool launch_quantize_tiered(const kvq_layout* L, uint8_t* cache, const void* k, const void* v,
+                            int64_t sb, int64_t st, int64_t sh, int T, int n_hi,
+                            const uint8_t* ws, const QuantWs& plan, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  const int U = L->cfg.batch * L->cfg.kv_heads;
+  const int lv[2] = {L->cfg.levels_hi, L->cfg.levels_lo};
+  const int np[2] = {n_hi, T - n_hi};
+  for (int p = 0; p < 2; ++p) {
+    QuantArgs a;
+    a.k = (const uint16_t*)k;
+    a.v = (const uint16_t*)v;
+    a.sb = sb; a.st = st; a.sh = sh;
+    a.inv = (const int32_t*)(ws + plan.inv[p]);
+    a.inv_cap = L->cap[p];
+    a.n = np[p];
+    a.L = lv[p]; a.nv = L->nv[p]; a.kw = L->kw[p]; a.tiles = L->tiles[p]; a.vrows = L->vrows[p];
+    a.Hkv = L->cfg.kv_heads;
+    a.kwords = (uint32_t*)(cache + L->k_words[p]);
+    a.kmeta = (uint32_t*)(cache + L->k_meta[p]);
+    a.vwords = (uint32_t*)(cache + L->v_words[p]);
+    a.vmeta = (uint32_t*)(cache + L->v_meta[p]);
+    if (!launch_pool(a, L->cfg.group, U, s)) return false;
+  }
+  return hipGetLastError() == hipSuccess;
+}
+
+// ---------------------------------------------------------------- kchan ----
+// One workgroup per (unit, 128-token key block): per key vector pick the
+// sparse_per_vec largest |x| (ties -> lower channel) into the sparse list and
+// zero them; per channel quantize the dense block (min/max over 128 tokens);
+// pack each token's codes along head_dim.
+__global__ __launch_bounds__(256) void k_kchan_keys(const uint16_t* __restrict__ k, int64_t sb,
+                                                    int64_t st, int64_t sh, int Hkv, int L,
+                                                    int nv, int kw, int tiles, int kblocks,
+                                                    int cap, int spv,
+                                                    uint32_t* __restrict__ kwords,
+                                                    uint32_t* __restrict__ kmeta,
+                                                    uint32_t* __restrict__ sparse) {
+  __shared__ uint16_t xs[128][kD + 2];     // dense block, padded rows
+  __shared__ uint8_t cs[128][kD];          // codes
+  const int tid = threadIdx.x;
+  const int blk = blockIdx.x, u = blockIdx.y;
+  const int b = u / Hkv, h = u % Hkv;
+  const int t0 = blk * 128;
+  for (int e = tid; e < 128 * kD / 8; e += 256) {
+    const int t = e / (kD / 8), c8 = (e % (kD / 8)) * 8;
+    uint4 raw = *reinterpret_cast<const uint4*>(k + b * sb + (int64_t)(t0 + t) * st + h * sh + c8);
+    const uint16_t* r = reinterpret_cast<const uint16_t*>(&raw);
+    for (int i = 0; i < 8; ++i) xs[t][c8 + i] = r[i];
+  }
+  __syncthreads();
+  if (tid < 128) {
+    const int t = tid;
+    int chosen[8];
+    for (int e = 0; e < spv; ++e) {
+      int best = -1;
+      uint32_t bmag = 0;
+      for (int d = 0; d < kD; ++d) {
+        bool taken = false;
+        for (int e2 = 0; e2 < e; ++e2) taken |= (chosen[e2] == d);
+        const uint32_t m = xs[t][d] & 0x7FFFu;
+        if (!taken && (best < 0 || m > bmag)) { best = d; bmag = m; }
+      }
+      chosen[e] = best;
+    }
+    // ascending channel order
+    for (int i = 1; i < spv; ++i)
+      for (int j = i; j > 0 && chosen[j - 1] > chosen[j]; --j) {
+        int x = chosen[j]; chosen[j] = chosen[j - 1]; chosen[j - 1] = x;
+      }
+    // each thread owns its token row: read the outliers, then zero them
+    for (int e = 0; e < spv; ++e) {
+      const uint32_t ent = ((uint32_t)chosen[e] << 16) | xs[t][chosen[e]];
+      sparse[((size_t)u * cap + t0 + t) * spv + e] = ent;
+    }
+    for (int e = 0; e < spv; ++e) xs[t][chosen[e]] = 0;
+  }
+  __syncthreads();
+  if (tid < kD) {
+    const int d = tid;
+    int kmn = f16_order_key(xs[0][d]), kmx = kmn;
+    for (int t = 1; t < 128; ++t) {
+      int kk = f16_order_key(xs[t][d]);
+      kmn = min(kmn, kk);
+      kmx = max(kmx, kk);
+    }
+    const uint32_t mn = f16_from_order_key(kmn), mx = f16_from_order_key(kmx);
+    GroupQ g = group_setup(mn, mx, L);
+    for (int t = 0; t < 128; ++t) cs[t][d] = (uint8_t)quant_value(h2f(xs[t][d]), g);
+    kmeta[((size_t)u * kblocks + blk) * kD + d] = g.s_bits | (mn << 16);
+  }
+  __syncthreads();
+  for (int task = tid; task < 128 * kw; task += 256) {
+    const int t = task / kw, w = task % kw;
+    const int s = t0 + t;
+    const int d0 = w * nv, d1 = min(kD, d0 + nv);
+    uint32_t word = 0;
+    for (int d = d1 - 1; d >= d0; --d) word = word * (uint32_t)L + cs[t][d];
+    kwords[(((size_t)u * tiles + s / kTile) * kw + w) * kTile + (s % kTile)] = word;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_kchan_window(const uint16_t* __restrict__ k,
+                                                      const uint16_t* __restrict__ v, int64_t sb,
+                                                      int64_t st, int64_t sh, int Hkv, int nq,
+                                                      int nwin, int win_cap,
+                                                      uint16_t* __restrict__ kwin,
+                                                      uint16_t* __restrict__ vwin) {
+  const int u = blockIdx.y;
+  const int b = u / Hkv, h = u % Hkv;
+  for (int e = blockIdx.x * 256 + threadIdx.x; e < win_cap * (kD / 8); e += gridDim.x * 256) {
+    const int i = e / (kD / 8), c8 = (e % (kD / 8)) * 8;
+    uint4 kr = make_uint4(0, 0, 0, 0), vr = make_uint4(0, 0, 0, 0);
+    if (i < nwin) {
+      const int64_t off = b * sb + (int64_t)(nq + i) * st + h * sh + c8;
+      kr = *reinterpret_cast<const uint4*>(k + off);
+      vr = *reinterpret_cast<const uint4*>(v + off);
+    }
+    const size_t o = ((size_t)u * win_cap + i) * kD + c8;
+    *reinterpret_cast<uint4*>(kwin + o) = kr;
+    *reinterpret_cast<uint4*>(vwin + o) = vr;
+  }
+}
+
+__global__ void k_kchan_counters(int32_t* counters, int B, int T, int nq) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < B) {
+    counters[b * 4 + 0] = T;
+    counters[b * 4 + 1] = nq;
+    counters[b * 4 + 2] = T - nq;
+    counters[b * 4 + 3] = 0;
+  }
+}
+
+bool launch_quantize_kchan(const kvq_layout* L, uint8_t* cache, const void* k, const void* v,
+                           int64_t sb, int64_t st, int64_t sh, int T, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  const kvq_config& c = L->cfg;
+  const int U = c.batch * c.kv_heads;
+  const int nq = kchan_nq(L, T);
+  const int nwin = T - nq;
+  if (nwin > L->win_cap) return false;
+  k_kchan_counters<<<ceil_div(c.batch, 64), 64, 0, s>>>((int32_t*)(cache + L->counters), c.batch,
+                                                        T, nq);
+  if (nq > 0) {
+    k_kchan_keys<<<dim3(nq / c.k_block, U), 256, 0, s>>>(
+        (const uint16_t*)k, sb, st, sh, c.kv_heads, c.k_levels, L->nv[0], L->kw[0], L->tiles[0],
+        L->kblocks, c.capacity, c.sparse_per_vec, (uint32_t*)(cache + L->k_words[0]),
+        (uint32_t*)(cache + L->k_meta[0]), (uint32_t*)(cache + L->sparse));
+  }
+  QuantArgs a;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.sb = sb; a.st = st; a.sh = sh;
+  a.inv = nullptr;
+  a.inv_cap = 0;
+  a.n = nq;
+  a.L = c.v_levels; a.nv = L->vnv; a.kw = 0; a.tiles = L->tiles[0]; a.vrows = L->vrows[0];
+  a.Hkv = c.kv_heads;
+  a.kwords = nullptr;
+  a.kmeta = nullptr;
+  a.vwords = (uint32_t*)(cache + L->v_words[0]);
+  a.vmeta = (uint32_t*)(cache + L->v_meta[0]);
+  if (!launch_pool(a, c.v_group, U, s)) return false;
+  k_kchan_window<<<dim3(ceil_div(L->win_cap * (kD / 8), 256), U), 256, 0, s>>>(
+      (const uint16_t*)k, (const uint16_t*)v, sb, st, sh, c.kv_heads, nq, nwin, L->win_cap,
+      (uint16_t*)(cache + L->k_win), (uint16_t*)(cache + L->v_win));
+  return hipGetLastError() == hipSuccess;
+}
+
+// --------------------------------------------------------------- append ----
+// One workgroup per sequence.  Reads the running median, decides the tier,
+// quantizes the new K and V rows of every KV head on that grid, writes them
+// at the tier's next slot, inserts the score into the sorted array and bumps
+// the counters.
+struct AppendArgs {
+  int32_t* counters;
+  uint32_t* tokmap;
+  float* sorted;
+  uint32_t* kwords[2];
+  uint32_t* kmeta[2];
+  uint32_t* vwords[2];
+  uint32_t* vmeta[2];
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const float* score_new;
+  int L[2], nv[2], kw[2], tiles[2], vrows[2], cap[2];
+  int capacity, Hkv, G;
+};
+
+template <int G>
+__global__ __launch_bounds__(256) void k_append(AppendArgs a) {
+  constexpr int NG = kD / G;
+  __shared__ int s_tier, s_len, s_slot, s_ok;
+  __shared__ uint32_t s_le;
+  __shared__ uint8_t codes[2][64][kD];     // [k/v][head][d], Hkv <= 64
+  const int tid = threadIdx.x, b = blockIdx.x;
+  int32_t* cnt = a.counters + b * 4;
+  float* srt = a.sorted + (size_t)b * a.capacity;
+  const float snew = a.score_new[b];
+  if (tid == 0) {
+    const int len = cnt[0];
+    int tier = 1;
+    if (len > 0) {
+      const double m = ((double)srt[(len - 1) / 2] + (double)srt[len / 2]) * 0.5;
+      tier = ((double)snew > m) ? 0 : 1;
+    } else {
+      tier = 0;
+    }
+    const int slot = cnt[1 + tier];
+    s_tier = tier;
+    s_len = len;
+    s_slot = slot;
+    s_ok = (len < a.capacity && slot < a.cap[tier]) ? 1 : 0;
+    s_le = 0;
+  }
+  __syncthreads();
+  if (!s_ok) {
+    if (tid == 0) cnt[3] = 1;
+    return;
+  }
+  const int tier = s_tier, len = s_len, slot = s_slot;
+  const int L = a.L[tier], nv = a.nv[tier], kw = a.kw[tier], tiles = a.tiles[tier],
+            vrows = a.vrows[tier];
+  // position of the new score: number of present scores <= snew
+  uint32_t le = 0;
+  for (int i = tid; i < len; i += 256) le += (srt[i] <= snew) ? 1u : 0u;
+  atomicAdd(&s_le, le);
+  // quantize every (head, k/v, group)
+  for (int task = tid; task < a.Hkv * 2 * NG; task += 256) {
+    const int h = task / (2 * NG), kv = (task / NG) % 2, g = task % NG;
+    const uint16_t* src = (kv ? a.v_new : a.k_new) + ((size_t)b * a.Hkv + h) * kD + g * G;
+    const uint32_t meta = quant_group<G>(src, L, &codes[kv][h][g * G]);
+    const int u = b * a.Hkv + h;
+    uint32_t* mp = kv ? a.vmeta[tier] : a.kmeta[tier];
+    mp[(((size_t)u * tiles + slot / kTile) * NG + g) * kTile + (slot % kTile)] = meta;
+  }
+  __syncthreads();
+  const uint32_t pos = s_le;
+  for (int task = tid; task < a.Hkv * kw; task += 256) {
+    const int h = task / kw, w = task % kw;
+    const int u = b * a.Hkv + h;
+    const int d0 = w * nv, d1 = min(kD, d0 + nv);
+    uint32_t word = 0;
+    for (int d = d1 - 1; d >= d0; --d) word = word * (uint32_t)L + codes[0][h][d];
+    a.kwords[tier][(((size_t)u * tiles + slot / kTile) * kw + w) * kTile + (slot % kTile)] = word;
+  }
+  const int r = slot / nv, j = slot % nv;
+  uint32_t pw = 1;
+  for (int i = 0; i < j; ++i) pw *= (uint32_t)L;
+  for (int task = tid; task < a.Hkv * kD; task += 256) {
+    const int h = task / kD, d = task % kD;
+    const int u = b * a.Hkv + h;
+    uint32_t* wp = &a.vwords[tier][((size_t)u * vrows + r) * kD + d];
+    *wp = *wp + pw * (uint32_t)codes[1][h][d];
+  }
+  // insert the score: shift srt[pos..len) up by one, highest chunk first
+  for (int hi = len; hi > (int)pos; hi -= 256) {
+    const int i = hi - 1 - tid;
+    float val = 0.0f;
+    const bool act = i >= (int)pos;
+    if (act) val = srt[i];
+    __syncthreads();
+    if (act) srt[i + 1] = val;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    srt[pos] = snew;
+    a.tokmap[(size_t)b * a.capacity + len] = (uint32_t)slot | ((uint32_t)tier << 31);
+    cnt[0] = len + 1;
+    cnt[1 + tier] = slot + 1;
+  }
+}
+
+bool launch_append(const kvq_layout* L, uint8_t* cache, const void* k_new, const void* v_new,
+                   const float* score_new, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  const kvq_config& c = L->cfg;
+  if (c.kv_heads > 64) return false;
+  AppendArgs a;
+  a.counters = (int32_t*)(cache + L->counters);
+  a.tokmap = (uint32_t*)(cache + L->tokmap);
+  a.sorted = (float*)(cache + L->sorted);
+  for (int p = 0; p < 2; ++p) {
+    a.kwords[p] = (uint32_t*)(cache + L->k_words[p]);
+    a.kmeta[p] = (uint32_t*)(cache + L->k_meta[p]);
+    a.vwords[p] = (uint32_t*)(cache + L->v_words[p]);
+    a.vmeta[p] = (uint32_t*)(cache + L->v_meta[p]);
+    a.nv[p] = L->nv[p]; a.kw[p] = L->kw[p]; a.tiles[p] = L->tiles[p];
+    a.vrows[p] = L->vrows[p]; a.cap[p] = L->cap[p];
+  }
+  a.L[0] = c.levels_hi;
+  a.L[1] = c.levels_lo;
+  a.k_new = (const uint16_t*)k_new;
+  a.v_new = (const uint16_t*)v_new;
+  a.score_new = score_new;
+  a.capacity = c.capacity;
+  a.Hkv = c.kv_heads;
+  a.G = c.group;
+  switch (c.group) {
+    case 32: k_append<32><<<c.batch, 256, 0, s>>>(a); break;
+    case 64: k_append<64><<<c.batch, 256, 0, s>>>(a); break;
+    case 128: k_append<128><<<c.batch, 256, 0, s>>>(a); break;
+    default: return false;
+  }
+  return hipGetLastError() == hipSuccess;
+}
+
+}  // namespace kvq

@@ -1,0 +1,166 @@
+"""C-ABI boundary: the library loads, exports every declared entry point, and
+validates arguments on the host (no GPU is touched on any path here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from mixed_precision_kv_amd import kvq, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(kvq.LIB_PATH), reason="libkvq.so not built")
+
+FAKE = 1 << 20          # aligned, never dereferenced: every call below fails validation first
+
+
+def declared_symbols():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\S[^;(]*\b(kvq_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_symbols()
+    assert {"kvq_layout_init", "kvq_workspace_bytes", "kvq_status_str", "kvq_quantize",
+            "kvq_append", "kvq_decode_attn"} <= set(names)
+    L = kvq.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_structs_match_header(tmp_path):
+    """Field offsets and sizes of the ctypes structs equal the C compiler's."""
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "kvq.h"', 'int main(void){']
+    for struct, cls in (("kvq_config", kvq.KvqConfig), ("kvq_layout", kvq.KvqLayout)):
+        lines.append(f'printf("{struct} %zu\\n", sizeof({struct}));')
+        for name, _ in cls._fields_:
+            lines.append(f'printf("{struct}.{name} %zu\\n", offsetof({struct}, {name}));')
+    lines.append("return 0;}")
+    src = tmp_path / "probe.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "probe"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                    check=True).stdout.splitlines())
+    for struct, cls in (("kvq_config", kvq.KvqConfig), ("kvq_layout", kvq.KvqLayout)):
+        assert int(got[struct]) == ctypes.sizeof(cls)
+        for name, _ in cls._fields_:
+            assert int(got[f"{struct}.{name}"]) == getattr(cls, name).offset, name
+
+
+@pytest.mark.parametrize("w", synth.CONFIGS, ids=lambda w: w.name)
+def test_layout_of_every_workload(w):
+    lay = kvq.layout_init(kvq.config_for(w))
+    assert lay.total_bytes > 0
+    offs = [lay.counters, lay.tokmap, lay.sorted, *lay.k_words, *lay.k_meta, *lay.v_words,
+            *lay.v_meta, lay.sparse, lay.k_win, lay.v_win]
+    assert all(o % 256 == 0 for o in offs)
+    assert kvq.workspace_bytes(lay, kvq.OP_QUANTIZE, w.tokens) > 0
+    assert kvq.workspace_bytes(lay, kvq.OP_DECODE, w.capacity) > 0
+    if w.mode == "tiered":
+        assert lay.nv[0] == {6: 12, 8: 10}[w.levels_hi]
+        assert lay.kw[1] == {5: 10, 6: 11}[w.levels_lo]
+    else:
+        assert lay.nv[0] == 16 and lay.vnv == 20 and lay.win_cap == 255
+
+
+def _cfg(**kw):
+    c = kvq.config_for(synth.CONFIGS[0])
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=64), 2), (dict(q_heads=8), 2), (dict(levels_hi=2), 2), (dict(levels_lo=17), 2),
+    (dict(group=48), 2), (dict(capacity=0), 1), (dict(batch=0), 1), (dict(mode=7), 1),
+    (dict(cap_hi=100, cap_lo=100), 1), (dict(cap_hi=5000), 1),
+])
+def test_layout_rejects(kw, status):
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.layout_init(_cfg(**kw))
+    assert e.value.status == status
+
+
+def test_kchan_rejects_unsupported():
+    w = synth.CONFIGS[4]
+    for kw in (dict(k_block=64), dict(v_levels=5), dict(window=600), dict(sparse_per_vec=9)):
+        c = kvq.config_for(w)
+        for k, v in kw.items():
+            setattr(c, k, v)
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.layout_init(c)
+        assert e.value.status == 2
+
+
+def test_workspace_bad_args():
+    lay = kvq.layout_init(_cfg())
+    assert kvq.workspace_bytes(lay, kvq.OP_DECODE, 0) == 0
+    assert kvq.workspace_bytes(lay, kvq.OP_DECODE, lay.cfg.capacity + 1) == 0
+    assert kvq.workspace_bytes(lay, 9, 16) == 0
+
+
+def _quant(lay, **over):
+    a = dict(cache=FAKE, k=FAKE, v=FAKE, strides=(4096 * 128, 128, 128), scores=FAKE, T=4096,
+             n_hi=2048, ranks_out=None, ws=FAKE, ws_bytes=1 << 40, stream=0)
+    a.update(over)
+    kvq.quantize(lay, a["cache"], a["k"], a["v"], a["scores"], a["T"], a["n_hi"], a["ranks_out"],
+                 a["ws"], a["ws_bytes"], strides=a["strides"], stream=a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(cache=0), 1), (dict(k=0), 1), (dict(v=FAKE + 4), 1), (dict(scores=0), 1),
+    (dict(T=0), 1), (dict(T=4097), 3), (dict(n_hi=-1), 1), (dict(n_hi=4097), 1),
+    (dict(strides=(4096 * 128, 100, 128)), 1), (dict(strides=(-8, 128, 128)), 1),
+    (dict(ws=0), 4), (dict(ws_bytes=1000), 4), (dict(ranks_out=FAKE + 2), 1),
+])
+def test_quantize_validation(over, status):
+    lay = kvq.layout_init(_cfg())
+    with pytest.raises(kvq.KvqError) as e:
+        _quant(lay, **over)
+    assert e.value.status == status
+
+
+def test_quantize_capacity_per_pool():
+    c = _cfg(capacity=4096, cap_hi=2048, cap_lo=2048)
+    lay = kvq.layout_init(c)
+    with pytest.raises(kvq.KvqError) as e:
+        _quant(lay, n_hi=2049)
+    assert e.value.status == 3
+
+
+def test_append_validation():
+    lay = kvq.layout_init(_cfg())
+    for args in ((0, FAKE, FAKE, FAKE), (FAKE, 0, FAKE, FAKE), (FAKE, FAKE, FAKE + 8, FAKE)):
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.append(lay, *args, stream=0)
+        assert e.value.status == 1
+    lay5 = kvq.layout_init(kvq.config_for(synth.CONFIGS[4]))
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.append(lay5, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.status == 2
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(cache=0), 1), (dict(q=FAKE + 2), 1), (dict(out=0), 1), (dict(scale=0.0), 1),
+    (dict(scale=float("nan")), 1), (dict(max_len=0), 1), (dict(max_len=4097), 3),
+    (dict(ws=0), 4), (dict(ws_bytes=64), 4),
+])
+def test_decode_validation(over, status):
+    lay = kvq.layout_init(_cfg())
+    a = dict(cache=FAKE, q=FAKE, scale=0.088, max_len=4096, out=FAKE, ws=FAKE, ws_bytes=1 << 40)
+    a.update(over)
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.decode_attn(lay, a["cache"], a["q"], a["scale"], a["max_len"], a["out"], a["ws"],
+                        ws_bytes=a["ws_bytes"], stream=0)
+    assert e.value.status == status
+
+
+def test_status_strings():
+    L = kvq.lib()
+    for s in range(6):
+        assert L.kvq_status_str(s)
+    assert L.kvq_status_str(99) == b"unknown status"
