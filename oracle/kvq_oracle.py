@@ -218,8 +218,11 @@ class Pool:
     def add_rows(self, k16: np.ndarray, v16: np.ndarray):
         """Quantize rows [N][D] (per-token groups of G) and append them."""
         N = k16.shape[0]
-        kc, ks, kz = quantize_groups(k16.reshape(N, -1, self.G), self.L)
-        vc, vs, vz = quantize_groups(v16.reshape(N, -1, self.G), self.L)
+        if N == 0:
+            return
+        ng = self.D // self.G
+        kc, ks, kz = quantize_groups(k16.reshape(N, ng, self.G), self.L)
+        vc, vs, vz = quantize_groups(v16.reshape(N, ng, self.G), self.L)
         self.k_codes = np.concatenate([self.k_codes, kc.reshape(N, self.D)])
         self.k_scale = np.concatenate([self.k_scale, ks])
         self.k_zero = np.concatenate([self.k_zero, kz])
@@ -234,13 +237,13 @@ class Pool:
         return pack_cols(self.v_codes, self.L)
 
     def k_hat(self):
-        N = self.n
-        return dequantize_groups(self.k_codes.reshape(N, -1, self.G), self.k_scale,
+        N, ng = self.n, self.D // self.G
+        return dequantize_groups(self.k_codes.reshape(N, ng, self.G), self.k_scale,
                                  self.k_zero).reshape(N, self.D)
 
     def v_hat(self):
-        N = self.n
-        return dequantize_groups(self.v_codes.reshape(N, -1, self.G), self.v_scale,
+        N, ng = self.n, self.D // self.G
+        return dequantize_groups(self.v_codes.reshape(N, ng, self.G), self.v_scale,
                                  self.v_zero).reshape(N, self.D)
 
 
@@ -343,7 +346,9 @@ class KChanUnit:
         kc, self.k_scale, self.k_zero = quantize_groups(np.ascontiguousarray(blk), w.k_levels)
         self.k_codes = kc.transpose(0, 2, 1).reshape(nq, D)               # [n_q][D]
         vc, self.v_scale, self.v_zero = quantize_groups(
-            v_unit[:nq].reshape(nq, D // w.v_group, w.v_group), w.v_levels)
+            v_unit[:nq].reshape(nq, D // w.v_group, w.v_group), w.v_levels) if nq else (
+            np.zeros((0, D // w.v_group, w.v_group), np.uint8), np.zeros((0, D // w.v_group), np.float16),
+            np.zeros((0, D // w.v_group), np.float16))
         self.v_codes = vc.reshape(nq, D)
         self.k_win = k_unit[nq:].copy()
         self.v_win = v_unit[nq:].copy()
@@ -365,7 +370,7 @@ class KChanUnit:
 
     def v_hat(self):
         nq, D = self.v_codes.shape
-        deq = dequantize_groups(self.v_codes.reshape(nq, -1, self.v_group), self.v_scale,
+        deq = dequantize_groups(self.v_codes.reshape(nq, D // self.v_group, self.v_group), self.v_scale,
                                 self.v_zero).reshape(nq, D)
         return np.concatenate([deq, self.v_win.astype(F64)])
 
