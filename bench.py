@@ -1,0 +1,287 @@
+"""Throughput of the mixed-precision KV-cache hot path on one MI355X.
+
+One step = quantize-on-write of the whole batch (rank, tier split, group
+quantize, base-L packing of K and V) followed by one decode-attention step of
+every sequence over the packed cache (split over the context, merged by
+log-sum-exp).  Default workload: the Llama-3.1-8B-shaped decode layer
+(batch 8, 8 KV heads, 32 query heads, head_dim 128, 32768 context tokens,
+6/5 levels, groups of 32).  Inputs are synthetic and resident in HBM before
+the timed region.
+
+Prints one JSON line.  `value` is context tokens per second per query head
+over the whole step (B * Hq * T / step time).  Decode and quantize are also
+timed on their own with HIP events on the stream they run on; the decode
+loop rotates cache replicas so that its reads come from HBM rather than the
+256 MB Infinity Cache.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import multiprocessing as mp
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def packed_decode_bytes(lay, counts):
+    """Algorithmic bytes one decode reads: every packed word and (scale, zero)
+    pair of every stored token, the query and the output."""
+    c = lay.cfg
+    D = c.head_dim
+    total = 0
+    if c.mode == 0:
+        ng = D // c.group
+        for b in range(c.batch):
+            for p in range(2):
+                n = int(counts[b][p])
+                per_unit = n * lay.kw[p] * 4 + 2 * n * ng * 4 + -(-n // lay.nv[p]) * D * 4
+                total += per_unit * c.kv_heads
+    else:
+        raise NotImplementedError
+    total += 2 * c.batch * c.q_heads * D * 2
+    return total
+
+
+def quantize_bytes(w, lay):
+    """Algorithmic bytes of quantize: fp16 K and V and the scores read once;
+    packed cache, token map, sorted scores and ranks written once."""
+    B, T, H, D = w.batch, w.tokens, w.kv_heads, w.head_dim
+    rd = 2 * B * T * H * D * 2 + B * T * 4
+    counts = [[w.n_hi, T - w.n_hi]] * B
+    wr = packed_decode_bytes(lay, counts) - 2 * B * w.q_heads * D * 2 + 3 * B * T * 4
+    return rd + wr
+
+
+def kernel_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "mixed_precision_kv_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, khash):
+    """HBM bytes per launch from committed rocprofv3 PMC summaries, only if the
+    kernel source is unchanged since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tr = json.load(f)
+    e = tr.get(kernel)
+    if not e or e.get("source_hash") != khash:
+        return None
+    return e.get("bytes_per_launch")
+
+
+# ----------------------------------------------------------- cpu baseline ---
+def _oracle_unit(args):
+    import numpy as np
+    from oracle import kvq_oracle as O
+    k_unit, v_unit, inv_b, q_group, w_fields, scale = args
+    L_hi, L_lo, G = w_fields
+    pools = O.quantize_tiered_unit(k_unit, v_unit, inv_b, L_hi, L_lo, G)
+    pools[0].k_words(), pools[0].v_words(), pools[1].k_words(), pools[1].v_words()
+    kh = np.concatenate([pools[0].k_hat(), pools[1].k_hat()])
+    vh = np.concatenate([pools[0].v_hat(), pools[1].v_hat()])
+    return O.decode_unit(q_group, kh, vh, scale)
+
+
+def cpu_baseline(w, inp, scale, max_units, workers):
+    """The oracle as it is (rank + tier split of every sequence; quantize,
+    pack and fp64 attention of a sample of (sequence, KV head) units) on the
+    host, units spread over `workers` processes."""
+    import numpy as np
+    from oracle import kvq_oracle as O
+    os.environ.setdefault("OMP_NUM_THREADS", "1")
+    t0 = time.perf_counter()
+    rank = O.rank_desc(inp.scores)
+    _, _, inv = O.tiers_and_slots(rank, w.n_hi)
+    t_rank = time.perf_counter() - t0
+    g = w.q_heads // w.kv_heads
+    units = [(b, h) for b in range(w.batch) for h in range(w.kv_heads)][:max_units]
+    jobs = [(np.ascontiguousarray(inp.k[b, :, h]), np.ascontiguousarray(inp.v[b, :, h]), inv[b],
+             inp.q[b, h * g:(h + 1) * g].astype(np.float64), (w.levels_hi, w.levels_lo, w.group),
+             scale) for b, h in units]
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(workers) as pool:
+        pool.map(_oracle_unit, jobs, chunksize=1)
+    t_units = time.perf_counter() - t0
+    n_all = w.batch * w.kv_heads
+    t_step = t_rank + t_units * n_all / len(units)        # scale the sample to the batch
+    return dict(value=w.batch * w.q_heads * w.tokens / t_step, unit="context tokens/s per head",
+                cores=workers, kind="oracle",
+                sample=f"rank+tiers of all {w.batch} sequences, quantize+pack+fp64 attention of "
+                       f"{len(units)} of {n_all} (sequence, KV head) units, scaled to the batch",
+                seconds=round(t_rank + t_units, 3))
+
+
+# ------------------------------------------------------------------- main ---
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c2_llama8b_b8_t32k")
+    ap.add_argument("--decode-iters", type=int, default=100)
+    ap.add_argument("--replicas", type=int, default=0, help="decode cache replicas (0: auto, >= 1 GB)")
+    ap.add_argument("--cpu-units", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["all", "decode", "quantize", "copy"], default="all",
+                    help="profiling aid: run just one kernel family (no JSON line)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (see the sharding "
+              "notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from mixed_precision_kv_amd import kvq, synth
+
+    dev = torch.device("cuda:0")
+    w = synth.BY_NAME[args.config]
+    assert w.mode == "tiered", "the step bench covers the tiered workloads"
+    print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(w, steps=0)
+    lay = kvq.layout_init(kvq.config_for(w))
+    stream = torch.cuda.current_stream()
+
+    if args.only == "copy":
+        # plain copy of a known size: calibrates the PMC byte counters
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(f"[bench] copy probe: 5 x {n} bytes", file=sys.stderr)
+        return
+
+    k = torch.from_numpy(inp.k).to(dev)
+    v = torch.from_numpy(inp.v).to(dev)
+    scores = torch.from_numpy(inp.scores).to(dev)
+    q = torch.from_numpy(inp.q).to(dev)
+    out = torch.empty_like(q)
+    ranks = torch.empty((w.batch, w.tokens), dtype=torch.int32, device=dev)
+    wsq = torch.empty(kvq.workspace_bytes(lay, kvq.OP_QUANTIZE, w.tokens), dtype=torch.uint8, device=dev)
+    wsd = torch.empty(kvq.workspace_bytes(lay, kvq.OP_DECODE, w.tokens), dtype=torch.uint8, device=dev)
+    R = args.replicas or max(1, math.ceil(1.0e9 / lay.total_bytes))
+    caches = [torch.zeros(lay.total_bytes, dtype=torch.uint8, device=dev) for _ in range(R)]
+    scale = 1.0 / math.sqrt(w.head_dim)
+
+    def quantize(i):
+        kvq.quantize(lay, caches[i % R], k, v, scores, w.tokens, w.n_hi, ranks, wsq, stream=stream)
+
+    def decode(i):
+        kvq.decode_attn(lay, caches[i % R], q, scale, w.tokens, out, wsd, stream=stream)
+
+    for i in range(R):
+        quantize(i)
+    torch.cuda.synchronize()
+    print(f"[bench] {R} cache replicas of {lay.total_bytes / 1e6:.1f} MB ready", file=sys.stderr, flush=True)
+
+    if args.only == "decode":
+        for i in range(args.decode_iters):
+            decode(i)
+        torch.cuda.synchronize()
+        return
+    if args.only == "quantize":
+        for i in range(args.steps):
+            quantize(i)
+        torch.cuda.synchronize()
+        return
+
+    # ---- the step: quantize then decode, K timed steps
+    for i in range(args.warmup):
+        quantize(i)
+        decode(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        quantize(i)
+        decode(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (wall {wall:.2f} s)", file=sys.stderr, flush=True)
+
+    # ---- per-kernel live timing with events around every call on the same stream
+    def timed(fn, iters):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(iters)]
+        for i in range(iters):
+            evs[i][0].record(stream)
+            fn(i)
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(b) for a, b in evs])
+        return float(np.median(t)), float(np.percentile(t, 10)), float(np.percentile(t, 90))
+
+    for i in range(5):
+        decode(i)
+    dec_med, dec_p10, dec_p90 = timed(decode, args.decode_iters)
+    q_med, q_p10, q_p90 = timed(quantize, max(10, args.steps))
+    counts = [[w.n_hi, w.tokens - w.n_hi]] * w.batch
+    dec_bytes = packed_decode_bytes(lay, counts)
+    q_bytes = quantize_bytes(w, lay)
+    dec_gbs = dec_bytes / (dec_med * 1e-3) / 1e9
+    q_gbs = q_bytes / (q_med * 1e-3) / 1e9
+    ctx_pairs = w.batch * w.q_heads * w.tokens
+    decode_info = dict(ms=dec_med, ms_p10=dec_p10, ms_p90=dec_p90, bytes=dec_bytes, gbs=round(dec_gbs, 1),
+                       frac_hbm=round(dec_gbs / HBM_PEAK_GBS, 4), replicas=R,
+                       ctx_tokens_per_s_per_qhead=ctx_pairs / (dec_med * 1e-3),
+                       ctx_tokens_per_s_per_kvhead=w.batch * w.kv_heads * w.tokens / (dec_med * 1e-3))
+    quant_info = dict(ms=q_med, ms_p10=q_p10, ms_p90=q_p90, bytes=q_bytes, gbs=round(q_gbs, 1),
+                      frac_hbm=round(q_gbs / HBM_PEAK_GBS, 4))
+    dominant = "decode" if dec_med >= q_med else "quantize"
+    if dominant == "decode":
+        khash = kernel_hash("decode.hip")
+        roof = dict(bound="hbm", achieved=round(dec_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(dec_gbs / HBM_PEAK_GBS, 4),
+                    traffic=measured_traffic("decode", khash), kernel="kvq_decode_attn (decode + merge)")
+    else:
+        khash = kernel_hash("quantize.hip", "rank.hip")
+        roof = dict(bound="hbm", achieved=round(q_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(q_gbs / HBM_PEAK_GBS, 4),
+                    traffic=measured_traffic("quantize", khash), kernel="kvq_quantize (rank + quantize)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        workers = max(1, min(16, os.cpu_count() or 1))
+        print(f"[bench] cpu baseline on {workers} workers", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, inp, float(np.float32(scale)), args.cpu_units, workers)
+
+    res = {
+        "metric": "decode-attn over packed KV: context tokens/s per head & HBM GB/s; quantize GB/s",
+        "value": ctx_pairs / (ms_step * 1e-3),
+        "unit": "context tokens/s per query head (quantize + decode step)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) K/V with 4 outlier key channels x10, lognormal scores)",
+        "config": {"workload": w.name, "batch": w.batch, "kv_heads": w.kv_heads, "q_heads": w.q_heads,
+                   "head_dim": w.head_dim, "context": w.tokens, "levels": [w.levels_hi, w.levels_lo],
+                   "group": w.group, "n_hi": w.n_hi},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "decode": decode_info,
+        "quantize": quant_info,
+    }
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -12,15 +12,20 @@ scores, two adjacent fractional-bit grids) and, for ``kchan``, the KVQuant
 per-channel-key / dense-and-sparse scheme (KVQuant summary, "techniques")
 with the SKVQ high-precision recent window (SKVQ abstract).
 
-Draw order for one workload with seed ``s`` (numpy ``Generator(PCG64(s))``):
-keys, values, scores, queries, then per append step (k_new, v_new, score_new,
-q_new).  fp32 normal draws are cast to fp16 with round-to-nearest-even; the
-first ``outlier_channels`` key channels are multiplied by ``outlier_scale``
-in fp32 before the cast.  Scores are fp32 ``exp(sigma * N(0,1))``.
+Streams for one workload with seed ``s``: ``SeedSequence(s).spawn(4 + 4*steps)``
+gives one child per array in the order keys, values, scores, queries, then
+per append step (k_new, v_new, score_new, q_new).  An array is drawn in
+chunks of 2**22 values (whole rows); chunk i uses ``PCG64(child.spawn(n)[i])``,
+so the bytes do not depend on how many threads draw them.  fp32 normal draws
+are cast to fp16 with round-to-nearest-even; the first ``outlier_channels``
+key channels are multiplied by ``outlier_scale`` in fp32 before the cast.
+Scores are fp32 ``exp(sigma * N(0,1))``.
 """
 from __future__ import annotations
 
 import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 from typing import Optional
 
@@ -91,30 +96,39 @@ CONFIGS = [
 BY_NAME = {w.name: w for w in CONFIGS}
 
 
-def _f16_normal(rng: np.random.Generator, shape, chunk: int = 1 << 24) -> np.ndarray:
-    """N(0,1) fp32 draws cast to fp16 (RNE), generated in chunks to bound memory."""
+CHUNK = 1 << 22
+_WORKERS = max(1, min(16, os.cpu_count() or 1))
+
+
+def _draw_f16(seq: np.random.SeedSequence, shape, col_scale=None) -> np.ndarray:
+    """N(0,1) fp32 draws (optionally scaled per last-axis channel in fp32)
+    cast to fp16 (RNE), chunk by chunk from independent child streams."""
     out = np.empty(shape, dtype=np.float16)
     flat = out.reshape(-1)
-    for i in range(0, flat.size, chunk):
-        n = min(chunk, flat.size - i)
-        flat[i:i + n] = rng.standard_normal(n, dtype=np.float32).astype(np.float16)
-    return out
-
-
-def _f16_normal_outliers(rng, shape, n_out: int, scale: float, chunk_rows: int = 1 << 17):
-    """Like ``_f16_normal`` but the first ``n_out`` channels (last axis) are
-    multiplied by ``scale`` in fp32 before the fp16 cast."""
-    out = np.empty(shape, dtype=np.float16)
+    n = flat.size
+    nchunk = max(1, -(-n // CHUNK))
+    kids = seq.spawn(nchunk)
     D = shape[-1]
-    rows = out.reshape(-1, D)
-    sc = np.ones(D, dtype=np.float32)
-    sc[:n_out] = np.float32(scale)
-    for i in range(0, rows.shape[0], chunk_rows):
-        n = min(chunk_rows, rows.shape[0] - i)
-        x = rng.standard_normal((n, D), dtype=np.float32)
-        x *= sc
-        rows[i:i + n] = x.astype(np.float16)
+    assert CHUNK % D == 0
+
+    def job(i):
+        lo, hi = i * CHUNK, min(n, (i + 1) * CHUNK)
+        x = np.random.Generator(np.random.PCG64(kids[i])).standard_normal(hi - lo, dtype=np.float32)
+        if col_scale is not None:
+            x = (x.reshape(-1, D) * col_scale).reshape(-1)
+        flat[lo:hi] = x.astype(np.float16)
+
+    if nchunk == 1:
+        job(0)
+    else:
+        with ThreadPoolExecutor(_WORKERS) as ex:
+            list(ex.map(job, range(nchunk)))
     return out
+
+
+def _draw_scores(seq: np.random.SeedSequence, shape, sigma: float) -> np.ndarray:
+    g = np.random.Generator(np.random.PCG64(seq))
+    return np.exp(np.float32(sigma) * g.standard_normal(shape, dtype=np.float32)).astype(np.float32)
 
 
 @dataclass
@@ -135,21 +149,18 @@ class Inputs:
 
 
 def make_inputs(w: Workload, steps: Optional[int] = None) -> Inputs:
-    rng = np.random.Generator(np.random.PCG64(w.seed))
     B, T, H, Hq, D = w.batch, w.tokens, w.kv_heads, w.q_heads, w.head_dim
-    k = _f16_normal_outliers(rng, (B, T, H, D), w.outlier_channels, w.outlier_scale)
-    v = _f16_normal(rng, (B, T, H, D))
-    scores = None
-    if w.mode == TIERED:
-        scores = np.exp(np.float32(w.score_sigma) *
-                        rng.standard_normal((B, T), dtype=np.float32)).astype(np.float32)
-    q = _f16_normal(rng, (B, Hq, D))
     n_steps = w.append_steps if steps is None else min(steps, w.append_steps)
+    kids = np.random.SeedSequence(w.seed).spawn(4 + 4 * w.append_steps)
+    col = np.ones(D, dtype=np.float32)
+    col[:w.outlier_channels] = np.float32(w.outlier_scale)
+    k = _draw_f16(kids[0], (B, T, H, D), col)
+    v = _draw_f16(kids[1], (B, T, H, D))
+    scores = _draw_scores(kids[2], (B, T), w.score_sigma) if w.mode == TIERED else None
+    q = _draw_f16(kids[3], (B, Hq, D))
     st = []
-    for _ in range(n_steps):
-        kn = _f16_normal(rng, (B, H, D))
-        vn = _f16_normal(rng, (B, H, D))
-        sn = np.exp(rng.standard_normal(B, dtype=np.float32)).astype(np.float32)
-        qn = _f16_normal(rng, (B, Hq, D))
-        st.append(dict(k_new=kn, v_new=vn, score_new=sn, q=qn))
+    for i in range(n_steps):
+        c = kids[4 + 4 * i: 8 + 4 * i]
+        st.append(dict(k_new=_draw_f16(c[0], (B, H, D)), v_new=_draw_f16(c[1], (B, H, D)),
+                       score_new=_draw_scores(c[2], (B,), 1.0), q=_draw_f16(c[3], (B, Hq, D))))
     return Inputs(k=k, v=v, scores=scores, q=q, steps=st)
