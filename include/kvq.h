@@ -60,7 +60,9 @@
  *     call returns a nonzero kvq_status and launches nothing.  A failed
  *     launch returns KVQ_ERR_LAUNCH.  Faults inside kernels surface at the
  *     caller's next synchronization.
- *   - Inputs must be finite.  Group scales must be finite in fp16.
+ *   - Inputs must be finite.  Group scales must be finite in fp16; value
+ *     group scales must stay below 1024 (the decode kernel forms fp16
+ *     products of softmax weights and value scales).
  *   - head_dim must be 128; q_heads / kv_heads must be 4 (grouped-query
  *     attention with four query heads per KV head).
  *   - Calls on one cache must not overlap (the library keeps no locks).

@@ -5,20 +5,22 @@
 
 #include "common.h"
 #include "internal.h"
+#include "tiling.h"
 
 namespace kvq {
 
 static int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
 static bool levels_ok(int L) { return L >= 3 && L <= 16; }
+static bool decode_levels_ok(int L) { return L >= 3 && L <= 8; }
 static bool group_ok(int G) { return G == 32 || G == 64 || G == 128; }
 
 int decode_chunks(const kvq_layout* L, int max_len, int* nch0, int* nch1) {
   if (L->cfg.mode == KVQ_MODE_TIERED) {
     int c0 = L->cap[0] < max_len ? L->cap[0] : max_len;
     int c1 = L->cap[1] < max_len ? L->cap[1] : max_len;
-    *nch0 = ceil_div(c0, decode_chunk_tiered(L->nv[0]));
-    *nch1 = ceil_div(c1, decode_chunk_tiered(L->nv[1]));
+    *nch0 = ceil_div(c0, decode_chunk_slots(L->cfg.levels_hi));
+    *nch1 = ceil_div(c1, decode_chunk_slots(L->cfg.levels_lo));
   } else {
     int nq = kchan_nq(L, max_len);
     *nch0 = ceil_div(nq, decode_chunk_kchan(L));
@@ -74,7 +76,7 @@ extern "C" kvq_status kvq_layout_init(const kvq_config* cfg, kvq_layout* out) {
   const int64_t B = c.batch, U = (int64_t)c.batch * c.kv_heads, D = kD;
   int64_t off = 0;
   if (c.mode == KVQ_MODE_TIERED) {
-    if (!levels_ok(c.levels_hi) || !levels_ok(c.levels_lo) || !group_ok(c.group))
+    if (!decode_levels_ok(c.levels_hi) || !decode_levels_ok(c.levels_lo) || !group_ok(c.group))
       return KVQ_ERR_UNSUPPORTED;
     if (c.cap_hi < 0 || c.cap_lo < 0) return KVQ_ERR_ARG;
     L.cap[0] = c.cap_hi ? c.cap_hi : c.capacity;

@@ -291,24 +291,50 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_kchan(DecodeArgs a) {
   finish_partial(part, sm, sl, accs);
 }
 
-// Log-sum-exp merge of every chunk partial of one unit -> fp16 output.
-__global__ __launch_bounds__(kGqa * kD) void k_merge(const float* __restrict__ part,
-                                                     uint16_t* __restrict__ out, int nch_total,
-                                                     int Hkv) {
-  const int u = blockIdx.x, tid = threadIdx.x;
-  const int hh = tid / kD, d = tid % kD;
+// Log-sum-exp merge of every chunk partial of one (unit, head) -> fp16 output.
+__global__ __launch_bounds__(kD) void k_merge(const float* __restrict__ part,
+                                              uint16_t* __restrict__ out, int nch_total,
+                                              int Hkv) {
+  __shared__ float sw[1024];
+  __shared__ float red[kD];
+  const int u = blockIdx.x, hh = blockIdx.y, d = threadIdx.x;
   const int b = u / Hkv, hk = u % Hkv;
   const float* pu = part + (size_t)u * nch_total * kGqa * kPartStride + hh * kPartStride;
+  const size_t cs = (size_t)kGqa * kPartStride;
   float M = -INFINITY;
-  for (int c = 0; c < nch_total; ++c) M = fmaxf(M, pu[(size_t)c * kGqa * kPartStride]);
-  float l = 0.f, o = 0.f;
+  for (int c = d; c < nch_total; c += kD) M = fmaxf(M, pu[c * cs]);
+  red[d] = M;
+  __syncthreads();
+  for (int o = kD / 2; o > 0; o >>= 1) {
+    if (d < o) red[d] = fmaxf(red[d], red[d + o]);
+    __syncthreads();
+  }
+  M = red[0];
+  __syncthreads();
+  float lsum = 0.f;
+  for (int c = d; c < nch_total; c += kD) {
+    const float m = pu[c * cs];
+    const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
+    if (c < 1024) sw[c] = w;
+    lsum = __builtin_fmaf(pu[c * cs + 1], w, lsum);
+  }
+  red[d] = lsum;
+  __syncthreads();
+  for (int o = kD / 2; o > 0; o >>= 1) {
+    if (d < o) red[d] += red[d + o];
+    __syncthreads();
+  }
+  const float l = red[0];
+  float o = 0.f;
   for (int c = 0; c < nch_total; ++c) {
-    const float* pc = pu + (size_t)c * kGqa * kPartStride;
-    const float m = pc[0];
-    if (m == -INFINITY) continue;
-    const float w = exp2f(m - M);
-    l = __builtin_fmaf(pc[1], w, l);
-    o = __builtin_fmaf(pc[4 + d], w, o);
+    float w;
+    if (c < 1024) {
+      w = sw[c];
+    } else {
+      const float m = pu[c * cs];
+      w = (m == -INFINITY) ? 0.f : exp2f(m - M);
+    }
+    o = __builtin_fmaf(pu[c * cs + 4 + d], w, o);
   }
   out[((size_t)b * Hkv * kGqa + hk * kGqa + hh) * kD + d] = f2h_rne(o / l);
 }
@@ -331,18 +357,25 @@ bool launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, flo
   a.scale_log2 = scale * kLog2e;
   if (c.mode == KVQ_MODE_TIERED) {
     const int lv[2] = {c.levels_hi, c.levels_lo};
+    const int nchp[2] = {nch0, nch1};
     for (int p = 0; p < 2; ++p) {
-      a.kwords[p] = (const uint32_t*)(cache + L->k_words[p]);
-      a.kmeta[p] = (const uint32_t*)(cache + L->k_meta[p]);
-      a.vwords[p] = (const uint32_t*)(cache + L->v_words[p]);
-      a.vmeta[p] = (const uint32_t*)(cache + L->v_meta[p]);
-      a.L[p] = lv[p]; a.nv[p] = L->nv[p]; a.kw[p] = L->kw[p]; a.tiles[p] = L->tiles[p];
-      a.vrows[p] = L->vrows[p];
-      a.chunk[p] = decode_chunk_tiered(L->nv[p]);
+      PoolArgs pa;
+      pa.counters = a.counters;
+      pa.q = a.q;
+      pa.part = a.part;
+      pa.kwords = (const uint32_t*)(cache + L->k_words[p]);
+      pa.kmeta = (const uint32_t*)(cache + L->k_meta[p]);
+      pa.vwords = (const uint32_t*)(cache + L->v_words[p]);
+      pa.vmeta = (const uint32_t*)(cache + L->v_meta[p]);
+      pa.pool = p;
+      pa.Hkv = c.kv_heads;
+      pa.tiles = L->tiles[p];
+      pa.vrows = L->vrows[p];
+      pa.nch_total = nch;
+      pa.part_off = p ? nch0 : 0;
+      pa.c = a.scale_log2;
+      if (nchp[p] > 0 && !launch_decode_pool(lv[p], pa, c.group, nchp[p], U, stream)) return false;
     }
-    a.group = c.group;
-    const int gx = nch0 > nch1 ? nch0 : nch1;
-    k_decode_tiered<<<dim3(gx, U, 2), kDecThreads, 0, s>>>(a);
   } else {
     a.kwords[0] = (const uint32_t*)(cache + L->k_words[0]);
     a.kmeta[0] = (const uint32_t*)(cache + L->k_meta[0]);
@@ -361,7 +394,7 @@ bool launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, flo
     const int gx = nch0 > 1 ? nch0 : 1;
     k_decode_kchan<<<dim3(gx, U, 2), kDecThreads, 0, s>>>(a);
   }
-  k_merge<<<U, kGqa * kD, 0, s>>>((const float*)ws, (uint16_t*)out, nch, c.kv_heads);
+  k_merge<<<dim3(U, kGqa), kD, 0, s>>>((const float*)ws, (uint16_t*)out, nch, c.kv_heads);
   return hipGetLastError() == hipSuccess;
 }
 

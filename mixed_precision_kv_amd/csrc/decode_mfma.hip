@@ -1,0 +1,388 @@
+// Decode attention over one tier pool on the matrix cores (gfx950
+// v_mfma_f32_16x16x32_f16).  SemKV, Abstract: attention reads every kept
+// token; KVQuant summary: small-batch decode is memory-bound, so packed words
+// are read once and expanded in registers.
+//
+// One wave per (chunk of slots, sequence x KV head).  Per 16-slot key tile:
+//   lane (n = slot, j) owns row words j, j+4, j+8, ... of slot n; their base-L
+//   digits, as fp16, are the B operand directly.  The A operand is the query
+//   of the four heads spread over 16 rows (sub-group of 32 channels x head),
+//   zero outside its sub-group, so the result row (g, h) of column n is the
+//   partial dot sum_{d in g} q_h[d] c_d of slot n.  Lane (n, g) holds rows
+//   (g, 0..3) and the (scale, zero) of group g of slot n, so it forms
+//     s_g * P + z_g * sum_{d in g} q_h[d]
+//   and a reduce-scatter across the four lanes of slot n (two permlane
+//   swaps) leaves lane (n, h) with the score of head h.
+// Values are stored in column words (n_L consecutive slots of one channel),
+// so the slot axis is the lane's contraction axis: B[k = slot][col = channel]
+// comes straight out of the words; A[(g, h)][slot] = p_h * s_g(slot) is
+// assembled from LDS; the zero-point term sum p_h z_g is accumulated on the
+// VALU.  Online softmax (base 2) per macro tile; partials (m, l, acc) go to
+// the workspace for the log-sum-exp merge.
+#include "common.h"
+#include "internal.h"
+#include "tiling.h"
+#include "digits.h"
+
+namespace kvq {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int kPartF = 4 + kD;      // floats per head in a partial: m, l, pad, pad, acc[128]
+constexpr float kAScale = 64.0f;    // value-operand weights carry 2^6 (fp16 range)
+
+// Position of (word, digit) in the extraction order of Digits<L, NW>.
+template <class Dg>
+__host__ __device__ constexpr int digit_pos(int word, int digit) {
+  for (int t = 0; t < Dg::NOUT; ++t)
+    if (Dg::word_of(t) == word && Dg::digit_of(t) == digit) return t;
+  return -1;
+}
+
+__device__ inline float dpp_ror(float v, int n) {
+  // row_ror:n within each row of 16 lanes
+  int x = __float_as_int(v);
+  int r;
+  switch (n) {
+    case 8: r = __builtin_amdgcn_update_dpp(x, x, 0x128, 0xF, 0xF, false); break;
+    case 4: r = __builtin_amdgcn_update_dpp(x, x, 0x124, 0xF, 0xF, false); break;
+    case 2: r = __builtin_amdgcn_update_dpp(x, x, 0x122, 0xF, 0xF, false); break;
+    default: r = __builtin_amdgcn_update_dpp(x, x, 0x121, 0xF, 0xF, false); break;
+  }
+  return __int_as_float(r);
+}
+__device__ inline float row_max16(float v) {
+  v = fmaxf(v, dpp_ror(v, 8));
+  v = fmaxf(v, dpp_ror(v, 4));
+  v = fmaxf(v, dpp_ror(v, 2));
+  v = fmaxf(v, dpp_ror(v, 1));
+  return v;
+}
+__device__ inline float row_sum16(float v) {
+  v += dpp_ror(v, 8);
+  v += dpp_ror(v, 4);
+  v += dpp_ror(v, 2);
+  v += dpp_ror(v, 1);
+  return v;
+}
+
+// Lane (n, g) holds x[h], h = 0..3, for slot n and sub-group g.  Returns, in
+// lane (n, r), the sum over g of x[r] (r = lane / 16).
+__device__ inline float reduce_scatter4(f4 x) {
+  auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[0]), __float_as_uint(x[2]), false, false);
+  auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[1]), __float_as_uint(x[3]), false, false);
+  const float y0 = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);
+  const float y1 = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
+  auto s01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(y0), __float_as_uint(y1), false, false);
+  return __uint_as_float(s01[0]) + __uint_as_float(s01[1]);
+}
+
+typedef __amdgpu_buffer_rsrc_t BufRes;
+constexpr uint32_t kOutOfRange = 0x80000000u;   // beyond every region: reads 0
+
+__device__ inline BufRes make_res(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ inline uint32_t bload(BufRes r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, 0);
+}
+
+template <int L, int G>
+__global__ __launch_bounds__(64) void k_decode_pool(PoolArgs a) {
+  using T = Tiling<L>;
+  constexpr int NV = T::NV, KW = T::KW, KWL = T::KWL, R = T::R, RUN = T::RUN, MT = T::MT,
+                KT = T::KT;
+  using DK = Digits<L, KWL>;                 // key words of one lane
+  using DV = Digits<L, R>;                   // value words of one lane and channel tile
+  constexpr int KM = DK::NOUT / 8, VM = DV::NOUT / 8;
+  constexpr bool AFF = DK::kAffine;
+  constexpr float MUL = (float)DK::kMul;
+  constexpr int NG = kD / G;                 // (scale, zero) groups per row
+  constexpr int SUB = G / 32;                // 32-channel sub-groups per group
+  constexpr int VK = VM * 8;                 // padded slot run per lane group
+  constexpr int CH = decode_chunk_slots(L);
+  constexpr int META = KT * NG * 16;         // (scale, zero) words per macro tile
+  constexpr int META_PER_LANE = (META + 63) / 64;
+
+  __shared__ float qf[kGqa][kD];
+  __shared__ float s_lds[kGqa][MT];          // scores of the macro tile, slot order
+  __shared__ float p_lds[kGqa][4 * VK];      // weights in lane-group / digit order
+  __shared__ float vs_lds[NG][4 * VK];       // value scale (x MUL x 2^6), same order
+  __shared__ float vz_lds[NG][4 * VK];       // value zero (affine-corrected), same order
+  __shared__ int ppos_lds[MT];               // slot -> position in that order
+  __shared__ int mpos_lds[64 * META_PER_LANE];
+  __shared__ float zred[16];
+
+  set_f16_round_toward_zero();
+  const int lane = threadIdx.x;
+  const int n = lane & 15, j = lane >> 4;    // B/C-operand view: slot/channel n, group j
+  const int c = blockIdx.x, u = blockIdx.y;
+  const int b = u / a.Hkv, hk = u % a.Hkv;
+  float* part = a.part + ((size_t)u * a.nch_total + a.part_off + c) * kGqa * kPartF;
+  const int n_valid = a.counters[b * 4 + 1 + a.pool];
+  const int s_begin = c * CH;
+  const int s_end = min(n_valid, s_begin + CH);
+  if (s_begin >= s_end) {
+    for (int i = lane; i < kGqa * kPartF; i += 64) part[i] = (i % kPartF == 0) ? -INFINITY : 0.f;
+    return;
+  }
+  // Buffer resources bounded to this unit's regions: an out-of-range offset
+  // reads 0 in hardware, so no load needs a guard (guards would turn into
+  // branches and break the compiler's wait counting).
+  const BufRes rK = make_res(a.kwords + (size_t)u * a.tiles * KW * 16, a.tiles * KW * 16 * 4);
+  const BufRes rKM = make_res(a.kmeta + (size_t)u * a.tiles * NG * 16, a.tiles * NG * 16 * 4);
+  const BufRes rVM = make_res(a.vmeta + (size_t)u * a.tiles * NG * 16, a.tiles * NG * 16 * 4);
+  const BufRes rV = make_res(a.vwords + (size_t)u * a.vrows * kD, a.vrows * kD * 4);
+  uint32_t kwoff[KWL];                       // byte offset of this lane's words in a tile
+#pragma unroll
+  for (int wi = 0; wi < KWL; ++wi) {
+    const int w = j + 4 * wi;
+    kwoff[wi] = w < KW ? (uint32_t)(w * 16 + n) * 4u : kOutOfRange;
+  }
+  const uint32_t kmoff = (uint32_t)((j / SUB) * 16 + n) * 4u;
+
+  // Loads of a whole macro tile, issued in the order they are consumed (key
+  // tiles, value (scale, zero), value words): the vector-memory counter is
+  // in-order, so waiting for one load waits for every older one.
+  struct MacroBuf {
+    uint32_t kw[KT][KWL];
+    uint32_t km[KT];
+    uint32_t vm[META_PER_LANE];
+    uint32_t vw[8][R];
+  };
+  auto load_macro = [&](MacroBuf& mb, int s0) {
+    const uint32_t tile0 = s0 / 16;
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+#pragma unroll
+      for (int wi = 0; wi < KWL; ++wi) mb.kw[t][wi] = bload(rK, kwoff[wi] + (tile0 + t) * (KW * 16 * 4));
+      mb.km[t] = bload(rKM, kmoff + (tile0 + t) * (NG * 16 * 4));
+    }
+#pragma unroll
+    for (int k = 0; k < META_PER_LANE; ++k) {
+      const int e = lane + 64 * k;
+      const uint32_t off = (META % 64 == 0 || e < META) ? (tile0 * NG * 16 + e) * 4u : kOutOfRange;
+      mb.vm[k] = bload(rVM, off);
+    }
+    const uint32_t row0 = s0 / NV + j * R;
+#pragma unroll
+    for (int v = 0; v < 8; ++v)
+#pragma unroll
+      for (int r2 = 0; r2 < R; ++r2) mb.vw[v][r2] = bload(rV, ((row0 + r2) * kD + 16 * v + n) * 4u);
+  };
+  MacroBuf nxt;
+  load_macro(nxt, s_begin);
+
+  // ---- query: fp32 copy in LDS, per-(sub-group, head) sums, A operands
+  for (int i = lane; i < kGqa * kD; i += 64)
+    qf[i / kD][i % kD] = h2f(a.q[((size_t)b * a.Hkv * kGqa + hk * kGqa) * kD + i]);
+  for (int sl = lane; sl < MT; sl += 64) {
+    const int jj = sl / RUN, rem = sl % RUN;
+    ppos_lds[sl] = jj * VK + digit_pos<DV>(rem / NV, rem % NV);
+  }
+  for (int e = lane; e < 64 * META_PER_LANE; e += 64) {
+    const int ee = min(e, META - 1);
+    const int sl = (ee / (NG * 16)) * 16 + (ee % 16);
+    const int jj = sl / RUN, rem = sl % RUN;
+    mpos_lds[e] = jj * VK + digit_pos<DV>(rem / NV, rem % NV);
+  }
+  for (int i = lane; i < 4 * VK; i += 64) {
+    for (int h = 0; h < 4; ++h) p_lds[h][i] = 0.f;
+    for (int g = 0; g < NG; ++g) { vs_lds[g][i] = 0.f; vz_lds[g][i] = 0.f; }
+  }
+  __syncthreads();
+  float qc[4];                               // lane (n, g): c * sum_{d in g} q_h[d]
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    float s = 0.f;
+    for (int d = 32 * j; d < 32 * j + 32; ++d) s += qf[h][d];
+    qc[h] = s * a.c;
+  }
+  h8 aq[KM];
+  {
+    const int r = n, g = r >> 2, h = r & 3;  // A-operand view: row r, k-range of group j
+    const int nw = (KW - j + 3) / 4;         // words this lane group owns
+#pragma unroll
+    for (int m = 0; m < KM; ++m)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int t = 8 * m + i;
+        const int wi = DK::word_of(t);
+        const int d = (j + 4 * wi) * NV + DK::digit_of(t);
+        const bool ok = wi >= 0 && wi < nw && d < kD && (d >> 5) == g;
+        const float qv = qf[h][min(max(d, 0), kD - 1)];
+        aq[m][i] = (_Float16)(ok ? qv : 0.0f);                    // q is fp16: exact
+      }
+  }
+  int mpos[META_PER_LANE];
+#pragma unroll
+  for (int k = 0; k < META_PER_LANE; ++k) mpos[k] = mpos_lds[lane + 64 * k];
+
+  float m_run = -INFINITY, l_run = 0.f, zacc = 0.f;
+  f4 acc[8];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) acc[v] = (f4){0.f, 0.f, 0.f, 0.f};
+
+  for (int s0 = s_begin; s0 < s_end; s0 += MT) {
+    const MacroBuf cur = nxt;
+    if (s0 + MT < s_end) load_macro(nxt, s0 + MT);
+    // ---- scores of the key tiles
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      _Float16 dg[DK::NOUT];
+      DK::run(cur.kw[t], dg);
+      f4 pr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < KM; ++m) {
+        h8 bk;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) bk[i] = dg[8 * m + i];
+        pr = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[m], bk, pr, 0, 0, 0);
+      }
+      const uint32_t meta = cur.km[t];
+      const float sg = h2f(meta & 0xFFFFu) * MUL;
+      const float ssc = sg * a.c, zz = AFF ? h2f(meta >> 16) - sg : h2f(meta >> 16);
+      f4 x;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) x[h] = __builtin_fmaf(ssc, pr[h], zz * qc[h]);
+      float sc = reduce_scatter4(x);
+      sc = (s0 + 16 * t + n < s_end) ? sc : -INFINITY;
+      mx = fmaxf(mx, sc);
+      s_lds[j][16 * t + n] = sc;
+    }
+    // ---- online softmax (lane (n, h): head h)
+    mx = row_max16(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    float ls = 0.f;
+#pragma unroll 2
+    for (int t = 0; t < KT; ++t) {
+      const float p = __builtin_amdgcn_exp2f(s_lds[j][16 * t + n] - m_use);
+      ls += p;
+      p_lds[j][ppos_lds[16 * t + n]] = p;
+    }
+    l_run = __builtin_fmaf(l_run, alpha, ls);
+    m_run = m_new;
+    const float al0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 0));
+    const float al1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 16));
+    const float al2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 32));
+    const float al3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 48));
+    if (!(al0 == 1.f && al1 == 1.f && al2 == 1.f && al3 == 1.f)) {
+      // acc rows are (g, h) with h = register index; zero-point sums are per
+      // (g, h) in the A-operand view (h = n & 3)
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        acc[v][0] *= al0; acc[v][1] *= al1; acc[v][2] *= al2; acc[v][3] *= al3;
+      }
+      const int hz = n & 3;
+      zacc *= hz == 0 ? al0 : hz == 1 ? al1 : hz == 2 ? al2 : al3;
+    }
+    // ---- value (scale, zero) in operand order.  Operand digits are 1 + d/MUL
+    // on power-of-two grids: fold the affine map; the A operand carries an
+    // extra 2^6 (undone at the end) so small weights stay out of the fp16
+    // subnormal range.
+#pragma unroll
+    for (int k = 0; k < META_PER_LANE; ++k) {
+      const int e = lane + 64 * k;
+      if (META % 64 == 0 || e < META) {
+        const int g = (e / 16) % NG;
+        const float sv = h2f(cur.vm[k] & 0xFFFFu) * MUL, zv = h2f(cur.vm[k] >> 16);
+        vs_lds[g][mpos[k]] = sv * kAScale;
+        vz_lds[g][mpos[k]] = AFF ? zv - sv : zv;
+      }
+    }
+    __syncthreads();
+    // ---- value operand A[(g, h)][slot] = p_h * s_g, zero-point term on the VALU
+    h8 av[VM];
+    {
+      const int r = n, g = (r >> 2) / SUB, h = r & 3;
+#pragma unroll
+      for (int m = 0; m < VM; ++m) {
+        const float* pp = &p_lds[h][j * VK + 8 * m];
+        const float* ss = &vs_lds[g][j * VK + 8 * m];
+        const float* zp = &vz_lds[g][j * VK + 8 * m];
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+          // fp32 -> fp16 rounding half up: add half an fp16 spacing to the fp32
+          // bits, then the truncating pack (unbiased, unlike truncation alone:
+          // the value sum cancels against the zero-point sum, so a bias would
+          // be amplified)
+          const float x0 = __uint_as_float(__float_as_uint(pp[i] * ss[i]) + 0x1000u);
+          const float x1 = __uint_as_float(__float_as_uint(pp[i + 1] * ss[i + 1]) + 0x1000u);
+          const h2v vv = __builtin_bit_cast(h2v, __builtin_amdgcn_cvt_pkrtz(x0, x1));
+          av[m][i] = vv[0];
+          av[m][i + 1] = vv[1];
+          zacc = __builtin_fmaf(pp[i], zp[i], zacc);
+          zacc = __builtin_fmaf(pp[i + 1], zp[i + 1], zacc);
+        }
+      }
+    }
+    // ---- value words -> B operands, 8 channel tiles of 16
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      _Float16 dg[DV::NOUT];
+      DV::run(cur.vw[v], dg);
+#pragma unroll
+      for (int m = 0; m < VM; ++m) {
+        h8 bv;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) bv[i] = dg[8 * m + i];
+        acc[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[m], bv, acc[v], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- partials: m, l per head; acc rows (g = j, h) hold channels of sub-group j
+  const float l_tot = row_sum16(l_run);
+  float zs = zacc;                           // lanes (r, j) -> sum over j, r = 4 g + h
+  zs += __shfl_xor(zs, 16);
+  zs += __shfl_xor(zs, 32);
+  if (lane < 16) zred[lane] = zs;
+  __syncthreads();
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    if ((v >> 1) != j) continue;             // channels 16v..16v+15 belong to sub-group v/2
+    const int d = 16 * v + n;
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      part[h * kPartF + 4 + d] = __builtin_fmaf(acc[v][h], 1.0f / kAScale, zred[4 * j + h]);
+  }
+  if (n == 0) {
+    part[j * kPartF + 0] = m_run;
+    part[j * kPartF + 1] = l_tot;
+  }
+}
+
+template <int L, int G>
+static void launch_one(const PoolArgs& a, int nch, int U, hipStream_t s) {
+  k_decode_pool<L, G><<<dim3(nch, U), 64, 0, s>>>(a);
+}
+
+template <int L>
+static bool launch_L(const PoolArgs& a, int G, int nch, int U, hipStream_t s) {
+  switch (G) {
+    case 32: launch_one<L, 32>(a, nch, U, s); return true;
+    case 64: launch_one<L, 64>(a, nch, U, s); return true;
+    case 128: launch_one<L, 128>(a, nch, U, s); return true;
+  }
+  return false;
+}
+
+bool launch_decode_pool(int L, const PoolArgs& a, int G, int nch, int U, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  switch (L) {
+    case 3: return launch_L<3>(a, G, nch, U, s);
+    case 4: return launch_L<4>(a, G, nch, U, s);
+    case 5: return launch_L<5>(a, G, nch, U, s);
+    case 6: return launch_L<6>(a, G, nch, U, s);
+    case 7: return launch_L<7>(a, G, nch, U, s);
+    case 8: return launch_L<8>(a, G, nch, U, s);
+  }
+  return false;
+}
+
+}  // namespace kvq

@@ -9,13 +9,6 @@ namespace kvq {
 
 constexpr int kSortTile = 4096;   // keys per radix-sort block (256 threads x 16)
 
-// Decode chunking: slots per split-K chunk for a pool with nv codes per value
-// word (a whole number of 16-slot key tiles and of value word rows).
-inline int decode_chunk_tiered(int nv) {
-  int unit = 16 * nv;
-  int m = 640 / unit;
-  return unit * (m < 1 ? 1 : m);
-}
 inline int gcd_i(int a, int b) { while (b) { int t = a % b; a = b; b = t; } return a; }
 inline int lcm_i(int a, int b) { return a / gcd_i(a, b) * b; }
 inline int decode_chunk_kchan(const kvq_layout* L) {
@@ -47,5 +40,19 @@ bool launch_append(const kvq_layout* L, uint8_t* cache, const void* k_new, const
                    const float* score_new, void* stream);
 bool launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, float scale,
                    int max_len, void* out, uint8_t* ws, void* stream);
+
+// One tier pool of the matrix-core decode kernel.
+struct PoolArgs {
+  const int32_t* counters;
+  const uint16_t* q;
+  float* part;
+  const uint32_t* kwords;
+  const uint32_t* kmeta;
+  const uint32_t* vwords;
+  const uint32_t* vmeta;
+  int pool, Hkv, tiles, vrows, nch_total, part_off;
+  float c;            // softmax scale * log2(e)
+};
+bool launch_decode_pool(int L, const PoolArgs& a, int G, int nch, int U, void* stream);
 
 }  // namespace kvq
