@@ -19,8 +19,9 @@ int decode_chunks(const kvq_layout* L, int max_len, int* nch0, int* nch1) {
   if (L->cfg.mode == KVQ_MODE_TIERED) {
     int c0 = L->cap[0] < max_len ? L->cap[0] : max_len;
     int c1 = L->cap[1] < max_len ? L->cap[1] : max_len;
-    *nch0 = ceil_div(c0, decode_chunk_slots(L->cfg.levels_hi));
-    *nch1 = ceil_div(c1, decode_chunk_slots(L->cfg.levels_lo));
+    // workspace bound: the finest split, one macro tile per chunk
+    *nch0 = ceil_div(c0, macro_tile_slots(L->cfg.levels_hi));
+    *nch1 = ceil_div(c1, macro_tile_slots(L->cfg.levels_lo));
   } else {
     int nq = kchan_nq(L, max_len);
     *nch0 = ceil_div(nq, decode_chunk_kchan(L));

@@ -357,7 +357,14 @@ bool launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, flo
   a.scale_log2 = scale * kLog2e;
   if (c.mode == KVQ_MODE_TIERED) {
     const int lv[2] = {c.levels_hi, c.levels_lo};
-    const int nchp[2] = {nch0, nch1};
+    int chunk[2], nchp[2];
+    for (int p = 0; p < 2; ++p) {
+      const int slots = L->cap[p] < max_len ? L->cap[p] : max_len;
+      chunk[p] = decode_pool_chunk(lv[p], c.group, U, slots);
+      nchp[p] = ceil_div(slots, chunk[p]);
+    }
+    const int nch_used = nchp[0] + nchp[1];
+    if (nch_used > nch) return false;          // workspace is sized for the finest split
     for (int p = 0; p < 2; ++p) {
       PoolArgs pa;
       pa.counters = a.counters;
@@ -371,11 +378,14 @@ bool launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, flo
       pa.Hkv = c.kv_heads;
       pa.tiles = L->tiles[p];
       pa.vrows = L->vrows[p];
-      pa.nch_total = nch;
-      pa.part_off = p ? nch0 : 0;
+      pa.nch_total = nch_used;
+      pa.part_off = p ? nchp[0] : 0;
+      pa.chunk = chunk[p];
       pa.c = a.scale_log2;
       if (nchp[p] > 0 && !launch_decode_pool(lv[p], pa, c.group, nchp[p], U, stream)) return false;
     }
+    k_merge<<<dim3(U, kGqa), kD, 0, s>>>((const float*)ws, (uint16_t*)out, nch_used, c.kv_heads);
+    return hipGetLastError() == hipSuccess;
   } else {
     a.kwords[0] = (const uint32_t*)(cache + L->k_words[0]);
     a.kmeta[0] = (const uint32_t*)(cache + L->k_meta[0]);

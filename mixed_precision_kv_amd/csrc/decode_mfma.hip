@@ -101,7 +101,6 @@ __global__ __launch_bounds__(64) void k_decode_pool(PoolArgs a) {
   constexpr int NG = kD / G;                 // (scale, zero) groups per row
   constexpr int SUB = G / 32;                // 32-channel sub-groups per group
   constexpr int VK = VM * 8;                 // padded slot run per lane group
-  constexpr int CH = decode_chunk_slots(L);
   constexpr int META = KT * NG * 16;         // (scale, zero) words per macro tile
   constexpr int META_PER_LANE = (META + 63) / 64;
 
@@ -121,8 +120,8 @@ __global__ __launch_bounds__(64) void k_decode_pool(PoolArgs a) {
   const int b = u / a.Hkv, hk = u % a.Hkv;
   float* part = a.part + ((size_t)u * a.nch_total + a.part_off + c) * kGqa * kPartF;
   const int n_valid = a.counters[b * 4 + 1 + a.pool];
-  const int s_begin = c * CH;
-  const int s_end = min(n_valid, s_begin + CH);
+  const int s_begin = c * a.chunk;
+  const int s_end = min(n_valid, s_begin + a.chunk);
   if (s_begin >= s_end) {
     for (int i = lane; i < kGqa * kPartF; i += 64) part[i] = (i % kPartF == 0) ? -INFINITY : 0.f;
     return;
@@ -362,6 +361,14 @@ static void launch_one(const PoolArgs& a, int nch, int U, hipStream_t s) {
   k_decode_pool<L, G><<<dim3(nch, U), 64, 0, s>>>(a);
 }
 
+template <int L, int G>
+static int occupancy_one() {
+  int blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_decode_pool<L, G>, 64, 0) != hipSuccess)
+    return 0;
+  return blocks;
+}
+
 template <int L>
 static bool launch_L(const PoolArgs& a, int G, int nch, int U, hipStream_t s) {
   switch (G) {
@@ -370,6 +377,56 @@ static bool launch_L(const PoolArgs& a, int G, int nch, int U, hipStream_t s) {
     case 128: launch_one<L, 128>(a, nch, U, s); return true;
   }
   return false;
+}
+
+template <int L>
+static int occupancy_L(int G) {
+  switch (G) {
+    case 32: return occupancy_one<L, 32>();
+    case 64: return occupancy_one<L, 64>();
+    case 128: return occupancy_one<L, 128>();
+  }
+  return 0;
+}
+
+static int occupancy(int L, int G) {
+  switch (L) {
+    case 3: return occupancy_L<3>(G);
+    case 4: return occupancy_L<4>(G);
+    case 5: return occupancy_L<5>(G);
+    case 6: return occupancy_L<6>(G);
+    case 7: return occupancy_L<7>(G);
+    case 8: return occupancy_L<8>(G);
+  }
+  return 0;
+}
+
+int decode_pool_chunk(int L, int G, int U, int slots_per_unit) {
+  static int cus = -1;
+  static int occ[17][3];
+  static bool have[17][3];
+  const int gi = G == 32 ? 0 : G == 64 ? 1 : 2;
+  const int mt = macro_tile_slots(L);
+  if (cus < 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+      cus = n;
+    else
+      cus = 0;
+  }
+  if (!have[L][gi]) {
+    occ[L][gi] = occupancy(L, G);
+    have[L][gi] = true;
+  }
+  const long waves = (long)cus * occ[L][gi];
+  if (waves <= 0 || slots_per_unit <= 0) return 8 * mt;
+  // macro tiles per wave so that U * chunks ~ waves (one round of the chip)
+  const long tiles_per_unit = (slots_per_unit + mt - 1) / mt;
+  long m = (tiles_per_unit * U + waves - 1) / waves;
+  if (m < 1) m = 1;
+  if (m > tiles_per_unit) m = tiles_per_unit;
+  return (int)(m * mt);
 }
 
 bool launch_decode_pool(int L, const PoolArgs& a, int G, int nch, int U, void* stream) {

@@ -51,8 +51,12 @@ struct PoolArgs {
   const uint32_t* vwords;
   const uint32_t* vmeta;
   int pool, Hkv, tiles, vrows, nch_total, part_off;
+  int chunk;          // slots per workgroup (a whole number of macro tiles)
   float c;            // softmax scale * log2(e)
 };
+// Slots per workgroup for one pool so that the grid fills the chip about once
+// (uses the kernel's occupancy; falls back to 8 macro tiles).
+int decode_pool_chunk(int L, int G, int U, int slots_per_unit);
 bool launch_decode_pool(int L, const PoolArgs& a, int G, int nch, int U, void* stream);
 
 }  // namespace kvq

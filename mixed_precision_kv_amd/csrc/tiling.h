@@ -43,12 +43,9 @@ struct Tiling {
   static_assert(MT % 16 == 0, "macro tile must hold whole key tiles");
 };
 
-// Slots one decode workgroup covers for a pool with L levels.
-__host__ __device__ constexpr int decode_chunk_slots(int L) {
-  int nv = cpw(L);
-  int mt = 4 * macro_rows(nv) * nv;
-  int m = 512 / mt;
-  return mt * (m < 1 ? 1 : m);
+// Slots of one macro tile for a pool with L levels (the unit of decode work).
+__host__ __device__ constexpr int macro_tile_slots(int L) {
+  return 4 * macro_rows(cpw(L)) * cpw(L);
 }
 
 }  // namespace kvq
