@@ -10,6 +10,7 @@
 // values (column words).
 #include "common.h"
 #include "internal.h"
+#include "digits.h"
 
 namespace kvq {
 
@@ -113,10 +114,177 @@ __global__ __launch_bounds__(kQThreads) void k_quant_pool(QuantArgs a) {
   }
 }
 
+// ---- row kernel: one thread per slot row (fast path, L <= 8) ----
+//
+// Thread i of a workgroup owns slot s0 + i: it loads the token's 128-value key
+// row, finds each group's min/max with packed fp16 min/max (IEEE min/max do
+// not order -0 and +0, so a zero result is redone in the total order), forms
+// the fp16 scale and zero, computes every code with the exact quotient of
+// group_setup/quant_value, and Horner-packs the row words in fp32 halves
+// (exact below 2^24) joined by one 24-bit integer multiply-add.  The value
+// row is coded the same way into LDS bytes; column words are packed after a
+// barrier by (row, channel) tasks.
+template <int L>
+struct RowPack {
+  static constexpr int NV = cpw(L);
+  static constexpr int KW = (kD + NV - 1) / NV;
+  static constexpr int LO = NV / 2;               // low digits per word (L^LO < 2^24)
+  static constexpr uint32_t LPOW_LO = ipow(L, LO);
+};
+
+template <int G>
+__device__ inline void group_minmax(const uint32_t* x2, int g, uint32_t& mn, uint32_t& mx) {
+  // x2: 64 packed fp16 pairs of the row; group g covers pairs [g*G/2, (g+1)*G/2)
+  h2v lo = h2_from_bits(x2[g * G / 2]), hi = lo;
+#pragma unroll
+  for (int i = 1; i < G / 2; ++i) {
+    const h2v v = h2_from_bits(x2[g * G / 2 + i]);
+    lo = __builtin_elementwise_min(lo, v);
+    hi = __builtin_elementwise_max(hi, v);
+  }
+  const _Float16 m0 = lo[0] < lo[1] ? lo[0] : lo[1];
+  const _Float16 m1 = hi[0] > hi[1] ? hi[0] : hi[1];
+  mn = __builtin_bit_cast(uint16_t, m0);
+  mx = __builtin_bit_cast(uint16_t, m1);
+  if (((mn & 0x7FFFu) == 0u) || ((mx & 0x7FFFu) == 0u)) {
+    // a zero extreme: settle -0 / +0 in the IEEE total order
+    int kmn = 0x7FFFFFFF, kmx = -0x7FFFFFFF;
+    for (int i = 0; i < G / 2; ++i) {
+      const uint32_t w = x2[g * G / 2 + i];
+      const int k0 = f16_order_key(w & 0xFFFFu), k1 = f16_order_key(w >> 16);
+      kmn = min(kmn, min(k0, k1));
+      kmx = max(kmx, max(k0, k1));
+    }
+    mn = f16_from_order_key(kmn);
+    mx = f16_from_order_key(kmx);
+  }
+}
+
+__device__ inline float code_of(_Float16 x, const GroupQ& g) {
+  // c = clamp(rint(fl32(x - z) / s), 0, L-1); s == 0 -> 0 (r = 0 makes q = 0)
+  const float a = __builtin_fmaf((float)x, 1.0f, -g.z);   // fl32(x - z), one rounding
+  const float q0 = a * g.r;
+  const float rho = __builtin_fmaf(-q0, g.s, a);
+  const float q = __builtin_fmaf(rho, g.r, q0);
+  return fminf(__builtin_rintf(q), g.top);
+}
+
+template <int L, int G>
+__global__ __launch_bounds__(kQThreads) void k_quant_rows(QuantArgs a) {
+  using P = RowPack<L>;
+  constexpr int NV = P::NV, KW = P::KW, LO = P::LO, NG = kD / G;
+  const int ROWS = rows_per_wg(NV), SL = ROWS * NV;
+  __shared__ uint32_t vcodes[256][kD / 4];         // value codes, 4 per word, [slot][d/4]
+  const int tid = threadIdx.x, u = blockIdx.y;
+  const int b = u / a.Hkv, h = u % a.Hkv;
+  const int s0 = blockIdx.x * SL;
+  const int s = s0 + tid;
+  const bool live = tid < SL;
+  const bool valid = live && s < a.n;
+  const bool in_tiles = live && s < a.tiles * kTile;
+  const int t = valid ? (a.inv ? a.inv[(size_t)b * a.inv_cap + s] : s) : 0;
+  for (int kv = a.kwords ? 0 : 1; kv < 2; ++kv) {
+    uint32_t x2[kD / 2];                           // the row as 64 packed fp16 pairs
+    if (valid) {
+      const uint16_t* src = (kv ? a.v : a.k) + b * a.sb + (int64_t)t * a.st + h * a.sh;
+#pragma unroll
+      for (int i = 0; i < kD / 8; ++i) {
+        const uint4 r = *reinterpret_cast<const uint4*>(src + 8 * i);
+        x2[4 * i] = r.x; x2[4 * i + 1] = r.y; x2[4 * i + 2] = r.z; x2[4 * i + 3] = r.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kD / 2; ++i) x2[i] = 0u;
+    }
+    GroupQ gq[NG];
+    uint32_t meta[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      uint32_t mn, mx;
+      group_minmax<G>(x2, g, mn, mx);
+      gq[g] = group_setup(mn, mx, L);
+      if (gq[g].s == 0.0f) gq[g].r = 0.0f;         // all codes 0
+      meta[g] = valid ? (gq[g].s_bits | (mn << 16)) : 0u;
+    }
+    if (in_tiles) {
+      uint32_t* mp = kv ? a.vmeta : a.kmeta;
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+        mp[(((size_t)u * a.tiles + s / kTile) * NG + g) * kTile + (s % kTile)] = meta[g];
+    }
+    if (kv == 0) {
+      // row words: digits along head_dim, fp32 Horner over each half of a word
+      uint32_t* kp = a.kwords + ((size_t)u * a.tiles + s / kTile) * KW * kTile + (s % kTile);
+#pragma unroll
+      for (int w = 0; w < KW; ++w) {
+        float lo = 0.f, hi = 0.f;
+#pragma unroll
+        for (int jj = NV - 1; jj >= 0; --jj) {
+          const int d = w * NV + jj;
+          if (d >= kD) continue;
+          const h2v pr = h2_from_bits(x2[d / 2]);
+          const float c = code_of(pr[d & 1], gq[d / G]);
+          if (jj >= LO) hi = __builtin_fmaf(hi, (float)L, c);
+          else lo = __builtin_fmaf(lo, (float)L, c);
+        }
+        const uint32_t word = __umul24((uint32_t)hi, P::LPOW_LO) + (uint32_t)lo;
+        if (in_tiles) kp[w * kTile] = valid ? word : 0u;
+      }
+    } else if (live) {
+#pragma unroll
+      for (int d4 = 0; d4 < kD / 4; ++d4) {
+        uint32_t packed = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int d = 4 * d4 + e;
+          const h2v pr = h2_from_bits(x2[d / 2]);
+          const uint32_t c = (uint32_t)code_of(pr[d & 1], gq[d / G]);
+          packed |= c << (8 * e);
+        }
+        vcodes[tid][d4] = valid ? packed : 0u;
+      }
+    }
+  }
+  __syncthreads();
+  const int r0 = s0 / NV;
+  const uint8_t* vc = reinterpret_cast<const uint8_t*>(&vcodes[0][0]);
+  for (int task = tid; task < ROWS * kD; task += kQThreads) {
+    const int r = task / kD, d = task % kD;
+    if (r0 + r >= a.vrows) continue;
+    float lo = 0.f, hi = 0.f;
+#pragma unroll
+    for (int jj = NV - 1; jj >= 0; --jj) {
+      const float c = (float)vc[(r * NV + jj) * kD + d];
+      if (jj >= LO) hi = __builtin_fmaf(hi, (float)L, c);
+      else lo = __builtin_fmaf(lo, (float)L, c);
+    }
+    a.vwords[((size_t)u * a.vrows + r0 + r) * kD + d] =
+        __umul24((uint32_t)hi, P::LPOW_LO) + (uint32_t)lo;
+  }
+}
+
+template <int L>
+static bool launch_rows_L(const QuantArgs& a, int G, dim3 grid, hipStream_t s) {
+  switch (G) {
+    case 32: k_quant_rows<L, 32><<<grid, kQThreads, 0, s>>>(a); return true;
+    case 64: k_quant_rows<L, 64><<<grid, kQThreads, 0, s>>>(a); return true;
+    case 128: k_quant_rows<L, 128><<<grid, kQThreads, 0, s>>>(a); return true;
+  }
+  return false;
+}
+
 static bool launch_pool(const QuantArgs& a, int G, int U, hipStream_t s) {
   const int SL = rows_per_wg(a.nv) * a.nv;
   const int cover = max(a.tiles * kTile, a.vrows * a.nv);
   dim3 grid(ceil_div(cover, SL), U);
+  switch (a.L) {
+    case 3: return launch_rows_L<3>(a, G, grid, s);
+    case 4: return launch_rows_L<4>(a, G, grid, s);
+    case 5: return launch_rows_L<5>(a, G, grid, s);
+    case 6: return launch_rows_L<6>(a, G, grid, s);
+    case 7: return launch_rows_L<7>(a, G, grid, s);
+    case 8: return launch_rows_L<8>(a, G, grid, s);
+  }
   size_t lds = (size_t)2 * SL * kD;
   switch (G) {
     case 32: k_quant_pool<32><<<grid, kQThreads, lds, s>>>(a); break;
