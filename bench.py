@@ -29,6 +29,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+DECODE_SOURCES = ("decode.hip", "decode_mfma.hip", "digits.h", "tiling.h", "common.h", "internal.h")
+QUANTIZE_SOURCES = ("quantize.hip", "rank.hip", "digits.h", "tiling.h", "common.h", "internal.h")
 
 
 def packed_decode_bytes(lay, counts):
@@ -248,12 +250,12 @@ def main():
                       frac_hbm=round(q_gbs / HBM_PEAK_GBS, 4))
     dominant = "decode" if dec_med >= q_med else "quantize"
     if dominant == "decode":
-        khash = kernel_hash("decode.hip")
+        khash = kernel_hash(*DECODE_SOURCES)
         roof = dict(bound="hbm", achieved=round(dec_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(dec_gbs / HBM_PEAK_GBS, 4),
                     traffic=measured_traffic("decode", khash), kernel="kvq_decode_attn (decode + merge)")
     else:
-        khash = kernel_hash("quantize.hip", "rank.hip")
+        khash = kernel_hash(*QUANTIZE_SOURCES)
         roof = dict(bound="hbm", achieved=round(q_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(q_gbs / HBM_PEAK_GBS, 4),
                     traffic=measured_traffic("quantize", khash), kernel="kvq_quantize (rank + quantize)")
