@@ -88,8 +88,15 @@ __device__ inline uint32_t bload(BufRes r, uint32_t byte_off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, 0);
 }
 
+// Two waves per workgroup, one per load stream (the vector-memory counter is
+// in-order, so each stream is issued in the order it is consumed):
+//   wave 0 (keys)   macro tile i: scores, running max, p = 2^(s - m) written
+//                   to an LDS double buffer, rescale factor alpha;
+//   wave 1 (values) macro tile i-1: A = p * s from that buffer, column-word
+//                   digits, matrix ops into the accumulators.
+// One barrier per macro tile hands buffer (i & 1) from wave 0 to wave 1.
 template <int L, int G>
-__global__ __launch_bounds__(64) void k_decode_pool(PoolArgs a) {
+__global__ __launch_bounds__(128) void k_decode_pool(PoolArgs a) {
   using T = Tiling<L>;
   constexpr int NV = T::NV, KW = T::KW, KWL = T::KWL, R = T::R, RUN = T::RUN, MT = T::MT,
                 KT = T::KT;
@@ -105,16 +112,17 @@ __global__ __launch_bounds__(64) void k_decode_pool(PoolArgs a) {
   constexpr int META_PER_LANE = (META + 63) / 64;
 
   __shared__ float qf[kGqa][kD];
-  __shared__ float s_lds[kGqa][MT];          // scores of the macro tile, slot order
-  __shared__ float p_lds[kGqa][4 * VK];      // weights in lane-group / digit order
-  __shared__ float vs_lds[NG][4 * VK];       // value scale (x MUL x 2^6), same order
+  __shared__ float s_lds[kGqa][MT];          // scores of the macro tile, slot order (wave 0)
+  __shared__ float p_lds[2][kGqa][4 * VK];   // weights in lane-group / digit order
+  __shared__ float al_lds[2][kGqa];          // rescale factor per head
+  __shared__ float vs_lds[NG][4 * VK];       // value scale (x MUL x 2^6), operand order (wave 1)
   __shared__ float vz_lds[NG][4 * VK];       // value zero (affine-corrected), same order
   __shared__ int ppos_lds[MT];               // slot -> position in that order
   __shared__ int mpos_lds[64 * META_PER_LANE];
   __shared__ float zred[16];
 
   set_f16_round_toward_zero();
-  const int lane = threadIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, j = lane >> 4;    // B/C-operand view: slot/channel n, group j
   const int c = blockIdx.x, u = blockIdx.y;
   const int b = u / a.Hkv, hk = u % a.Hkv;
@@ -123,248 +131,265 @@ __global__ __launch_bounds__(64) void k_decode_pool(PoolArgs a) {
   const int s_begin = c * a.chunk;
   const int s_end = min(n_valid, s_begin + a.chunk);
   if (s_begin >= s_end) {
-    for (int i = lane; i < kGqa * kPartF; i += 64) part[i] = (i % kPartF == 0) ? -INFINITY : 0.f;
+    for (int i = threadIdx.x; i < kGqa * kPartF; i += 128) part[i] = (i % kPartF == 0) ? -INFINITY : 0.f;
     return;
   }
-  // Buffer resources bounded to this unit's regions: an out-of-range offset
-  // reads 0 in hardware, so no load needs a guard (guards would turn into
-  // branches and break the compiler's wait counting).
-  const BufRes rK = make_res(a.kwords + (size_t)u * a.tiles * KW * 16, a.tiles * KW * 16 * 4);
-  const BufRes rKM = make_res(a.kmeta + (size_t)u * a.tiles * NG * 16, a.tiles * NG * 16 * 4);
-  const BufRes rVM = make_res(a.vmeta + (size_t)u * a.tiles * NG * 16, a.tiles * NG * 16 * 4);
-  const BufRes rV = make_res(a.vwords + (size_t)u * a.vrows * kD, a.vrows * kD * 4);
-  uint32_t kwoff[KWL];                       // byte offset of this lane's words in a tile
-#pragma unroll
-  for (int wi = 0; wi < KWL; ++wi) {
-    const int w = j + 4 * wi;
-    kwoff[wi] = w < KW ? (uint32_t)(w * 16 + n) * 4u : kOutOfRange;
-  }
-  const uint32_t kmoff = (uint32_t)((j / SUB) * 16 + n) * 4u;
+  const int nmt = (s_end - s_begin + MT - 1) / MT;
 
-  // Loads of a whole macro tile, issued in the order they are consumed (key
-  // tiles, value (scale, zero), value words): the vector-memory counter is
-  // in-order, so waiting for one load waits for every older one.
-  struct MacroBuf {
-    uint32_t kw[KT][KWL];
-    uint32_t km[KT];
-    uint32_t vm[META_PER_LANE];
-    uint32_t vw[8][R];
-  };
-  auto load_macro = [&](MacroBuf& mb, int s0) {
-    const uint32_t tile0 = s0 / 16;
-#pragma unroll
-    for (int t = 0; t < KT; ++t) {
-#pragma unroll
-      for (int wi = 0; wi < KWL; ++wi) mb.kw[t][wi] = bload(rK, kwoff[wi] + (tile0 + t) * (KW * 16 * 4));
-      mb.km[t] = bload(rKM, kmoff + (tile0 + t) * (NG * 16 * 4));
-    }
-#pragma unroll
-    for (int k = 0; k < META_PER_LANE; ++k) {
-      const int e = lane + 64 * k;
-      const uint32_t off = (META % 64 == 0 || e < META) ? (tile0 * NG * 16 + e) * 4u : kOutOfRange;
-      mb.vm[k] = bload(rVM, off);
-    }
-    const uint32_t row0 = s0 / NV + j * R;
-#pragma unroll
-    for (int v = 0; v < 8; ++v)
-#pragma unroll
-      for (int r2 = 0; r2 < R; ++r2) mb.vw[v][r2] = bload(rV, ((row0 + r2) * kD + 16 * v + n) * 4u);
-  };
-  MacroBuf nxt;
-  load_macro(nxt, s_begin);
-
-  // ---- query: fp32 copy in LDS, per-(sub-group, head) sums, A operands
-  for (int i = lane; i < kGqa * kD; i += 64)
+  // ---- shared set-up
+  for (int i = threadIdx.x; i < kGqa * kD; i += 128)
     qf[i / kD][i % kD] = h2f(a.q[((size_t)b * a.Hkv * kGqa + hk * kGqa) * kD + i]);
-  for (int sl = lane; sl < MT; sl += 64) {
+  for (int sl = threadIdx.x; sl < MT; sl += 128) {
     const int jj = sl / RUN, rem = sl % RUN;
     ppos_lds[sl] = jj * VK + digit_pos<DV>(rem / NV, rem % NV);
   }
-  for (int e = lane; e < 64 * META_PER_LANE; e += 64) {
+  for (int e = threadIdx.x; e < 64 * META_PER_LANE; e += 128) {
     const int ee = min(e, META - 1);
     const int sl = (ee / (NG * 16)) * 16 + (ee % 16);
     const int jj = sl / RUN, rem = sl % RUN;
     mpos_lds[e] = jj * VK + digit_pos<DV>(rem / NV, rem % NV);
   }
-  for (int i = lane; i < 4 * VK; i += 64) {
-    for (int h = 0; h < 4; ++h) p_lds[h][i] = 0.f;
+  for (int i = threadIdx.x; i < 4 * VK; i += 128) {
+    for (int h = 0; h < 4; ++h) { p_lds[0][h][i] = 0.f; p_lds[1][h][i] = 0.f; }
     for (int g = 0; g < NG; ++g) { vs_lds[g][i] = 0.f; vz_lds[g][i] = 0.f; }
   }
   __syncthreads();
-  float qc[4];                               // lane (n, g): c * sum_{d in g} q_h[d]
-#pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    float s = 0.f;
-    for (int d = 32 * j; d < 32 * j + 32; ++d) s += qf[h][d];
-    qc[h] = s * a.c;
-  }
-  h8 aq[KM];
-  {
-    const int r = n, g = r >> 2, h = r & 3;  // A-operand view: row r, k-range of group j
-    const int nw = (KW - j + 3) / 4;         // words this lane group owns
-#pragma unroll
-    for (int m = 0; m < KM; ++m)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int t = 8 * m + i;
-        const int wi = DK::word_of(t);
-        const int d = (j + 4 * wi) * NV + DK::digit_of(t);
-        const bool ok = wi >= 0 && wi < nw && d < kD && (d >> 5) == g;
-        const float qv = qf[h][min(max(d, 0), kD - 1)];
-        aq[m][i] = (_Float16)(ok ? qv : 0.0f);                    // q is fp16: exact
-      }
-  }
-  int mpos[META_PER_LANE];
-#pragma unroll
-  for (int k = 0; k < META_PER_LANE; ++k) mpos[k] = mpos_lds[lane + 64 * k];
 
-  float m_run = -INFINITY, l_run = 0.f, zacc = 0.f;
-  f4 acc[8];
+  if (wave == 0) {
+    // ================= keys: scores, softmax, weights =================
+    const BufRes rK = make_res(a.kwords + (size_t)u * a.tiles * KW * 16, a.tiles * KW * 16 * 4);
+    const BufRes rKM = make_res(a.kmeta + (size_t)u * a.tiles * NG * 16, a.tiles * NG * 16 * 4);
+    uint32_t kwoff[KWL];
 #pragma unroll
-  for (int v = 0; v < 8; ++v) acc[v] = (f4){0.f, 0.f, 0.f, 0.f};
-
-  for (int s0 = s_begin; s0 < s_end; s0 += MT) {
-    const MacroBuf cur = nxt;
-    if (s0 + MT < s_end) load_macro(nxt, s0 + MT);
-    // ---- scores of the key tiles
-    float mx = -INFINITY;
+    for (int wi = 0; wi < KWL; ++wi) {
+      const int w = j + 4 * wi;
+      kwoff[wi] = w < KW ? (uint32_t)(w * 16 + n) * 4u : kOutOfRange;
+    }
+    const uint32_t kmoff = (uint32_t)((j / SUB) * 16 + n) * 4u;
+    struct KBuf {
+      uint32_t kw[KT][KWL];
+      uint32_t km[KT];
+    };
+    auto load_k = [&](KBuf& kb, int s0) {
+      const uint32_t tile0 = s0 / 16;
 #pragma unroll
-    for (int t = 0; t < KT; ++t) {
-      _Float16 dg[DK::NOUT];
-      DK::run(cur.kw[t], dg);
-      f4 pr = {0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < KT; ++t) {
 #pragma unroll
-      for (int m = 0; m < KM; ++m) {
-        h8 bk;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) bk[i] = dg[8 * m + i];
-        pr = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[m], bk, pr, 0, 0, 0);
+        for (int wi = 0; wi < KWL; ++wi) kb.kw[t][wi] = bload(rK, kwoff[wi] + (tile0 + t) * (KW * 16 * 4));
+        kb.km[t] = bload(rKM, kmoff + (tile0 + t) * (NG * 16 * 4));
       }
-      const uint32_t meta = cur.km[t];
-      const float sg = h2f(meta & 0xFFFFu) * MUL;
-      const float ssc = sg * a.c, zz = AFF ? h2f(meta >> 16) - sg : h2f(meta >> 16);
-      f4 x;
+    };
+    KBuf nxt;
+    load_k(nxt, s_begin);
+    float qc[4];                             // lane (n, g): c * sum_{d in g} q_h[d]
 #pragma unroll
-      for (int h = 0; h < 4; ++h) x[h] = __builtin_fmaf(ssc, pr[h], zz * qc[h]);
-      float sc = reduce_scatter4(x);
-      sc = (s0 + 16 * t + n < s_end) ? sc : -INFINITY;
-      mx = fmaxf(mx, sc);
-      s_lds[j][16 * t + n] = sc;
+    for (int h = 0; h < 4; ++h) {
+      float sum = 0.f;
+      for (int d = 32 * j; d < 32 * j + 32; ++d) sum += qf[h][d];
+      qc[h] = sum * a.c;
     }
-    // ---- online softmax (lane (n, h): head h)
-    mx = row_max16(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    float ls = 0.f;
-#pragma unroll 2
-    for (int t = 0; t < KT; ++t) {
-      const float p = __builtin_amdgcn_exp2f(s_lds[j][16 * t + n] - m_use);
-      ls += p;
-      p_lds[j][ppos_lds[16 * t + n]] = p;
-    }
-    l_run = __builtin_fmaf(l_run, alpha, ls);
-    m_run = m_new;
-    const float al0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 0));
-    const float al1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 16));
-    const float al2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 32));
-    const float al3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 48));
-    if (!(al0 == 1.f && al1 == 1.f && al2 == 1.f && al3 == 1.f)) {
-      // acc rows are (g, h) with h = register index; zero-point sums are per
-      // (g, h) in the A-operand view (h = n & 3)
-#pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        acc[v][0] *= al0; acc[v][1] *= al1; acc[v][2] *= al2; acc[v][3] *= al3;
-      }
-      const int hz = n & 3;
-      zacc *= hz == 0 ? al0 : hz == 1 ? al1 : hz == 2 ? al2 : al3;
-    }
-    // ---- value (scale, zero) in operand order.  Operand digits are 1 + d/MUL
-    // on power-of-two grids: fold the affine map; the A operand carries an
-    // extra 2^6 (undone at the end) so small weights stay out of the fp16
-    // subnormal range.
-#pragma unroll
-    for (int k = 0; k < META_PER_LANE; ++k) {
-      const int e = lane + 64 * k;
-      if (META % 64 == 0 || e < META) {
-        const int g = (e / 16) % NG;
-        const float sv = h2f(cur.vm[k] & 0xFFFFu) * MUL, zv = h2f(cur.vm[k] >> 16);
-        vs_lds[g][mpos[k]] = sv * kAScale;
-        vz_lds[g][mpos[k]] = AFF ? zv - sv : zv;
-      }
-    }
-    __syncthreads();
-    // ---- value operand A[(g, h)][slot] = p_h * s_g, zero-point term on the VALU
-    h8 av[VM];
+    h8 aq[KM];
     {
-      const int r = n, g = (r >> 2) / SUB, h = r & 3;
+      const int r = n, g = r >> 2, h = r & 3;   // A-operand view: row r, k-range of group j
+      const int nw = (KW - j + 3) / 4;          // words this lane group owns
 #pragma unroll
-      for (int m = 0; m < VM; ++m) {
-        const float* pp = &p_lds[h][j * VK + 8 * m];
-        const float* ss = &vs_lds[g][j * VK + 8 * m];
-        const float* zp = &vz_lds[g][j * VK + 8 * m];
+      for (int m = 0; m < KM; ++m)
 #pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-          // fp32 -> fp16 rounding half up: add half an fp16 spacing to the fp32
-          // bits, then the truncating pack (unbiased, unlike truncation alone:
-          // the value sum cancels against the zero-point sum, so a bias would
-          // be amplified)
-          const float x0 = __uint_as_float(__float_as_uint(pp[i] * ss[i]) + 0x1000u);
-          const float x1 = __uint_as_float(__float_as_uint(pp[i + 1] * ss[i + 1]) + 0x1000u);
-          const h2v vv = __builtin_bit_cast(h2v, __builtin_amdgcn_cvt_pkrtz(x0, x1));
-          av[m][i] = vv[0];
-          av[m][i + 1] = vv[1];
-          zacc = __builtin_fmaf(pp[i], zp[i], zacc);
-          zacc = __builtin_fmaf(pp[i + 1], zp[i + 1], zacc);
+        for (int i = 0; i < 8; ++i) {
+          const int t = 8 * m + i;
+          const int wi = DK::word_of(t);
+          const int d = (j + 4 * wi) * NV + DK::digit_of(t);
+          const bool ok = wi >= 0 && wi < nw && d < kD && (d >> 5) == g;
+          const float qv = qf[h][min(max(d, 0), kD - 1)];
+          aq[m][i] = (_Float16)(ok ? qv : 0.0f);   // q is fp16: exact
+        }
+    }
+    float m_run = -INFINITY, l_run = 0.f;
+    for (int it = 0; it <= nmt; ++it) {
+      if (it < nmt) {
+        const int s0 = s_begin + it * MT;
+        const KBuf cur = nxt;
+        if (it + 1 < nmt) load_k(nxt, s0 + MT);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+          _Float16 dg[DK::NOUT];
+          DK::run(cur.kw[t], dg);
+          f4 pr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int m = 0; m < KM; ++m) {
+            h8 bk;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) bk[i] = dg[8 * m + i];
+            pr = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[m], bk, pr, 0, 0, 0);
+          }
+          const uint32_t meta = cur.km[t];
+          const float sg = h2f(meta & 0xFFFFu) * MUL;
+          const float ssc = sg * a.c, zz = AFF ? h2f(meta >> 16) - sg : h2f(meta >> 16);
+          f4 x;
+#pragma unroll
+          for (int h = 0; h < 4; ++h) x[h] = __builtin_fmaf(ssc, pr[h], zz * qc[h]);
+          float sc = reduce_scatter4(x);
+          sc = (s0 + 16 * t + n < s_end) ? sc : -INFINITY;
+          mx = fmaxf(mx, sc);
+          s_lds[j][16 * t + n] = sc;
+        }
+        // online softmax (lane (n, h): head h)
+        mx = row_max16(mx);
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        float ls = 0.f;
+        float* pb = &p_lds[it & 1][j][0];
+#pragma unroll 2
+        for (int t = 0; t < KT; ++t) {
+          const float p = __builtin_amdgcn_exp2f(s_lds[j][16 * t + n] - m_use);
+          ls += p;
+          pb[ppos_lds[16 * t + n]] = p;
+        }
+        l_run = __builtin_fmaf(l_run, alpha, ls);
+        m_run = m_new;
+        if (n == 0) al_lds[it & 1][j] = alpha;
+      }
+      __syncthreads();
+    }
+    const float l_tot = row_sum16(l_run);
+    if (n == 0) {
+      part[j * kPartF + 0] = m_run;
+      part[j * kPartF + 1] = l_tot;
+    }
+  } else {
+    // ================= values: A = p * s, matrix ops =================
+    const BufRes rVM = make_res(a.vmeta + (size_t)u * a.tiles * NG * 16, a.tiles * NG * 16 * 4);
+    const BufRes rV = make_res(a.vwords + (size_t)u * a.vrows * kD, a.vrows * kD * 4);
+    int mpos[META_PER_LANE];
+#pragma unroll
+    for (int k = 0; k < META_PER_LANE; ++k) mpos[k] = mpos_lds[lane + 64 * k];
+    struct VBuf {
+      uint32_t vm[META_PER_LANE];
+      uint32_t vw[8][R];
+    };
+    auto load_v = [&](VBuf& vb, int s0) {
+      const uint32_t tile0 = s0 / 16;
+#pragma unroll
+      for (int k = 0; k < META_PER_LANE; ++k) {
+        const int e = lane + 64 * k;
+        const uint32_t off = (META % 64 == 0 || e < META) ? (tile0 * NG * 16 + e) * 4u : kOutOfRange;
+        vb.vm[k] = bload(rVM, off);
+      }
+      const uint32_t row0 = s0 / NV + j * R;
+#pragma unroll
+      for (int v = 0; v < 8; ++v)
+#pragma unroll
+        for (int r2 = 0; r2 < R; ++r2) vb.vw[v][r2] = bload(rV, ((row0 + r2) * kD + 16 * v + n) * 4u);
+    };
+    VBuf nxt;
+    load_v(nxt, s_begin);
+    float zacc = 0.f;
+    f4 acc[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) acc[v] = (f4){0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it <= nmt; ++it) {
+      if (it >= 1) {
+        const int i = it - 1;
+        const int s0 = s_begin + i * MT;
+        const VBuf cur = nxt;
+        if (i + 1 < nmt) load_v(nxt, s0 + MT);
+        const float al0 = al_lds[i & 1][0], al1 = al_lds[i & 1][1];
+        const float al2 = al_lds[i & 1][2], al3 = al_lds[i & 1][3];
+        if (!(al0 == 1.f && al1 == 1.f && al2 == 1.f && al3 == 1.f)) {
+          // acc rows are (g, h) with h = register index; zero-point sums are
+          // per (g, h) in the A-operand view (h = n & 3)
+#pragma unroll
+          for (int v = 0; v < 8; ++v) {
+            acc[v][0] *= al0; acc[v][1] *= al1; acc[v][2] *= al2; acc[v][3] *= al3;
+          }
+          const int hz = n & 3;
+          zacc *= hz == 0 ? al0 : hz == 1 ? al1 : hz == 2 ? al2 : al3;
+        }
+        // value (scale, zero) in operand order.  Operand digits are 1 + d/MUL
+        // on power-of-two grids: fold the affine map; the A operand carries
+        // an extra 2^6 (undone at the end) so small weights stay out of the
+        // fp16 subnormal range.  Only this wave uses vs/vz; its LDS accesses
+        // execute in order.
+#pragma unroll
+        for (int k = 0; k < META_PER_LANE; ++k) {
+          const int e = lane + 64 * k;
+          if (META % 64 == 0 || e < META) {
+            const int g = (e / 16) % NG;
+            const float sv = h2f(cur.vm[k] & 0xFFFFu) * MUL, zv = h2f(cur.vm[k] >> 16);
+            vs_lds[g][mpos[k]] = sv * kAScale;
+            vz_lds[g][mpos[k]] = AFF ? zv - sv : zv;
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the stores above have landed
+        __builtin_amdgcn_wave_barrier();
+        h8 av[VM];
+        {
+          const int r = n, g = (r >> 2) / SUB, h = r & 3;
+#pragma unroll
+          for (int m = 0; m < VM; ++m) {
+            const float* pp = &p_lds[i & 1][h][j * VK + 8 * m];
+            const float* ss = &vs_lds[g][j * VK + 8 * m];
+            const float* zp = &vz_lds[g][j * VK + 8 * m];
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+              // fp32 -> fp16 rounding half up: add half an fp16 spacing to the
+              // fp32 bits, then the truncating pack (unbiased, unlike truncation
+              // alone: the value sum cancels against the zero-point sum, so a
+              // bias would be amplified)
+              const float x0 = __uint_as_float(__float_as_uint(pp[e] * ss[e]) + 0x1000u);
+              const float x1 = __uint_as_float(__float_as_uint(pp[e + 1] * ss[e + 1]) + 0x1000u);
+              const h2v vv = __builtin_bit_cast(h2v, __builtin_amdgcn_cvt_pkrtz(x0, x1));
+              av[m][e] = vv[0];
+              av[m][e + 1] = vv[1];
+              zacc = __builtin_fmaf(pp[e], zp[e], zacc);
+              zacc = __builtin_fmaf(pp[e + 1], zp[e + 1], zacc);
+            }
+          }
+        }
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          _Float16 dg[DV::NOUT];
+          DV::run(cur.vw[v], dg);
+#pragma unroll
+          for (int m = 0; m < VM; ++m) {
+            h8 bv;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bv[e] = dg[8 * m + e];
+            acc[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[m], bv, acc[v], 0, 0, 0);
+          }
         }
       }
+      __syncthreads();
     }
-    // ---- value words -> B operands, 8 channel tiles of 16
+    // partials: acc rows (g = j, h) hold channels of sub-group j
+    float zs = zacc;                         // lanes (r, j) -> sum over j, r = 4 g + h
+    zs += __shfl_xor(zs, 16);
+    zs += __shfl_xor(zs, 32);
+    if (lane < 16) zred[lane] = zs;
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int v = 0; v < 8; ++v) {
-      _Float16 dg[DV::NOUT];
-      DV::run(cur.vw[v], dg);
+      if ((v >> 1) != j) continue;           // channels 16v..16v+15 belong to sub-group v/2
+      const int d = 16 * v + n;
 #pragma unroll
-      for (int m = 0; m < VM; ++m) {
-        h8 bv;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) bv[i] = dg[8 * m + i];
-        acc[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[m], bv, acc[v], 0, 0, 0);
-      }
+      for (int h = 0; h < 4; ++h)
+        part[h * kPartF + 4 + d] = __builtin_fmaf(acc[v][h], 1.0f / kAScale, zred[4 * j + h]);
     }
-    __syncthreads();
-  }
-
-  // ---- partials: m, l per head; acc rows (g = j, h) hold channels of sub-group j
-  const float l_tot = row_sum16(l_run);
-  float zs = zacc;                           // lanes (r, j) -> sum over j, r = 4 g + h
-  zs += __shfl_xor(zs, 16);
-  zs += __shfl_xor(zs, 32);
-  if (lane < 16) zred[lane] = zs;
-  __syncthreads();
-#pragma unroll
-  for (int v = 0; v < 8; ++v) {
-    if ((v >> 1) != j) continue;             // channels 16v..16v+15 belong to sub-group v/2
-    const int d = 16 * v + n;
-#pragma unroll
-    for (int h = 0; h < 4; ++h)
-      part[h * kPartF + 4 + d] = __builtin_fmaf(acc[v][h], 1.0f / kAScale, zred[4 * j + h]);
-  }
-  if (n == 0) {
-    part[j * kPartF + 0] = m_run;
-    part[j * kPartF + 1] = l_tot;
   }
 }
 
 template <int L, int G>
 static void launch_one(const PoolArgs& a, int nch, int U, hipStream_t s) {
-  k_decode_pool<L, G><<<dim3(nch, U), 64, 0, s>>>(a);
+  k_decode_pool<L, G><<<dim3(nch, U), 128, 0, s>>>(a);
 }
 
 template <int L, int G>
 static int occupancy_one() {
   int blocks = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_decode_pool<L, G>, 64, 0) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_decode_pool<L, G>, 128, 0) != hipSuccess)
     return 0;
   return blocks;
 }
