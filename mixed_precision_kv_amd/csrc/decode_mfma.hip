@@ -22,23 +22,14 @@
 #include "common.h"
 #include "internal.h"
 #include "tiling.h"
-#include "digits.h"
+#include "unpack.h"
 
 namespace kvq {
 
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPartF = 4 + kD;      // floats per head in a partial: m, l, pad, pad, acc[128]
 constexpr float kAScale = 64.0f;    // value-operand weights carry 2^6 (fp16 range)
-
-// Position of (word, digit) in the extraction order of Digits<L, NW>.
-template <class Dg>
-__host__ __device__ constexpr int digit_pos(int word, int digit) {
-  for (int t = 0; t < Dg::NOUT; ++t)
-    if (Dg::word_of(t) == word && Dg::digit_of(t) == digit) return t;
-  return -1;
-}
 
 __device__ inline float dpp_ror(float v, int n) {
   // row_ror:n within each row of 16 lanes
@@ -96,13 +87,13 @@ __device__ inline uint32_t bload(BufRes r, uint32_t byte_off) {
 //                   digits, matrix ops into the accumulators.
 // One barrier per macro tile hands buffer (i & 1) from wave 0 to wave 1.
 template <int L, int G>
-__global__ __launch_bounds__(128) void k_decode_pool(PoolArgs a) {
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k_decode_pool(PoolArgs a) {
   using T = Tiling<L>;
   constexpr int NV = T::NV, KW = T::KW, KWL = T::KWL, R = T::R, RUN = T::RUN, MT = T::MT,
                 KT = T::KT;
-  using DK = Digits<L, KWL>;                 // key words of one lane
-  using DV = Digits<L, R>;                   // value words of one lane and channel tile
-  constexpr int KM = DK::NOUT / 8, VM = DV::NOUT / 8;
+  using DK = Unpack<L, KWL>;                 // key words of one lane
+  using DV = Unpack<L, R>;                   // value words of one lane and channel tile
+  constexpr int KM = DK::NH8, VM = DV::NH8;
   constexpr bool AFF = DK::kAffine;
   constexpr float MUL = (float)DK::kMul;
   constexpr int NG = kD / G;                 // (scale, zero) groups per row
@@ -120,8 +111,8 @@ __global__ __launch_bounds__(128) void k_decode_pool(PoolArgs a) {
   __shared__ int ppos_lds[MT];               // slot -> position in that order
   __shared__ int mpos_lds[64 * META_PER_LANE];
   __shared__ float zred[16];
+  __shared__ uint2 ctab[DK::kTableEntries];   // chunk -> four fp16 digits
 
-  set_f16_round_toward_zero();
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, j = lane >> 4;    // B/C-operand view: slot/channel n, group j
   const int c = blockIdx.x, u = blockIdx.y;
@@ -141,14 +132,15 @@ __global__ __launch_bounds__(128) void k_decode_pool(PoolArgs a) {
     qf[i / kD][i % kD] = h2f(a.q[((size_t)b * a.Hkv * kGqa + hk * kGqa) * kD + i]);
   for (int sl = threadIdx.x; sl < MT; sl += 128) {
     const int jj = sl / RUN, rem = sl % RUN;
-    ppos_lds[sl] = jj * VK + digit_pos<DV>(rem / NV, rem % NV);
+    ppos_lds[sl] = jj * VK + DV::pos_of(rem / NV, rem % NV);
   }
   for (int e = threadIdx.x; e < 64 * META_PER_LANE; e += 128) {
     const int ee = min(e, META - 1);
     const int sl = (ee / (NG * 16)) * 16 + (ee % 16);
     const int jj = sl / RUN, rem = sl % RUN;
-    mpos_lds[e] = jj * VK + digit_pos<DV>(rem / NV, rem % NV);
+    mpos_lds[e] = jj * VK + DV::pos_of(rem / NV, rem % NV);
   }
+  DK::fill(ctab, threadIdx.x, 128);
   for (int i = threadIdx.x; i < 4 * VK; i += 128) {
     for (int h = 0; h < 4; ++h) { p_lds[0][h][i] = 0.f; p_lds[1][h][i] = 0.f; }
     for (int g = 0; g < NG; ++g) { vs_lds[g][i] = 0.f; vz_lds[g][i] = 0.f; }
@@ -213,16 +205,11 @@ __global__ __launch_bounds__(128) void k_decode_pool(PoolArgs a) {
         float mx = -INFINITY;
 #pragma unroll
         for (int t = 0; t < KT; ++t) {
-          _Float16 dg[DK::NOUT];
-          DK::run(cur.kw[t], dg);
+          h8 bk[KM];
+          DK::run(cur.kw[t], ctab, bk);
           f4 pr = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int m = 0; m < KM; ++m) {
-            h8 bk;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) bk[i] = dg[8 * m + i];
-            pr = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[m], bk, pr, 0, 0, 0);
-          }
+          for (int m = 0; m < KM; ++m) pr = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[m], bk[m], pr, 0, 0, 0);
           const uint32_t meta = cur.km[t];
           const float sg = h2f(meta & 0xFFFFu) * MUL;
           const float ssc = sg * a.c, zz = AFF ? h2f(meta >> 16) - sg : h2f(meta >> 16);
@@ -350,15 +337,10 @@ __global__ __launch_bounds__(128) void k_decode_pool(PoolArgs a) {
         }
 #pragma unroll
         for (int v = 0; v < 8; ++v) {
-          _Float16 dg[DV::NOUT];
-          DV::run(cur.vw[v], dg);
+          h8 bv[VM];
+          DV::run(cur.vw[v], ctab, bv);
 #pragma unroll
-          for (int m = 0; m < VM; ++m) {
-            h8 bv;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) bv[e] = dg[8 * m + e];
-            acc[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[m], bv, acc[v], 0, 0, 0);
-          }
+          for (int m = 0; m < VM; ++m) acc[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[m], bv[m], acc[v], 0, 0, 0);
         }
       }
       __syncthreads();
