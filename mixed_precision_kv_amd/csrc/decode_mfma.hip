@@ -3,22 +3,22 @@
 // token; KVQuant summary: small-batch decode is memory-bound, so packed words
 // are read once and expanded in registers.
 //
-// One wave per (chunk of slots, sequence x KV head).  Per 16-slot key tile:
-//   lane (n = slot, j) owns row words j, j+4, j+8, ... of slot n; their base-L
-//   digits, as fp16, are the B operand directly.  The A operand is the query
-//   of the four heads spread over 16 rows (sub-group of 32 channels x head),
-//   zero outside its sub-group, so the result row (g, h) of column n is the
-//   partial dot sum_{d in g} q_h[d] c_d of slot n.  Lane (n, g) holds rows
-//   (g, 0..3) and the (scale, zero) of group g of slot n, so it forms
+// One workgroup per (chunk of slots, sequence x KV head).  Per 16-slot key
+// tile: lane (n = slot, j) owns row words j, j+4, j+8, ... of slot n; their
+// base-L digits, as fp16, are the B operand directly.  The A operand is the
+// query of the four heads spread over 16 rows (sub-group of 32 channels x
+// head), zero outside its sub-group, so the result row (g, h) of column n is
+// the partial dot sum_{d in g} q_h[d] c_d of slot n.  Lane (n, g) holds rows
+// (g, 0..3) and the (scale, zero) of group g of slot n, so it forms
 //     s_g * P + z_g * sum_{d in g} q_h[d]
-//   and a reduce-scatter across the four lanes of slot n (two permlane
-//   swaps) leaves lane (n, h) with the score of head h.
+// and a reduce-scatter across the four lanes of slot n (two permlane swaps)
+// leaves lane (n, h) with the score of head h.
 // Values are stored in column words (n_L consecutive slots of one channel),
 // so the slot axis is the lane's contraction axis: B[k = slot][col = channel]
-// comes straight out of the words; A[(g, h)][slot] = p_h * s_g(slot) is
-// assembled from LDS; the zero-point term sum p_h z_g is accumulated on the
-// VALU.  Online softmax (base 2) per macro tile; partials (m, l, acc) go to
-// the workspace for the log-sum-exp merge.
+// comes straight out of the words; A[(g, h)][slot] = p_h * s_g(slot) is an
+// fp16 product of the weight and the scale; the zero-point term sum p_h z_g
+// is a dot product on the VALU.  Online softmax (base 2) per macro tile;
+// partials (m, l, acc) go to the workspace for the log-sum-exp merge.
 #include "common.h"
 #include "internal.h"
 #include "tiling.h"
@@ -81,8 +81,9 @@ __device__ inline uint32_t bload(BufRes r, uint32_t byte_off) {
 
 // Two waves per workgroup, one per load stream (the vector-memory counter is
 // in-order, so each stream is issued in the order it is consumed):
-//   wave 0 (keys)   macro tile i: scores, running max, p = 2^(s - m) written
-//                   to an LDS double buffer, rescale factor alpha;
+//   wave 0 (keys)   macro tile i: scores, running max, weights p = 2^(s - m)
+//                   as fp16 into an LDS double buffer (in the value
+//                   operand's order), rescale factor alpha;
 //   wave 1 (values) macro tile i-1: A = p * s from that buffer, column-word
 //                   digits, matrix ops into the accumulators.
 // One barrier per macro tile hands buffer (i & 1) from wave 0 to wave 1.
@@ -103,11 +104,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
   constexpr int META_PER_LANE = (META + 63) / 64;
 
   __shared__ float qf[kGqa][kD];
-  __shared__ float s_lds[kGqa][MT];          // scores of the macro tile, slot order (wave 0)
-  __shared__ float p_lds[2][kGqa][4 * VK];   // weights in lane-group / digit order
+  __shared__ __attribute__((aligned(16))) _Float16 pw_lds[2][kGqa][4 * VK];  // 2^6 p, operand order (wave 0 -> 1)
   __shared__ float al_lds[2][kGqa];          // rescale factor per head
-  __shared__ float vs_lds[NG][4 * VK];       // value scale (x MUL x 2^6), operand order (wave 1)
-  __shared__ float vz_lds[NG][4 * VK];       // value zero (affine-corrected), same order
+  __shared__ __attribute__((aligned(16))) _Float16 vs_lds[NG][4 * VK];  // value scale (x MUL), operand order
+  __shared__ __attribute__((aligned(16))) _Float16 vz_lds[NG][4 * VK];  // value zero, same order
   __shared__ int ppos_lds[MT];               // slot -> position in that order
   __shared__ int mpos_lds[64 * META_PER_LANE];
   __shared__ float zred[16];
@@ -141,9 +141,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
     mpos_lds[e] = jj * VK + DV::pos_of(rem / NV, rem % NV);
   }
   DK::fill(ctab, threadIdx.x, 128);
+  // operand positions that hold no slot keep weight and scale 0
   for (int i = threadIdx.x; i < 4 * VK; i += 128) {
-    for (int h = 0; h < 4; ++h) { p_lds[0][h][i] = 0.f; p_lds[1][h][i] = 0.f; }
-    for (int g = 0; g < NG; ++g) { vs_lds[g][i] = 0.f; vz_lds[g][i] = 0.f; }
+    for (int h = 0; h < 4; ++h) { pw_lds[0][h][i] = (_Float16)0.0f; pw_lds[1][h][i] = (_Float16)0.0f; }
+    for (int g = 0; g < NG; ++g) { vs_lds[g][i] = (_Float16)0.0f; vz_lds[g][i] = (_Float16)0.0f; }
   }
   __syncthreads();
 
@@ -196,12 +197,16 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
           aq[m][i] = (_Float16)(ok ? qv : 0.0f);   // q is fp16: exact
         }
     }
+    int spos[KT];                            // operand position of slot 16 t + n
+#pragma unroll
+    for (int t = 0; t < KT; ++t) spos[t] = ppos_lds[16 * t + n];
     float m_run = -INFINITY, l_run = 0.f;
     for (int it = 0; it <= nmt; ++it) {
       if (it < nmt) {
         const int s0 = s_begin + it * MT;
         const KBuf cur = nxt;
         if (it + 1 < nmt) load_k(nxt, s0 + MT);
+        float scs[KT];
         float mx = -INFINITY;
 #pragma unroll
         for (int t = 0; t < KT; ++t) {
@@ -217,22 +222,27 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
           for (int h = 0; h < 4; ++h) x[h] = __builtin_fmaf(ssc, pr[h], zz * qc[h]);
           float sc = reduce_scatter4(x);
-          sc = (s0 + 16 * t + n < s_end) ? sc : -INFINITY;
-          mx = fmaxf(mx, sc);
-          s_lds[j][16 * t + n] = sc;
+          scs[t] = (s0 + 16 * t + n < s_end) ? sc : -INFINITY;
+          mx = fmaxf(mx, scs[t]);
         }
-        // online softmax (lane (n, h): head h)
+        // online softmax (lane (n, h): head h).  Weights go to the value wave
+        // as fp16 2^6 p, rounded half up: add half an fp16 spacing to the fp32
+        // bits, then the truncating conversion (unbiased, unlike truncation
+        // alone, whose bias the cancellation between the value and zero-point
+        // sums would amplify).  The 2^6 keeps small weights out of the fp16
+        // subnormal range.
         mx = row_max16(mx);
         const float m_new = fmaxf(m_run, mx);
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        _Float16* pb = &pw_lds[it & 1][j][0];
         float ls = 0.f;
-        float* pb = &p_lds[it & 1][j][0];
-#pragma unroll 2
+#pragma unroll
         for (int t = 0; t < KT; ++t) {
-          const float p = __builtin_amdgcn_exp2f(s_lds[j][16 * t + n] - m_use);
+          const float p = __builtin_amdgcn_exp2f(scs[t] - m_use);
           ls += p;
-          pb[ppos_lds[16 * t + n]] = p;
+          const float x = __uint_as_float(__float_as_uint(p * kAScale) + 0x1000u);
+          pb[spos[t]] = __builtin_bit_cast(h2v, __builtin_amdgcn_cvt_pkrtz(x, x))[0];
         }
         l_run = __builtin_fmaf(l_run, alpha, ls);
         m_run = m_new;
@@ -272,10 +282,14 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
     };
     VBuf nxt;
     load_v(nxt, s_begin);
-    float zacc = 0.f;
+    // A-operand view: lane (r, j) holds row r = (sub-group sg, head h) over
+    // the operand positions of lane group j
+    const int h = n & 3, g = (n >> 2) / SUB;
+    float zacc = 0.f;                        // 2^6 sum p z (row r)
     f4 acc[8];
 #pragma unroll
     for (int v = 0; v < 8; ++v) acc[v] = (f4){0.f, 0.f, 0.f, 0.f};
+    f4 asum = {0.f, 0.f, 0.f, 0.f};          // power-of-two grids: sum of A per row
     for (int it = 0; it <= nmt; ++it) {
       if (it >= 1) {
         const int i = it - 1;
@@ -285,55 +299,44 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
         const float al0 = al_lds[i & 1][0], al1 = al_lds[i & 1][1];
         const float al2 = al_lds[i & 1][2], al3 = al_lds[i & 1][3];
         if (!(al0 == 1.f && al1 == 1.f && al2 == 1.f && al3 == 1.f)) {
-          // acc rows are (g, h) with h = register index; zero-point sums are
-          // per (g, h) in the A-operand view (h = n & 3)
+          // acc rows are (sg, h) with h = register index
 #pragma unroll
           for (int v = 0; v < 8; ++v) {
             acc[v][0] *= al0; acc[v][1] *= al1; acc[v][2] *= al2; acc[v][3] *= al3;
           }
-          const int hz = n & 3;
-          zacc *= hz == 0 ? al0 : hz == 1 ? al1 : hz == 2 ? al2 : al3;
+          if (AFF) { asum[0] *= al0; asum[1] *= al1; asum[2] *= al2; asum[3] *= al3; }
+          const float alh = h == 0 ? al0 : h == 1 ? al1 : h == 2 ? al2 : al3;
+          zacc *= alh;
         }
-        // value (scale, zero) in operand order.  Operand digits are 1 + d/MUL
-        // on power-of-two grids: fold the affine map; the A operand carries
-        // an extra 2^6 (undone at the end) so small weights stay out of the
-        // fp16 subnormal range.  Only this wave uses vs/vz; its LDS accesses
-        // execute in order.
+        // value (scale, zero) in operand order, as fp16.  Operand digits are
+        // 1 + d/MUL on power-of-two grids, so the scale carries MUL (exact)
+        // and the affine offset is removed at the end through asum.  Only
+        // this wave uses vs/vz; its LDS accesses execute in order.
 #pragma unroll
         for (int k = 0; k < META_PER_LANE; ++k) {
           const int e = lane + 64 * k;
           if (META % 64 == 0 || e < META) {
-            const int g = (e / 16) % NG;
-            const float sv = h2f(cur.vm[k] & 0xFFFFu) * MUL, zv = h2f(cur.vm[k] >> 16);
-            vs_lds[g][mpos[k]] = sv * kAScale;
-            vz_lds[g][mpos[k]] = AFF ? zv - sv : zv;
+            const int gg = (e / 16) % NG;
+            const uint32_t mw = cur.vm[k];
+            const _Float16 sv = AFF ? (_Float16)(h2f(mw & 0xFFFFu) * MUL)
+                                    : __builtin_bit_cast(_Float16, (uint16_t)(mw & 0xFFFFu));
+            vs_lds[gg][mpos[k]] = sv;
+            vz_lds[gg][mpos[k]] = __builtin_bit_cast(_Float16, (uint16_t)(mw >> 16));
           }
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the stores above have landed
         __builtin_amdgcn_wave_barrier();
         h8 av[VM];
-        {
-          const int r = n, g = (r >> 2) / SUB, h = r & 3;
 #pragma unroll
-          for (int m = 0; m < VM; ++m) {
-            const float* pp = &p_lds[i & 1][h][j * VK + 8 * m];
-            const float* ss = &vs_lds[g][j * VK + 8 * m];
-            const float* zp = &vz_lds[g][j * VK + 8 * m];
+        for (int m = 0; m < VM; ++m) {
+          const int pos = j * VK + 8 * m;
+          const h8 p16 = *reinterpret_cast<const h8*>(&pw_lds[i & 1][h][pos]);
+          const h8 sv = *reinterpret_cast<const h8*>(&vs_lds[g][pos]);
+          const h8 zv = *reinterpret_cast<const h8*>(&vz_lds[g][pos]);
+          av[m] = p16 * sv;                  // fp16 products, rounded to nearest
 #pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-              // fp32 -> fp16 rounding half up: add half an fp16 spacing to the
-              // fp32 bits, then the truncating pack (unbiased, unlike truncation
-              // alone: the value sum cancels against the zero-point sum, so a
-              // bias would be amplified)
-              const float x0 = __uint_as_float(__float_as_uint(pp[e] * ss[e]) + 0x1000u);
-              const float x1 = __uint_as_float(__float_as_uint(pp[e + 1] * ss[e + 1]) + 0x1000u);
-              const h2v vv = __builtin_bit_cast(h2v, __builtin_amdgcn_cvt_pkrtz(x0, x1));
-              av[m][e] = vv[0];
-              av[m][e + 1] = vv[1];
-              zacc = __builtin_fmaf(pp[e], zp[e], zacc);
-              zacc = __builtin_fmaf(pp[e + 1], zp[e + 1], zacc);
-            }
-          }
+          for (int e = 0; e < 8; e += 2)
+            zacc = __builtin_amdgcn_fdot2((h2v){p16[e], p16[e + 1]}, (h2v){zv[e], zv[e + 1]}, zacc, false);
         }
 #pragma unroll
         for (int v = 0; v < 8; ++v) {
@@ -342,23 +345,31 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
           for (int m = 0; m < VM; ++m) acc[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[m], bv[m], acc[v], 0, 0, 0);
         }
+        if (AFF) {
+          const h8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+#pragma unroll
+          for (int m = 0; m < VM; ++m) asum = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[m], ones, asum, 0, 0, 0);
+        }
       }
       __syncthreads();
     }
-    // partials: acc rows (g = j, h) hold channels of sub-group j
-    float zs = zacc;                         // lanes (r, j) -> sum over j, r = 4 g + h
+    // partials.  zacc: lanes (r, j) -> sum over j per row r = 4 sg + h.
+    float zs = zacc;
     zs += __shfl_xor(zs, 16);
     zs += __shfl_xor(zs, 32);
     if (lane < 16) zred[lane] = zs;
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
+    // acc rows (sg = j, h) hold channels of sub-group j
 #pragma unroll
     for (int v = 0; v < 8; ++v) {
       if ((v >> 1) != j) continue;           // channels 16v..16v+15 belong to sub-group v/2
       const int d = 16 * v + n;
 #pragma unroll
-      for (int h = 0; h < 4; ++h)
-        part[h * kPartF + 4 + d] = __builtin_fmaf(acc[v][h], 1.0f / kAScale, zred[4 * j + h]);
+      for (int hh = 0; hh < 4; ++hh) {
+        const float t = acc[v][hh] + zred[4 * j + hh] - (AFF ? asum[hh] : 0.f);
+        part[hh * kPartF + 4 + d] = t * (1.0f / kAScale);
+      }
     }
   }
 }
