@@ -292,51 +292,76 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_kchan(DecodeArgs a) {
 }
 
 // Log-sum-exp merge of every chunk partial of one (unit, head) -> fp16 output.
-__global__ __launch_bounds__(kD) void k_merge(const float* __restrict__ part,
-                                              uint16_t* __restrict__ out, int nch_total,
-                                              int Hkv) {
-  __shared__ float sw[1024];
-  __shared__ float red[kD];
-  const int u = blockIdx.x, hh = blockIdx.y, d = threadIdx.x;
+// Thread (slice sl, quad q) owns chunks c = sl, sl + 8, ... and channels
+// 4q..4q+3; it issues all its loads (running max m_c, sum l_c, four acc
+// values, 16-byte aligned: 132 floats per head) before using any, so one
+// memory round trip serves a batch of up to kMergeBatch chunks.  The largest
+// m_c (M) is found across slices through LDS, then each thread weights its
+// chunks by 2^(m_c - M) and the slices are summed.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeSlices = kMergeThreads / 32;
+constexpr int kMergeBatch = 8;                // chunks per thread per round trip
+__global__ __launch_bounds__(kMergeThreads) void k_merge(const float* __restrict__ part,
+                                                         uint16_t* __restrict__ out, int nch_total,
+                                                         int Hkv) {
+  __shared__ float smax[kMergeSlices];
+  __shared__ float4 racc[kMergeSlices][32];
+  __shared__ float rl[kMergeSlices];
+  const int u = blockIdx.x, hh = blockIdx.y, t = threadIdx.x;
   const int b = u / Hkv, hk = u % Hkv;
   const float* pu = part + (size_t)u * nch_total * kGqa * kPartStride + hh * kPartStride;
   const size_t cs = (size_t)kGqa * kPartStride;
+  const int q = t & 31, sl = t >> 5;
+  // pass 1: the largest running max over all chunks
   float M = -INFINITY;
-  for (int c = d; c < nch_total; c += kD) M = fmaxf(M, pu[c * cs]);
-  red[d] = M;
+  for (int c = sl; c < nch_total; c += kMergeSlices) M = fmaxf(M, pu[c * cs]);
+  if (q == 0) smax[sl] = M;
   __syncthreads();
-  for (int o = kD / 2; o > 0; o >>= 1) {
-    if (d < o) red[d] = fmaxf(red[d], red[d + o]);
-    __syncthreads();
-  }
-  M = red[0];
-  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kMergeSlices; ++k) M = fmaxf(M, smax[k]);
+  // pass 2: weighted sums, kMergeBatch chunks per round trip
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   float lsum = 0.f;
-  for (int c = d; c < nch_total; c += kD) {
-    const float m = pu[c * cs];
-    const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
-    if (c < 1024) sw[c] = w;
-    lsum = __builtin_fmaf(pu[c * cs + 1], w, lsum);
-  }
-  red[d] = lsum;
-  __syncthreads();
-  for (int o = kD / 2; o > 0; o >>= 1) {
-    if (d < o) red[d] += red[d + o];
-    __syncthreads();
-  }
-  const float l = red[0];
-  float o = 0.f;
-  for (int c = 0; c < nch_total; ++c) {
-    float w;
-    if (c < 1024) {
-      w = sw[c];
-    } else {
-      const float m = pu[c * cs];
-      w = (m == -INFINITY) ? 0.f : exp2f(m - M);
+  for (int c0 = sl; c0 < nch_total; c0 += kMergeSlices * kMergeBatch) {
+    float mv[kMergeBatch], lv[kMergeBatch];
+    float4 av[kMergeBatch];
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const int c = c0 + k * kMergeSlices;
+      const bool ok = c < nch_total;
+      const float* pc = pu + (size_t)(ok ? c : 0) * cs;
+      mv[k] = ok ? pc[0] : -INFINITY;
+      lv[k] = pc[1];
+      av[k] = *reinterpret_cast<const float4*>(pc + 4 + 4 * q);
     }
-    o = __builtin_fmaf(pu[c * cs + 4 + d], w, o);
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const float w = (mv[k] == -INFINITY) ? 0.f : exp2f(mv[k] - M);
+      lsum = __builtin_fmaf(lv[k], w, lsum);
+      o.x = __builtin_fmaf(av[k].x, w, o.x);
+      o.y = __builtin_fmaf(av[k].y, w, o.y);
+      o.z = __builtin_fmaf(av[k].z, w, o.z);
+      o.w = __builtin_fmaf(av[k].w, w, o.w);
+    }
   }
-  out[((size_t)b * Hkv * kGqa + hk * kGqa + hh) * kD + d] = f2h_rne(o / l);
+  racc[sl][q] = o;
+  if (q == 0) rl[sl] = lsum;
+  __syncthreads();
+  if (t < 32) {
+    float4 r = racc[0][t];
+    float l = rl[0];
+#pragma unroll
+    for (int k = 1; k < kMergeSlices; ++k) {
+      const float4 x = racc[k][t];
+      r.x += x.x; r.y += x.y; r.z += x.z; r.w += x.w;
+      l += rl[k];
+    }
+    uint16_t* po = out + ((size_t)b * Hkv * kGqa + hk * kGqa + hh) * kD + 4 * t;
+    po[0] = f2h_rne(r.x / l);
+    po[1] = f2h_rne(r.y / l);
+    po[2] = f2h_rne(r.z / l);
+    po[3] = f2h_rne(r.w / l);
+  }
 }
 
 bool launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, float scale,
@@ -384,7 +409,7 @@ bool launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, flo
       pa.c = a.scale_log2;
       if (nchp[p] > 0 && !launch_decode_pool(lv[p], pa, c.group, nchp[p], U, stream)) return false;
     }
-    k_merge<<<dim3(U, kGqa), kD, 0, s>>>((const float*)ws, (uint16_t*)out, nch_used, c.kv_heads);
+    k_merge<<<dim3(U, kGqa), kMergeThreads, 0, s>>>((const float*)ws, (uint16_t*)out, nch_used, c.kv_heads);
     return hipGetLastError() == hipSuccess;
   } else {
     a.kwords[0] = (const uint32_t*)(cache + L->k_words[0]);
@@ -404,7 +429,7 @@ bool launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, flo
     const int gx = nch0 > 1 ? nch0 : 1;
     k_decode_kchan<<<dim3(gx, U, 2), kDecThreads, 0, s>>>(a);
   }
-  k_merge<<<dim3(U, kGqa), kD, 0, s>>>((const float*)ws, (uint16_t*)out, nch, c.kv_heads);
+  k_merge<<<dim3(U, kGqa), kMergeThreads, 0, s>>>((const float*)ws, (uint16_t*)out, nch, c.kv_heads);
   return hipGetLastError() == hipSuccess;
 }
 
