@@ -174,7 +174,7 @@ const char* kvq_status_str(kvq_status s);
  *            h*stride_h + d (d contiguous; strides in elements, multiples of 8).
  *   scores:  device fp32 [B][T] (tiered; NULL in kchan mode).
  *   T:       tokens per sequence, 1 <= T <= capacity (tiered: n_hi <= cap_hi
- *            and T - n_hi <= cap_lo).
+ *            and T - n_hi <= cap_lo; T <= 262144, else KVQ_ERR_UNSUPPORTED).
  *   n_hi:    tokens per sequence on the hi grid (tiered), 0 <= n_hi <= T.
  *   ranks_out: device int32 [B][T] or NULL (tiered).
  *   ws:      device workspace of at least kvq_workspace_bytes(lay,

@@ -39,10 +39,10 @@ QuantWs quant_ws_plan(const kvq_layout* L, int T) {
     const int64_t nblk = ceil_div(T, kSortTile);
     for (int i = 0; i < 2; ++i) { p.keys[i] = off; off = align256(off + B * T * 4); }
     for (int i = 0; i < 2; ++i) { p.idx[i] = off; off = align256(off + B * T * 4); }
-    p.hist = off;   off = align256(off + B * 256 * nblk * 4);
+    p.hist = off;   off = align256(off + B * 4 * 256 * nblk * 4);   // 4 digit positions
+    p.segcnt = off; off = align256(off + B * ceil_div(T, kSlotSeg) * 4);  // high-tier count per segment
     p.ranks = off;  off = align256(off + B * T * 4);
     for (int i = 0; i < 2; ++i) { p.inv[i] = off; off = align256(off + B * (int64_t)L->cap[i] * 4); }
-    p.bcount = off; off = align256(off + B * nblk * 4);
   }
   p.total = (size_t)(off > 256 ? off : 256);
   return p;
@@ -164,6 +164,7 @@ extern "C" kvq_status kvq_quantize(const kvq_layout* lay, void* cache, const voi
     if (ranks_out && !aligned16(ranks_out)) return KVQ_ERR_ARG;
     if (n_hi < 0 || n_hi > T) return KVQ_ERR_ARG;
     if (n_hi > lay->cap[0] || T - n_hi > lay->cap[1]) return KVQ_ERR_CAPACITY;
+    if (T > kMaxSortLen) return KVQ_ERR_UNSUPPORTED;
     QuantWs plan = quant_ws_plan(lay, T);
     if (!ws || !aligned16(ws) || ws_bytes < plan.total) return KVQ_ERR_WORKSPACE;
     if (!launch_rank_tiers(lay, (uint8_t*)cache, scores, T, n_hi, ranks_out, (uint8_t*)ws, plan, stream))

@@ -53,14 +53,45 @@ struct GroupQ {
   float top;
 };
 
+// RN(a / d) for a = 0 or a in [2^-24, 2^17] (every difference of two fp16
+// values) and d in 2..7, without the IEEE division sequence: the quotient
+// correction q = fma(fma(-q0, d, a), r, q0), q0 = a * r, r = RN(1/d)
+// (Markstein) returns the correctly rounded quotient for d = 2, 3, 4, 5, 7
+// on that whole domain (checked exhaustively against IEEE division); for
+// d = 6 it does not, so a is halved first (exact there) and divided by 3.
+__device__ inline float div_by_small(float a, int d) {
+  if (d < 2 || d > 7) return a / (float)d;        // outside the checked set: IEEE division
+  if (d == 6) {
+    a *= 0.5f;
+    d = 3;
+  }
+  const float df = (float)d;
+  const float r = 1.0f / df;                      // folded at compile time for constant d
+  const float q0 = a * r;
+  const float rho = __builtin_fmaf(-q0, df, a);
+  return __builtin_fmaf(rho, r, q0);
+}
+
+// RN(1 / s) for a positive finite fp16 value s: the hardware reciprocal and
+// one Newton step (checked on the device against IEEE division for every
+// such s).
+__device__ inline float recip_f16_exact(float s) {
+  const float r0 = __builtin_amdgcn_rcpf(s);
+  const float e = __builtin_fmaf(-s, r0, 1.0f);
+  return __builtin_fmaf(r0, e, r0);
+}
+
 __device__ inline GroupQ group_setup(uint32_t mn_bits, uint32_t mx_bits, int L) {
   GroupQ g;
   g.z = h2f(mn_bits);
-  float range = h2f(mx_bits) - g.z;               // fp32, round to nearest even
-  float s32 = range / (float)(L - 1);             // IEEE division
+  const float range = h2f(mx_bits) - g.z;         // fp32, round to nearest even
+  float s32 = div_by_small(range, L - 1);         // = RN(range / (L-1))
+  // keep the fp32 rounding: without this the compiler may fuse the last fma
+  // with the fp16 conversion (one rounding instead of fp32 then fp16)
+  asm volatile("" : "+v"(s32));
   g.s_bits = f2h_rne(s32);
   g.s = h2f(g.s_bits);
-  g.r = (g.s != 0.0f) ? 1.0f / g.s : 0.0f;        // correctly rounded reciprocal
+  g.r = (g.s != 0.0f) ? recip_f16_exact(g.s) : 0.0f;   // = RN(1 / s)
   g.top = (float)(L - 1);
   return g;
 }

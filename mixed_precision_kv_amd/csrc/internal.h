@@ -7,7 +7,9 @@
 
 namespace kvq {
 
-constexpr int kSortTile = 4096;   // keys per radix-sort block (256 threads x 16)
+constexpr int kSortTile = 1024;   // keys per radix-sort block (256 threads x 4)
+constexpr int kSlotSeg = 4096;    // tokens per slot-scan workgroup
+constexpr int kMaxSortLen = 1 << 18;   // longest ranked sequence (tokens)
 
 inline int gcd_i(int a, int b) { while (b) { int t = a % b; a = b; b = t; } return a; }
 inline int lcm_i(int a, int b) { return a / gcd_i(a, b) * b; }
@@ -24,7 +26,7 @@ inline int kchan_nq(const kvq_layout* L, int T) {
 int decode_chunks(const kvq_layout* L, int max_len, int* nch0, int* nch1);
 
 struct QuantWs {           // byte offsets inside the quantize workspace
-  size_t keys[2], idx[2], hist, ranks, inv[2], bcount, total;
+  size_t keys[2], idx[2], hist, segcnt, ranks, inv[2], total;
 };
 QuantWs quant_ws_plan(const kvq_layout* L, int T);
 

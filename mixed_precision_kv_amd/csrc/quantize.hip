@@ -146,8 +146,10 @@ __device__ inline void group_minmax(const uint32_t* x2, int g, uint32_t& mn, uin
   const _Float16 m1 = hi[0] > hi[1] ? hi[0] : hi[1];
   mn = __builtin_bit_cast(uint16_t, m0);
   mx = __builtin_bit_cast(uint16_t, m1);
-  if (((mn & 0x7FFFu) == 0u) || ((mx & 0x7FFFu) == 0u)) {
-    // a zero extreme: settle -0 / +0 in the IEEE total order
+  if (__builtin_expect(((mn & 0x7FFFu) == 0u) || ((mx & 0x7FFFu) == 0u), 0)) {
+    // a zero extreme: settle -0 / +0 in the IEEE total order.  Rare: kept as
+    // a branch (the empty asm stops the compiler from if-converting it)
+    asm volatile("" ::: "memory");
     int kmn = 0x7FFFFFFF, kmx = -0x7FFFFFFF;
     for (int i = 0; i < G / 2; ++i) {
       const uint32_t w = x2[g * G / 2 + i];
@@ -160,13 +162,21 @@ __device__ inline void group_minmax(const uint32_t* x2, int g, uint32_t& mn, uin
   }
 }
 
-__device__ inline float code_of(_Float16 x, const GroupQ& g) {
-  // c = clamp(rint(fl32(x - z) / s), 0, L-1); s == 0 -> 0 (r = 0 makes q = 0)
-  const float a = __builtin_fmaf((float)x, 1.0f, -g.z);   // fl32(x - z), one rounding
+// q = RN(fl32(x - z) / s) by the quotient correction of group_setup (s == 0
+// gives r = 0 and q = 0).  `one` is 1.0 hidden from the optimizer so that
+// x * one - z stays a single mixed-precision fma on the fp16 input.
+__device__ inline float quotient_of(_Float16 x, const GroupQ& g, float one) {
+  const float a = __builtin_fmaf((float)x, one, -g.z);    // fl32(x - z), one rounding
   const float q0 = a * g.r;
   const float rho = __builtin_fmaf(-q0, g.s, a);
-  const float q = __builtin_fmaf(rho, g.r, q0);
-  return fminf(__builtin_rintf(q), g.top);
+  return __builtin_fmaf(rho, g.r, q0);
+}
+// c = clamp(rint(q), 0, L-1) as an fp32 integer (q >= 0): clamping before
+// rounding gives the same code since L-1 is an integer; adding and removing
+// 1.5 * 2^23 rounds to the nearest integer, ties to even.
+__device__ inline float code_of_q(float q, float top) {
+  constexpr float kMagic = 12582912.0f;
+  return (fminf(q, top) + kMagic) - kMagic;
 }
 
 template <int L, int G>
@@ -183,6 +193,8 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows(QuantArgs a) {
   const bool valid = live && s < a.n;
   const bool in_tiles = live && s < a.tiles * kTile;
   const int t = valid ? (a.inv ? a.inv[(size_t)b * a.inv_cap + s] : s) : 0;
+  float one = 1.0f;
+  asm volatile("" : "+v"(one));
   for (int kv = a.kwords ? 0 : 1; kv < 2; ++kv) {
     uint32_t x2[kD / 2];                           // the row as 64 packed fp16 pairs
     if (valid) {
@@ -223,7 +235,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows(QuantArgs a) {
           const int d = w * NV + jj;
           if (d >= kD) continue;
           const h2v pr = h2_from_bits(x2[d / 2]);
-          const float c = code_of(pr[d & 1], gq[d / G]);
+          const float c = code_of_q(quotient_of(pr[d & 1], gq[d / G], one), (float)(L - 1));
           if (jj >= LO) hi = __builtin_fmaf(hi, (float)L, c);
           else lo = __builtin_fmaf(lo, (float)L, c);
         }
@@ -233,33 +245,44 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows(QuantArgs a) {
     } else if (live) {
 #pragma unroll
       for (int d4 = 0; d4 < kD / 4; ++d4) {
+        // codes as bytes: the packed u8 conversion rounds to nearest even
         uint32_t packed = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int d = 4 * d4 + e;
           const h2v pr = h2_from_bits(x2[d / 2]);
-          const uint32_t c = (uint32_t)code_of(pr[d & 1], gq[d / G]);
-          packed |= c << (8 * e);
+          const float q = fminf(quotient_of(pr[d & 1], gq[d / G], one), (float)(L - 1));
+          packed = __builtin_amdgcn_cvt_pk_u8_f32(q, e, packed);
         }
         vcodes[tid][d4] = valid ? packed : 0u;
       }
     }
   }
   __syncthreads();
+  // column words: task (row r, channels 4 d4 .. 4 d4 + 3), one dword of four
+  // byte codes per slot
   const int r0 = s0 / NV;
-  const uint8_t* vc = reinterpret_cast<const uint8_t*>(&vcodes[0][0]);
-  for (int task = tid; task < ROWS * kD; task += kQThreads) {
-    const int r = task / kD, d = task % kD;
+  for (int task = tid; task < ROWS * (kD / 4); task += kQThreads) {
+    const int r = task / (kD / 4), d4 = task % (kD / 4);
     if (r0 + r >= a.vrows) continue;
-    float lo = 0.f, hi = 0.f;
+    float lo[4] = {0.f, 0.f, 0.f, 0.f}, hi[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int jj = NV - 1; jj >= 0; --jj) {
-      const float c = (float)vc[(r * NV + jj) * kD + d];
-      if (jj >= LO) hi = __builtin_fmaf(hi, (float)L, c);
-      else lo = __builtin_fmaf(lo, (float)L, c);
+      const uint32_t c4 = vcodes[r * NV + jj][d4];
+      const float c[4] = {(float)(c4 & 0xFFu), (float)((c4 >> 8) & 0xFFu), (float)((c4 >> 16) & 0xFFu),
+                          (float)(c4 >> 24)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (jj >= LO) hi[e] = __builtin_fmaf(hi[e], (float)L, c[e]);
+        else lo[e] = __builtin_fmaf(lo[e], (float)L, c[e]);
+      }
     }
-    a.vwords[((size_t)u * a.vrows + r0 + r) * kD + d] =
-        __umul24((uint32_t)hi, P::LPOW_LO) + (uint32_t)lo;
+    uint4 wv;
+    wv.x = __umul24((uint32_t)hi[0], P::LPOW_LO) + (uint32_t)lo[0];
+    wv.y = __umul24((uint32_t)hi[1], P::LPOW_LO) + (uint32_t)lo[1];
+    wv.z = __umul24((uint32_t)hi[2], P::LPOW_LO) + (uint32_t)lo[2];
+    wv.w = __umul24((uint32_t)hi[3], P::LPOW_LO) + (uint32_t)lo[3];
+    *reinterpret_cast<uint4*>(&a.vwords[((size_t)u * a.vrows + r0 + r) * kD + 4 * d4]) = wv;
   }
 }
 

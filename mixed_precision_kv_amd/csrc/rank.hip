@@ -6,103 +6,152 @@
 // computed with a least-significant-digit radix sort (4 passes of 8 bits) of
 // the order-preserving u32 key, carrying the token index; each pass is
 // stable, so equal scores stay in token order.  One sort segment per
-// sequence.  Per pass: block histograms -> per-sequence exclusive scan ->
-// stable scatter (wave ballots give each element its rank among equal
-// digits of its wave, LDS counters order the waves and the rounds).
+// sequence, cut into blocks of kSortTile keys.  Per pass: per-(digit,
+// block) counts -> stable scatter, each block deriving its own output
+// offsets from the counts (wave ballots give each element its rank among
+// equal digits of its wave, LDS counters order the waves and the rounds).
+// The first pass's counts come from the kernel that forms the keys; the last
+// pass writes the ranks and the ascending score array instead of keys.
+// Slots (index among same-tier tokens in token order) come from one scan per
+// sequence.
 #include "common.h"
 #include "internal.h"
 
 namespace kvq {
 
 constexpr int kSortThreads = 256;
-constexpr int kSortItems = kSortTile / kSortThreads;   // 16, striped
+constexpr int kSortItems = kSortTile / kSortThreads;   // 4, striped
 
-__global__ __launch_bounds__(256) void k_key_init(const float* __restrict__ scores,
-                                                  uint32_t* __restrict__ keys,
-                                                  uint32_t* __restrict__ idx, int T) {
-  const int b = blockIdx.y;
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t < T) {
-    keys[(size_t)b * T + t] = score_desc_key(scores[(size_t)b * T + t]);
-    idx[(size_t)b * T + t] = (uint32_t)t;
-  }
+// Workgroups are handed to the 8 XCDs round-robin by linear id, and each XCD
+// has its own L2.  The sort kernels run on a 1-D grid of 8 * ceil(B / 8) *
+// nblk workgroups mapped so that every block of sequence b runs on XCD b % 8:
+// the scattered 4-byte writes of one sequence then meet in one L2 instead of
+// partial lines in several.
+constexpr int kXcds = 8;
+__device__ inline bool seq_block(int nblk, int B, int& b, int& blk) {
+  const int id = blockIdx.x, x = id % kXcds, k = id / kXcds;
+  b = x + kXcds * (k / nblk);
+  blk = k % nblk;
+  return b < B;
 }
+static inline dim3 seq_grid(int nblk, int B) { return dim3(kXcds * ((B + kXcds - 1) / kXcds) * nblk); }
 
-__global__ __launch_bounds__(256) void k_hist(const uint32_t* __restrict__ keys,
-                                              uint32_t* __restrict__ hist, int T, int nblk,
-                                              int shift) {
+// hist layout: [b][pass][blk][digit].  The first kernel forms the keys and
+// the pass-0 counts, and zeroes the per-segment counts of high-tier tokens
+// (filled by the last scatter).
+__global__ __launch_bounds__(256) void k_rank_keys(const float* __restrict__ scores,
+                                                   uint32_t* __restrict__ keys,
+                                                   uint32_t* __restrict__ hist,
+                                                   uint32_t* __restrict__ segcnt, int T, int nblk,
+                                                   int nseg, int B) {
   __shared__ uint32_t h[256];
-  const int tid = threadIdx.x, blk = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x;
+  int b, blk;
+  if (!seq_block(nblk, B, b, blk)) return;
   h[tid] = 0;
   __syncthreads();
-  const uint32_t* kb = keys + (size_t)b * T;
-  const int base = blk * kSortTile;
+#pragma unroll
   for (int j = 0; j < kSortItems; ++j) {
-    int i = base + j * kSortThreads + tid;
-    if (i < T) atomicAdd(&h[(kb[i] >> shift) & 255u], 1u);
+    const int i = blk * kSortTile + j * kSortThreads + tid;
+    if (i < T) {
+      const uint32_t key = score_desc_key(scores[(size_t)b * T + i]);
+      keys[(size_t)b * T + i] = key;
+      atomicAdd(&h[key & 255u], 1u);
+    }
   }
   __syncthreads();
-  hist[((size_t)b * 256 + tid) * nblk + blk] = h[tid];
+  hist[(((size_t)b * 4 + 0) * nblk + blk) * 256 + tid] = h[tid];
+  if (blk == 0)
+    for (int k = tid; k < nseg; k += 256) segcnt[(size_t)b * nseg + k] = 0u;
 }
 
-// Exclusive scan of a 256-entry block-wide value (Hillis-Steele in LDS).
-__device__ inline uint32_t block_excl_scan256(uint32_t v, uint32_t* sh, uint32_t* total) {
+// Per-block counts of one pass's digit in the current key order.
+__global__ __launch_bounds__(256) void k_rank_count(const uint32_t* __restrict__ keys,
+                                                    uint32_t* __restrict__ hist, int T, int nblk,
+                                                    int pass, int B) {
+  __shared__ uint32_t h[256];
   const int tid = threadIdx.x;
-  sh[tid] = v;
+  int b, blk;
+  if (!seq_block(nblk, B, b, blk)) return;
+  h[tid] = 0;
   __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    uint32_t t = tid >= off ? sh[tid - off] : 0u;
-    __syncthreads();
-    sh[tid] += t;
-    __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kSortItems; ++j) {
+    const int i = blk * kSortTile + j * kSortThreads + tid;
+    if (i < T) atomicAdd(&h[(keys[(size_t)b * T + i] >> (8 * pass)) & 255u], 1u);
   }
-  uint32_t incl = sh[tid];
-  *total = sh[255];
   __syncthreads();
-  return incl - v;
+  hist[(((size_t)b * 4 + pass) * nblk + blk) * 256 + tid] = h[tid];
 }
 
-// One block per sequence: exclusive scan of hist[b] laid out digit-major
-// ([digit][blk]), so offsets order by digit, then by block.
-__global__ __launch_bounds__(256) void k_scan(uint32_t* __restrict__ hist, int nblk) {
-  __shared__ uint32_t sh[256];
-  const int tid = threadIdx.x, b = blockIdx.x;
-  uint32_t* hb = hist + (size_t)b * 256 * nblk;
-  uint32_t sum = 0;
-  for (int j = 0; j < nblk; ++j) sum += hb[tid * nblk + j];
-  uint32_t total;
-  uint32_t run = block_excl_scan256(sum, sh, &total);
-  for (int j = 0; j < nblk; ++j) {
-    uint32_t c = hb[tid * nblk + j];
-    hb[tid * nblk + j] = run;
-    run += c;
-  }
-}
+struct ScatterArgs {
+  const uint32_t* kin;
+  const uint32_t* iin;          // null: the token index itself (first pass)
+  uint32_t* kout;
+  uint32_t* iout;
+  const uint32_t* hist;         // this pass's offsets
+  int T, nblk, pass;
+  // last pass: ranks, the ascending score array, high-tier counts per segment
+  const float* scores;
+  int32_t* ranks;
+  int32_t* ranks_out;
+  float* sorted_asc;
+  uint32_t* segcnt;
+  int cap, n_hi, nseg, B;
+};
 
-__global__ __launch_bounds__(256) void k_scatter(const uint32_t* __restrict__ kin,
-                                                 const uint32_t* __restrict__ iin,
-                                                 uint32_t* __restrict__ kout,
-                                                 uint32_t* __restrict__ iout,
-                                                 const uint32_t* __restrict__ hist, int T,
-                                                 int nblk, int shift) {
+// One pass of the stable LSD sort.
+__global__ __launch_bounds__(256) void k_rank_scatter(ScatterArgs a) {
   __shared__ uint32_t goff[256];
   __shared__ uint32_t cnt[4][256];
   __shared__ uint32_t run[256];
-  const int tid = threadIdx.x, blk = blockIdx.x, b = blockIdx.y;
+  __shared__ uint32_t segl[kMaxSortLen / kSlotSeg];   // last pass: high-tier tokens per segment
+  const int tid = threadIdx.x;
+  int b, blk;
+  if (!seq_block(a.nblk, a.B, b, blk)) return;
   const int lane = tid & 63, w = tid >> 6;
-  goff[tid] = hist[((size_t)b * 256 + tid) * nblk + blk];
+  const int shift = 8 * a.pass;
+  const bool last = a.pass == 3;
+  {
+    // output offset of (digit tid, this block) = keys with a smaller digit +
+    // keys with this digit in earlier blocks (counts read 16 blocks per trip)
+    const uint32_t* hp = a.hist + ((size_t)b * 4 + a.pass) * a.nblk * 256;
+    uint32_t before = 0, total = 0;
+    for (int j0 = 0; j0 < a.nblk; j0 += 16) {
+      uint32_t c[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) c[k] = (j0 + k < a.nblk) ? hp[(size_t)(j0 + k) * 256 + tid] : 0u;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        total += c[k];
+        before += (j0 + k < blk) ? c[k] : 0u;
+      }
+    }
+    cnt[0][tid] = total;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const uint32_t t = tid >= off ? cnt[0][tid - off] : 0u;
+      __syncthreads();
+      cnt[0][tid] += t;
+      __syncthreads();
+    }
+    goff[tid] = cnt[0][tid] - total + before;
+  }
   run[tid] = 0;
-  const size_t sb = (size_t)b * T;
+  if (tid < kMaxSortLen / kSlotSeg) segl[tid] = 0;
+  const size_t sb = (size_t)b * a.T;
   const int base = blk * kSortTile;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int j = 0; j < kSortItems; ++j) {
     for (int x = 0; x < 4; ++x) cnt[x][tid] = 0;
     __syncthreads();
     const int i = base + j * kSortThreads + tid;
-    const bool valid = i < T;
-    const uint32_t key = valid ? kin[sb + i] : 0u;
+    const bool valid = i < a.T;
+    const uint32_t key = valid ? a.kin[sb + i] : 0u;
+    const uint32_t idx = valid ? (a.iin ? a.iin[sb + i] : (uint32_t)i) : 0u;
     const uint32_t d = (key >> shift) & 255u;
     uint64_t peers = __ballot(valid);
+#pragma unroll
     for (int bit = 0; bit < 8; ++bit) {
       const bool on = (d >> bit) & 1u;
       const uint64_t bb = __ballot(on);
@@ -123,91 +172,80 @@ __global__ __launch_bounds__(256) void k_scatter(const uint32_t* __restrict__ ki
     __syncthreads();
     if (valid) {
       const uint32_t pos = goff[d] + cnt[w][d] + rank_w;
-      kout[sb + pos] = key;
-      iout[sb + pos] = iin[sb + i];
+      if (!last) {
+        a.kout[sb + pos] = key;
+        a.iout[sb + pos] = idx;
+      } else {
+        a.ranks[sb + idx] = (int32_t)pos;
+        if (a.ranks_out) a.ranks_out[sb + idx] = (int32_t)pos;
+        a.sorted_asc[(size_t)b * a.cap + (a.T - 1 - pos)] = a.scores[sb + idx];
+        if ((int)pos < a.n_hi) atomicAdd(&segl[idx / kSlotSeg], 1u);
+      }
     }
     __syncthreads();
   }
+  if (last && tid < a.nseg && segl[tid]) atomicAdd(&a.segcnt[(size_t)b * a.nseg + tid], segl[tid]);
 }
 
-// rank[t] = sorted position; the ascending score array for the running
-// median is the sorted order reversed.
-__global__ __launch_bounds__(256) void k_rank_write(const uint32_t* __restrict__ idx,
-                                                    const float* __restrict__ scores,
-                                                    int32_t* __restrict__ ranks,
-                                                    int32_t* __restrict__ ranks_out,
-                                                    float* __restrict__ sorted_asc, int T,
-                                                    int cap) {
-  const int b = blockIdx.y;
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= T) return;
-  const uint32_t t = idx[(size_t)b * T + i];
-  ranks[(size_t)b * T + t] = i;
-  if (ranks_out) ranks_out[(size_t)b * T + t] = i;
-  sorted_asc[(size_t)b * cap + (T - 1 - i)] = scores[(size_t)b * T + t];
-}
-
-__global__ __launch_bounds__(256) void k_count_hi(const int32_t* __restrict__ ranks,
-                                                  uint32_t* __restrict__ bcount, int T, int nblk,
-                                                  int n_hi) {
-  __shared__ uint32_t sh[256];
-  const int tid = threadIdx.x, blk = blockIdx.x, b = blockIdx.y;
-  uint32_t c = 0;
-  for (int j = 0; j < kSortItems; ++j) {
-    int t = blk * kSortTile + j * kSortThreads + tid;
-    if (t < T && ranks[(size_t)b * T + t] < n_hi) ++c;
-  }
-  uint32_t total;
-  block_excl_scan256(c, sh, &total);
-  if (tid == 0) bcount[(size_t)b * nblk + blk] = total;
-}
-
-// Slot = index among same-tier tokens in token order.  Each thread owns 16
-// consecutive tokens; the block scans thread counts; earlier blocks' counts
-// are summed directly (a sequence has at most a few dozen blocks).
-__global__ __launch_bounds__(256) void k_slots(const int32_t* __restrict__ ranks,
-                                               const uint32_t* __restrict__ bcount,
-                                               uint32_t* __restrict__ tokmap,
-                                               int32_t* __restrict__ inv_hi,
-                                               int32_t* __restrict__ inv_lo,
-                                               int32_t* __restrict__ counters, int T, int nblk,
-                                               int n_hi, int cap, int cap_hi, int cap_lo) {
-  __shared__ uint32_t sh[256];
-  __shared__ uint32_t prefix;
-  const int tid = threadIdx.x, blk = blockIdx.x, b = blockIdx.y;
+// Slot = index among same-tier tokens in token order.  Workgroup (seg, b)
+// owns tokens [seg * kSlotSeg, (seg + 1) * kSlotSeg); earlier segments'
+// high-tier counts give its base; wave w owns a contiguous quarter, read in
+// 64-token chunks (coalesced) with ballots for the in-chunk prefix.
+__global__ __launch_bounds__(256) void k_rank_slots(const int32_t* __restrict__ ranks,
+                                                    const uint32_t* __restrict__ segcnt,
+                                                    uint32_t* __restrict__ tokmap,
+                                                    int32_t* __restrict__ inv_hi,
+                                                    int32_t* __restrict__ inv_lo,
+                                                    int32_t* __restrict__ counters, int T, int n_hi,
+                                                    int cap, int cap_hi, int cap_lo, int nseg, int B) {
+  constexpr int kChunks = kSlotSeg / 4 / 64;          // 64-token chunks per wave
+  __shared__ uint32_t wtot[4];
+  __shared__ uint32_t segbase;
+  const int tid = threadIdx.x;
+  int b, seg;
+  if (!seq_block(nseg, B, b, seg)) return;
+  const int lane = tid & 63, w = tid >> 6;
   if (tid == 0) {
     uint32_t p = 0;
-    for (int j = 0; j < blk; ++j) p += bcount[(size_t)b * nblk + j];
-    prefix = p;
-    if (blk == 0) {
+    for (int k = 0; k < seg; ++k) p += segcnt[(size_t)b * nseg + k];
+    segbase = p;
+    if (seg == 0) {
       counters[b * 4 + 0] = T;
       counters[b * 4 + 1] = n_hi;
       counters[b * 4 + 2] = T - n_hi;
       counters[b * 4 + 3] = 0;
     }
   }
-  const int t0 = blk * kSortTile + tid * kSortItems;
-  bool hi[kSortItems];
-  uint32_t c = 0;
-  for (int j = 0; j < kSortItems; ++j) {
-    int t = t0 + j;
-    hi[j] = t < T && ranks[(size_t)b * T + t] < n_hi;
-    c += hi[j];
+  const int t0 = seg * kSlotSeg + w * (kSlotSeg / 4);
+  const int32_t* rb = ranks + (size_t)b * T;
+  uint64_t m[kChunks];
+  uint32_t mine = 0;
+#pragma unroll
+  for (int k = 0; k < kChunks; ++k) {
+    const int t = t0 + k * 64 + lane;
+    m[k] = __ballot(t < T && rb[t] < n_hi);
+    mine += (uint32_t)__popcll(m[k]);
   }
-  uint32_t total;
-  uint32_t pre = block_excl_scan256(c, sh, &total) + prefix;
-  for (int j = 0; j < kSortItems; ++j) {
-    int t = t0 + j;
-    if (t >= T) break;
-    if (hi[j]) {
-      tokmap[(size_t)b * cap + t] = pre;
-      inv_hi[(size_t)b * cap_hi + pre] = t;
-      ++pre;
-    } else {
-      uint32_t slot = (uint32_t)t - pre;
-      tokmap[(size_t)b * cap + t] = slot | 0x80000000u;
-      inv_lo[(size_t)b * cap_lo + slot] = t;
+  if (lane == 0) wtot[w] = mine;
+  __syncthreads();
+  uint32_t pre = segbase;
+  for (int k = 0; k < w; ++k) pre += wtot[k];
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int k = 0; k < kChunks; ++k) {
+    const int t = t0 + k * 64 + lane;
+    if (t < T) {
+      const uint32_t hb = pre + (uint32_t)__popcll(m[k] & lt_mask);   // high-tier tokens before t
+      if ((m[k] >> lane) & 1ull) {
+        tokmap[(size_t)b * cap + t] = hb;
+        inv_hi[(size_t)b * cap_hi + hb] = t;
+      } else {
+        const uint32_t slot = (uint32_t)t - hb;
+        tokmap[(size_t)b * cap + t] = slot | 0x80000000u;
+        inv_lo[(size_t)b * cap_lo + slot] = t;
+      }
     }
+    pre += (uint32_t)__popcll(m[k]);
   }
 }
 
@@ -216,29 +254,38 @@ bool launch_rank_tiers(const kvq_layout* L, uint8_t* cache, const float* scores,
   hipStream_t s = (hipStream_t)stream;
   const int B = L->cfg.batch;
   const int nblk = ceil_div(T, kSortTile);
+  const int nseg = ceil_div(T, kSlotSeg);
   uint32_t* keys[2] = {(uint32_t*)(ws + plan.keys[0]), (uint32_t*)(ws + plan.keys[1])};
   uint32_t* idx[2] = {(uint32_t*)(ws + plan.idx[0]), (uint32_t*)(ws + plan.idx[1])};
   uint32_t* hist = (uint32_t*)(ws + plan.hist);
+  uint32_t* segcnt = (uint32_t*)(ws + plan.segcnt);
   int32_t* ranks = (int32_t*)(ws + plan.ranks);
   int32_t* inv_hi = (int32_t*)(ws + plan.inv[0]);
   int32_t* inv_lo = (int32_t*)(ws + plan.inv[1]);
-  uint32_t* bcount = (uint32_t*)(ws + plan.bcount);
-  dim3 g256(ceil_div(T, 256), B), gblk(nblk, B);
-  k_key_init<<<g256, 256, 0, s>>>(scores, keys[0], idx[0], T);
+  const dim3 gblk = seq_grid(nblk, B);
+  k_rank_keys<<<gblk, kSortThreads, 0, s>>>(scores, keys[0], hist, segcnt, T, nblk, nseg, B);
   int cur = 0;
   for (int pass = 0; pass < 4; ++pass) {
-    k_hist<<<gblk, 256, 0, s>>>(keys[cur], hist, T, nblk, pass * 8);
-    k_scan<<<B, 256, 0, s>>>(hist, nblk);
-    k_scatter<<<gblk, 256, 0, s>>>(keys[cur], idx[cur], keys[cur ^ 1], idx[cur ^ 1], hist, T, nblk,
-                                   pass * 8);
+    if (pass > 0) k_rank_count<<<gblk, kSortThreads, 0, s>>>(keys[cur], hist, T, nblk, pass, B);
+    ScatterArgs a;
+    a.kin = keys[cur];
+    a.iin = pass == 0 ? nullptr : idx[cur];
+    a.kout = keys[cur ^ 1];
+    a.iout = idx[cur ^ 1];
+    a.hist = hist;
+    a.T = T; a.nblk = nblk; a.pass = pass;
+    a.scores = scores;
+    a.ranks = ranks;
+    a.ranks_out = ranks_out;
+    a.sorted_asc = (float*)(cache + L->sorted);
+    a.segcnt = segcnt;
+    a.cap = L->cfg.capacity; a.n_hi = n_hi; a.nseg = nseg; a.B = B;
+    k_rank_scatter<<<gblk, kSortThreads, 0, s>>>(a);
     cur ^= 1;
   }
-  k_rank_write<<<g256, 256, 0, s>>>(idx[cur], scores, ranks, ranks_out,
-                                    (float*)(cache + L->sorted), T, L->cfg.capacity);
-  k_count_hi<<<gblk, 256, 0, s>>>(ranks, bcount, T, nblk, n_hi);
-  k_slots<<<gblk, 256, 0, s>>>(ranks, bcount, (uint32_t*)(cache + L->tokmap), inv_hi, inv_lo,
-                               (int32_t*)(cache + L->counters), T, nblk, n_hi, L->cfg.capacity,
-                               L->cap[0], L->cap[1]);
+  k_rank_slots<<<seq_grid(nseg, B), 256, 0, s>>>(ranks, segcnt, (uint32_t*)(cache + L->tokmap),
+                                                 inv_hi, inv_lo, (int32_t*)(cache + L->counters), T,
+                                                 n_hi, L->cfg.capacity, L->cap[0], L->cap[1], nseg, B);
   return hipGetLastError() == hipSuccess;
 }
 
