@@ -114,53 +114,27 @@ __global__ __launch_bounds__(kQThreads) void k_quant_pool(QuantArgs a) {
   }
 }
 
-// ---- row kernel: one thread per slot row (fast path, L <= 8) ----
+// ---- row kernel: sixteen lanes per slot row (fast path, L <= 8) ----
 //
-// Thread i of a workgroup owns slot s0 + i: it loads the token's 128-value key
-// row, finds each group's min/max with packed fp16 min/max (IEEE min/max do
-// not order -0 and +0, so a zero result is redone in the total order), forms
-// the fp16 scale and zero, computes every code with the exact quotient of
-// group_setup/quant_value, and Horner-packs the row words in fp32 halves
-// (exact below 2^24) joined by one 24-bit integer multiply-add.  The value
-// row is coded the same way into LDS bytes; column words are packed after a
-// barrier by (row, channel) tasks.
+// Lane l of a 16-lane row group holds channels 8l..8l+7 of one slot row, so
+// each row is read as one contiguous 256-byte piece.  Thread (row group rg,
+// lane l) handles rows rg, rg + 16, ... of the workgroup's slots.  A group's
+// min/max combines the lanes of the group with lane shuffles (IEEE min/max
+// do not order -0 and +0; if any extreme is a zero, the wave redoes the
+// reduction in the total order); each lane then forms its group's fp16
+// scale and zero and codes its eight values with the exact quotient of
+// group_setup.  Codes go to LDS as bytes; key row words (along head_dim) and
+// value column words (along slots) are packed from there in fp32 Horner
+// halves (exact below 2^24) joined by one 24-bit integer multiply-add.
 template <int L>
 struct RowPack {
   static constexpr int NV = cpw(L);
   static constexpr int KW = (kD + NV - 1) / NV;
   static constexpr int LO = NV / 2;               // low digits per word (L^LO < 2^24)
   static constexpr uint32_t LPOW_LO = ipow(L, LO);
+  static constexpr int ROWS = NV >= 256 ? 1 : 256 / NV;   // value word rows per workgroup
+  static constexpr int SL = ROWS * NV;                    // slots per workgroup (<= 256)
 };
-
-template <int G>
-__device__ inline void group_minmax(const uint32_t* x2, int g, uint32_t& mn, uint32_t& mx) {
-  // x2: 64 packed fp16 pairs of the row; group g covers pairs [g*G/2, (g+1)*G/2)
-  h2v lo = h2_from_bits(x2[g * G / 2]), hi = lo;
-#pragma unroll
-  for (int i = 1; i < G / 2; ++i) {
-    const h2v v = h2_from_bits(x2[g * G / 2 + i]);
-    lo = __builtin_elementwise_min(lo, v);
-    hi = __builtin_elementwise_max(hi, v);
-  }
-  const _Float16 m0 = lo[0] < lo[1] ? lo[0] : lo[1];
-  const _Float16 m1 = hi[0] > hi[1] ? hi[0] : hi[1];
-  mn = __builtin_bit_cast(uint16_t, m0);
-  mx = __builtin_bit_cast(uint16_t, m1);
-  if (__builtin_expect(((mn & 0x7FFFu) == 0u) || ((mx & 0x7FFFu) == 0u), 0)) {
-    // a zero extreme: settle -0 / +0 in the IEEE total order.  Rare: kept as
-    // a branch (the empty asm stops the compiler from if-converting it)
-    asm volatile("" ::: "memory");
-    int kmn = 0x7FFFFFFF, kmx = -0x7FFFFFFF;
-    for (int i = 0; i < G / 2; ++i) {
-      const uint32_t w = x2[g * G / 2 + i];
-      const int k0 = f16_order_key(w & 0xFFFFu), k1 = f16_order_key(w >> 16);
-      kmn = min(kmn, min(k0, k1));
-      kmx = max(kmx, max(k0, k1));
-    }
-    mn = f16_from_order_key(kmn);
-    mx = f16_from_order_key(kmx);
-  }
-}
 
 // q = RN(fl32(x - z) / s) by the quotient correction of group_setup (s == 0
 // gives r = 0 and q = 0).  `one` is 1.0 hidden from the optimizer so that
@@ -171,118 +145,144 @@ __device__ inline float quotient_of(_Float16 x, const GroupQ& g, float one) {
   const float rho = __builtin_fmaf(-q0, g.s, a);
   return __builtin_fmaf(rho, g.r, q0);
 }
-// c = clamp(rint(q), 0, L-1) as an fp32 integer (q >= 0): clamping before
-// rounding gives the same code since L-1 is an integer; adding and removing
-// 1.5 * 2^23 rounds to the nearest integer, ties to even.
-__device__ inline float code_of_q(float q, float top) {
-  constexpr float kMagic = 12582912.0f;
-  return (fminf(q, top) + kMagic) - kMagic;
+
+// Two fp16 bit patterns per word mapped to 16-bit keys whose unsigned order
+// is the IEEE total order (-0 below +0): positive values get the sign bit
+// set, negative ones are complemented.
+__device__ inline uint32_t f16x2_order_key(uint32_t b) {
+  const uint32_t neg = (b >> 15) & 0x00010001u;
+  return b ^ 0x80008000u ^ (neg * 0x7FFFu);
+}
+__device__ inline uint32_t f16_from_key16(uint32_t k) {
+  return (k & 0x8000u) ? (k ^ 0x8000u) : (~k & 0xFFFFu);
+}
+
+// Group extremes (fp16 bits, IEEE total order) of eight values per lane over
+// the G/8 lanes of the group (aligned lane blocks of a 16-lane row).  The
+// reduction runs on integer keys in plain 32-bit registers.
+template <int G>
+__device__ inline void row_group_minmax(uint4 x, uint32_t& mn, uint32_t& mx) {
+  const uint32_t k[4] = {f16x2_order_key(x.x), f16x2_order_key(x.y), f16x2_order_key(x.z),
+                         f16x2_order_key(x.w)};
+  uint32_t lo = 0xFFFFu, hi = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lo = min(lo, min(k[i] & 0xFFFFu, k[i] >> 16));
+    hi = max(hi, max(k[i] & 0xFFFFu, k[i] >> 16));
+  }
+#pragma unroll
+  for (int o = 1; o < G / 8; o <<= 1) {
+    const uint32_t f = (uint32_t)__shfl_xor((int)(lo | (hi << 16)), o, 16);
+    lo = min(lo, f & 0xFFFFu);
+    hi = max(hi, f >> 16);
+  }
+  mn = f16_from_key16(lo);
+  mx = f16_from_key16(hi);
 }
 
 template <int L, int G>
 __global__ __launch_bounds__(kQThreads) void k_quant_rows(QuantArgs a) {
   using P = RowPack<L>;
-  constexpr int NV = P::NV, KW = P::KW, LO = P::LO, NG = kD / G;
-  const int ROWS = rows_per_wg(NV), SL = ROWS * NV;
-  __shared__ uint32_t vcodes[256][kD / 4];         // value codes, 4 per word, [slot][d/4]
+  constexpr int NV = P::NV, KW = P::KW, LO = P::LO, NG = kD / G, SL = P::SL, ROWS = P::ROWS;
+  constexpr int RPT = (SL + 15) / 16;              // rows per thread
+  constexpr int CW = kD / 4 + 1;                   // dwords per code row (+1: bank spread)
+  __shared__ uint32_t codes[SL][CW];               // byte codes, [slot][channel]
+  __shared__ int tok[256];
   const int tid = threadIdx.x, u = blockIdx.y;
   const int b = u / a.Hkv, h = u % a.Hkv;
   const int s0 = blockIdx.x * SL;
-  const int s = s0 + tid;
-  const bool live = tid < SL;
-  const bool valid = live && s < a.n;
-  const bool in_tiles = live && s < a.tiles * kTile;
-  const int t = valid ? (a.inv ? a.inv[(size_t)b * a.inv_cap + s] : s) : 0;
+  const int l16 = tid & 15, rg = tid >> 4;
+  {
+    const int s = s0 + tid;
+    tok[tid] = (tid < SL && s < a.n) ? (a.inv ? a.inv[(size_t)b * a.inv_cap + s] : s) : -1;
+  }
+  __syncthreads();
   float one = 1.0f;
   asm volatile("" : "+v"(one));
+  const int tiled = a.tiles * kTile;
   for (int kv = a.kwords ? 0 : 1; kv < 2; ++kv) {
-    uint32_t x2[kD / 2];                           // the row as 64 packed fp16 pairs
-    if (valid) {
-      const uint16_t* src = (kv ? a.v : a.k) + b * a.sb + (int64_t)t * a.st + h * a.sh;
+    const uint16_t* base = (kv ? a.v : a.k) + b * a.sb + h * a.sh + 8 * l16;
+    uint4 x[RPT];
 #pragma unroll
-      for (int i = 0; i < kD / 8; ++i) {
-        const uint4 r = *reinterpret_cast<const uint4*>(src + 8 * i);
-        x2[4 * i] = r.x; x2[4 * i + 1] = r.y; x2[4 * i + 2] = r.z; x2[4 * i + 3] = r.w;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kD / 2; ++i) x2[i] = 0u;
+    for (int k = 0; k < RPT; ++k) {
+      const int r = rg + 16 * k;
+      const int t = r < SL ? tok[r] : -1;
+      x[k] = t >= 0 ? *reinterpret_cast<const uint4*>(base + (int64_t)t * a.st) : make_uint4(0u, 0u, 0u, 0u);
     }
-    GroupQ gq[NG];
-    uint32_t meta[NG];
+    uint32_t* mp = kv ? a.vmeta : a.kmeta;
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
+    for (int k = 0; k < RPT; ++k) {
+      const int r = rg + 16 * k;                   // uniform over the 16 lanes of the row
+      if (r >= SL) continue;
+      const int s = s0 + r;
+      const bool valid = tok[r] >= 0;
       uint32_t mn, mx;
-      group_minmax<G>(x2, g, mn, mx);
-      gq[g] = group_setup(mn, mx, L);
-      if (gq[g].s == 0.0f) gq[g].r = 0.0f;         // all codes 0
-      meta[g] = valid ? (gq[g].s_bits | (mn << 16)) : 0u;
-    }
-    if (in_tiles) {
-      uint32_t* mp = kv ? a.vmeta : a.kmeta;
+      row_group_minmax<G>(x[k], mn, mx);
+      GroupQ gq = group_setup(mn, mx, L);
+      if (gq.s == 0.0f) gq.r = 0.0f;               // all codes 0
+      // codes as bytes: the packed u8 conversion rounds to nearest even
+      const uint32_t w4[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
+      uint32_t c[2] = {0u, 0u};
 #pragma unroll
-      for (int g = 0; g < NG; ++g)
-        mp[(((size_t)u * a.tiles + s / kTile) * NG + g) * kTile + (s % kTile)] = meta[g];
+      for (int e = 0; e < 8; ++e) {
+        const h2v pr = h2_from_bits(w4[e / 2]);
+        const float q = fminf(quotient_of(pr[e & 1], gq, one), (float)(L - 1));
+        c[e / 4] = __builtin_amdgcn_cvt_pk_u8_f32(q, e & 3, c[e / 4]);
+      }
+      codes[r][2 * l16] = valid ? c[0] : 0u;
+      codes[r][2 * l16 + 1] = valid ? c[1] : 0u;
+      if ((l16 % (G / 8)) == 0 && s < tiled) {
+        const int g = l16 / (G / 8);
+        mp[(((size_t)u * a.tiles + s / kTile) * NG + g) * kTile + (s % kTile)] =
+            valid ? (gq.s_bits | (mn << 16)) : 0u;
+      }
     }
+    __syncthreads();
     if (kv == 0) {
-      // row words: digits along head_dim, fp32 Horner over each half of a word
-      uint32_t* kp = a.kwords + ((size_t)u * a.tiles + s / kTile) * KW * kTile + (s % kTile);
-#pragma unroll
-      for (int w = 0; w < KW; ++w) {
+      // key row words: task (word w, slot r), slots fastest
+      for (int task = tid; task < KW * SL; task += kQThreads) {
+        const int w = task / SL, r = task % SL, s = s0 + r;
+        if (s >= tiled) continue;
+        const uint8_t* cb = reinterpret_cast<const uint8_t*>(&codes[r][0]);
         float lo = 0.f, hi = 0.f;
 #pragma unroll
         for (int jj = NV - 1; jj >= 0; --jj) {
           const int d = w * NV + jj;
           if (d >= kD) continue;
-          const h2v pr = h2_from_bits(x2[d / 2]);
-          const float c = code_of_q(quotient_of(pr[d & 1], gq[d / G], one), (float)(L - 1));
-          if (jj >= LO) hi = __builtin_fmaf(hi, (float)L, c);
-          else lo = __builtin_fmaf(lo, (float)L, c);
+          const float cf = (float)cb[d];
+          if (jj >= LO) hi = __builtin_fmaf(hi, (float)L, cf);
+          else lo = __builtin_fmaf(lo, (float)L, cf);
         }
-        const uint32_t word = __umul24((uint32_t)hi, P::LPOW_LO) + (uint32_t)lo;
-        if (in_tiles) kp[w * kTile] = valid ? word : 0u;
+        a.kwords[(((size_t)u * a.tiles + s / kTile) * KW + w) * kTile + (s % kTile)] =
+            __umul24((uint32_t)hi, P::LPOW_LO) + (uint32_t)lo;
       }
-    } else if (live) {
+    } else {
+      // value column words: task (word row rr, channels 4 d4 .. 4 d4 + 3)
+      const int r0 = s0 / NV;
+      for (int task = tid; task < ROWS * (kD / 4); task += kQThreads) {
+        const int rr = task / (kD / 4), d4 = task % (kD / 4);
+        if (r0 + rr >= a.vrows) continue;
+        float lo[4] = {0.f, 0.f, 0.f, 0.f}, hi[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int d4 = 0; d4 < kD / 4; ++d4) {
-        // codes as bytes: the packed u8 conversion rounds to nearest even
-        uint32_t packed = 0;
+        for (int jj = NV - 1; jj >= 0; --jj) {
+          const uint32_t c4 = codes[rr * NV + jj][d4];
+          const float cf[4] = {(float)(c4 & 0xFFu), (float)((c4 >> 8) & 0xFFu),
+                               (float)((c4 >> 16) & 0xFFu), (float)(c4 >> 24)};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int d = 4 * d4 + e;
-          const h2v pr = h2_from_bits(x2[d / 2]);
-          const float q = fminf(quotient_of(pr[d & 1], gq[d / G], one), (float)(L - 1));
-          packed = __builtin_amdgcn_cvt_pk_u8_f32(q, e, packed);
+          for (int e = 0; e < 4; ++e) {
+            if (jj >= LO) hi[e] = __builtin_fmaf(hi[e], (float)L, cf[e]);
+            else lo[e] = __builtin_fmaf(lo[e], (float)L, cf[e]);
+          }
         }
-        vcodes[tid][d4] = valid ? packed : 0u;
+        uint4 wv;
+        wv.x = __umul24((uint32_t)hi[0], P::LPOW_LO) + (uint32_t)lo[0];
+        wv.y = __umul24((uint32_t)hi[1], P::LPOW_LO) + (uint32_t)lo[1];
+        wv.z = __umul24((uint32_t)hi[2], P::LPOW_LO) + (uint32_t)lo[2];
+        wv.w = __umul24((uint32_t)hi[3], P::LPOW_LO) + (uint32_t)lo[3];
+        *reinterpret_cast<uint4*>(&a.vwords[((size_t)u * a.vrows + r0 + rr) * kD + 4 * d4]) = wv;
       }
     }
-  }
-  __syncthreads();
-  // column words: task (row r, channels 4 d4 .. 4 d4 + 3), one dword of four
-  // byte codes per slot
-  const int r0 = s0 / NV;
-  for (int task = tid; task < ROWS * (kD / 4); task += kQThreads) {
-    const int r = task / (kD / 4), d4 = task % (kD / 4);
-    if (r0 + r >= a.vrows) continue;
-    float lo[4] = {0.f, 0.f, 0.f, 0.f}, hi[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int jj = NV - 1; jj >= 0; --jj) {
-      const uint32_t c4 = vcodes[r * NV + jj][d4];
-      const float c[4] = {(float)(c4 & 0xFFu), (float)((c4 >> 8) & 0xFFu), (float)((c4 >> 16) & 0xFFu),
-                          (float)(c4 >> 24)};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (jj >= LO) hi[e] = __builtin_fmaf(hi[e], (float)L, c[e]);
-        else lo[e] = __builtin_fmaf(lo[e], (float)L, c[e]);
-      }
-    }
-    uint4 wv;
-    wv.x = __umul24((uint32_t)hi[0], P::LPOW_LO) + (uint32_t)lo[0];
-    wv.y = __umul24((uint32_t)hi[1], P::LPOW_LO) + (uint32_t)lo[1];
-    wv.z = __umul24((uint32_t)hi[2], P::LPOW_LO) + (uint32_t)lo[2];
-    wv.w = __umul24((uint32_t)hi[3], P::LPOW_LO) + (uint32_t)lo[3];
-    *reinterpret_cast<uint4*>(&a.vwords[((size_t)u * a.vrows + r0 + r) * kD + 4 * d4]) = wv;
+    __syncthreads();
   }
 }
 
