@@ -117,81 +117,160 @@ __global__ __launch_bounds__(kQThreads) void k_quant_pool(QuantArgs a) {
 // ---- row kernel: sixteen lanes per slot row (fast path, L <= 8) ----
 //
 // Lane l of a 16-lane row group holds channels 8l..8l+7 of one slot row, so
-// each row is read as one contiguous 256-byte piece.  Thread (row group rg,
-// lane l) handles rows rg, rg + 16, ... of the workgroup's slots.  A group's
-// min/max combines the lanes of the group with lane shuffles (IEEE min/max
-// do not order -0 and +0; if any extreme is a zero, the wave redoes the
-// reduction in the total order); each lane then forms its group's fp16
-// scale and zero and codes its eight values with the exact quotient of
-// group_setup.  Codes go to LDS as bytes; key row words (along head_dim) and
-// value column words (along slots) are packed from there in fp32 Horner
-// halves (exact below 2^24) joined by one 24-bit integer multiply-add.
+// Four lanes (a quad) per slot row: load i of lane q reads channels
+// 32 i + 8 q .. 32 i + 8 q + 7, so each load instruction covers 64
+// contiguous bytes of sixteen rows and a group of G channels is chunks
+// i in [G/32 g, G/32 (g + 1)) of all four lanes.  Group extremes use the
+// IEEE-2019 minimum/maximum (-0 below +0) on packed fp16, with the maximum
+// carried negated so that one packed minimum reduces both over the quad
+// (DPP lane permutes).  Lane q then forms the fp16 scale/zero of one group
+// (with the exact quotient of group_setup) and the quad shares them.  Codes
+// go to LDS as bytes; key row words (along head_dim) and value column words
+// (along slots) are packed from there in fp32 Horner halves (exact below
+// 2^24) joined by one 24-bit integer multiply-add.
 template <int L>
 struct RowPack {
   static constexpr int NV = cpw(L);
   static constexpr int KW = (kD + NV - 1) / NV;
-  static constexpr int LO = NV / 2;               // low digits per word (L^LO < 2^24)
-  static constexpr uint32_t LPOW_LO = ipow(L, LO);
   static constexpr int ROWS = NV >= 256 ? 1 : 256 / NV;   // value word rows per workgroup
   static constexpr int SL = ROWS * NV;                    // slots per workgroup (<= 256)
+  // Horner over chunks of CS digits: a chunk is one 4-byte dot product with
+  // byte weights L^0 .. L^(CS-1) (each below 256)
+  static constexpr int CS = ipow(L, 3) <= 255u ? 4 : 3;
+  static constexpr int NCH = (NV + CS - 1) / CS;
+  static constexpr uint32_t LCS = ipow(L, CS);
+  // byte weights of a chunk whose first n digits count
+  static constexpr uint32_t weights(int n) {
+    uint32_t w = 0;
+    for (int k = 0; k < CS && k < n; ++k) w |= ipow(L, k) << (8 * k);
+    return w;
+  }
+  // acc * L^CS + p, exact: 24-bit multiply while the accumulator stays below
+  // 2^24 (L^(digits above this chunk) bounds it)
+  __device__ static inline uint32_t horner(uint32_t acc, uint32_t p, int above) {
+    return ipow(L, above) <= (1u << 24) ? __umul24(acc, LCS) + p : acc * LCS + p;
+  }
+  // key word w of a code row (bytes = channels; entries past head_dim count 0)
+  __device__ static inline uint32_t key_word(const uint32_t* row, int w) {
+    uint32_t acc = 0;
+#pragma unroll
+    for (int k = NCH - 1; k >= 0; --k) {
+      const int d0 = w * NV + CS * k;                     // first channel of the chunk
+      const int n = min(min(CS, NV - CS * k), kD - d0);   // digits that count
+      uint32_t p = 0;
+      if (n > 0) {
+        const int o = d0 >> 2, sh = d0 & 3;
+        const uint32_t bytes = sh == 0 ? row[o] : __builtin_amdgcn_alignbyte(row[o + 1], row[o], sh);
+        p = __builtin_amdgcn_udot4(bytes, weights(n), 0u, false);
+      }
+      acc = k == NCH - 1 ? p : horner(acc, p, NV - CS * (k + 1));
+    }
+    return acc;
+  }
+  // four value column words from NV code dwords (dword jj = slot jj of the
+  // word row, byte c = channel c): 4x4 byte transposes feed the dot products
+  __device__ static inline uint4 value_words(const uint32_t* col) {
+    uint32_t acc[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = NCH - 1; k >= 0; --k) {
+      const int j0 = CS * k, n = min(CS, NV - j0);
+      const uint32_t d0 = col[j0], d1 = n > 1 ? col[j0 + 1] : 0u;
+      const uint32_t d2 = n > 2 ? col[j0 + 2] : 0u, d3 = n > 3 ? col[j0 + 3] : 0u;
+      const uint32_t lo01 = __builtin_amdgcn_perm(d1, d0, 0x05010400u);
+      const uint32_t hi01 = __builtin_amdgcn_perm(d1, d0, 0x07030602u);
+      const uint32_t lo23 = __builtin_amdgcn_perm(d3, d2, 0x05010400u);
+      const uint32_t hi23 = __builtin_amdgcn_perm(d3, d2, 0x07030602u);
+      const uint32_t t[4] = {__builtin_amdgcn_perm(lo23, lo01, 0x05040100u),
+                             __builtin_amdgcn_perm(lo23, lo01, 0x07060302u),
+                             __builtin_amdgcn_perm(hi23, hi01, 0x05040100u),
+                             __builtin_amdgcn_perm(hi23, hi01, 0x07060302u)};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t p = __builtin_amdgcn_udot4(t[c], weights(n), 0u, false);
+        acc[c] = k == NCH - 1 ? p : horner(acc[c], p, NV - CS * (k + 1));
+      }
+    }
+    return make_uint4(acc[0], acc[1], acc[2], acc[3]);
+  }
 };
 
+__device__ inline h2v hb(uint32_t x) { return h2_from_bits(x); }
+__device__ inline uint32_t bh(h2v x) { return __builtin_bit_cast(uint32_t, x); }
+// packed fp16 IEEE-2019 minimum / maximum
+__device__ inline uint32_t hmin(uint32_t x, uint32_t y) { return bh(__builtin_elementwise_minimum(hb(x), hb(y))); }
+__device__ inline uint32_t hmax(uint32_t x, uint32_t y) { return bh(__builtin_elementwise_maximum(hb(x), hb(y))); }
+// value of lane (quad base + pattern) via a DPP quad permute
+template <int CTRL>
+__device__ inline uint32_t quad_perm(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E;    // quad_perm [1,0,3,2], [2,3,0,1]
+template <int O>
+__device__ inline uint32_t quad_bcast(uint32_t v) { return quad_perm<O * 0x55>(v); }
+
 // q = RN(fl32(x - z) / s) by the quotient correction of group_setup (s == 0
-// gives r = 0 and q = 0).  `one` is 1.0 hidden from the optimizer so that
-// x * one - z stays a single mixed-precision fma on the fp16 input.
-__device__ inline float quotient_of(_Float16 x, const GroupQ& g, float one) {
-  const float a = __builtin_fmaf((float)x, one, -g.z);    // fl32(x - z), one rounding
-  const float q0 = a * g.r;
-  const float rho = __builtin_fmaf(-q0, g.s, a);
-  return __builtin_fmaf(rho, g.r, q0);
+// gives r = 0 and q = 0); z and s are the fp16 halves of the meta word.
+// `one` is 1.0 hidden from the optimizer so that x * one - z stays a single
+// mixed-precision fma on the fp16 input.
+__device__ inline float quotient_of(_Float16 x, _Float16 z, _Float16 s, float r, float one) {
+  const float a = __builtin_fmaf((float)x, one, -(float)z);    // fl32(x - z), one rounding
+  const float q0 = a * r;
+  const float rho = __builtin_fmaf(-q0, (float)s, a);
+  return __builtin_fmaf(rho, r, q0);
 }
 
-// Two fp16 bit patterns per word mapped to 16-bit keys whose unsigned order
-// is the IEEE total order (-0 below +0): positive values get the sign bit
-// set, negative ones are complemented.
-__device__ inline uint32_t f16x2_order_key(uint32_t b) {
-  const uint32_t neg = (b >> 15) & 0x00010001u;
-  return b ^ 0x80008000u ^ (neg * 0x7FFFu);
-}
-__device__ inline uint32_t f16_from_key16(uint32_t k) {
-  return (k & 0x8000u) ? (k ^ 0x8000u) : (~k & 0xFFFFu);
+// (min, -max) of the 8 CPG fp16 values of a lane's chunks of one group
+template <int CPG>
+__device__ inline uint32_t chunk_extremes(const uint4* x) {
+  uint32_t lo = x[0].x, hi = x[0].x;
+#pragma unroll
+  for (int c = 0; c < CPG; ++c) {
+    const uint32_t w[4] = {x[c].x, x[c].y, x[c].z, x[c].w};
+#pragma unroll
+    for (int j = (c == 0 ? 1 : 0); j < 4; ++j) {
+      lo = hmin(lo, w[j]);
+      hi = hmax(hi, w[j]);
+    }
+  }
+  // halves side by side: (lo.lo, -hi.lo) and (lo.hi, -hi.hi)
+  const uint32_t e0 = __builtin_amdgcn_perm(hi, lo, 0x05040100u) ^ 0x80000000u;
+  const uint32_t e1 = __builtin_amdgcn_perm(hi, lo, 0x07060302u) ^ 0x80000000u;
+  return hmin(e0, e1);
 }
 
-// Group extremes (fp16 bits, IEEE total order) of eight values per lane over
-// the G/8 lanes of the group (aligned lane blocks of a 16-lane row).  The
-// reduction runs on integer keys in plain 32-bit registers.
-template <int G>
-__device__ inline void row_group_minmax(uint4 x, uint32_t& mn, uint32_t& mx) {
-  const uint32_t k[4] = {f16x2_order_key(x.x), f16x2_order_key(x.y), f16x2_order_key(x.z),
-                         f16x2_order_key(x.w)};
-  uint32_t lo = 0xFFFFu, hi = 0u;
+// codes of the 8 values of one chunk (fp16 bits in x) into two byte words;
+// CLAMP bounds the quotient by the top level (needed only for subnormal
+// scales, where s can be far below range / (L - 1))
+template <int L, bool CLAMP>
+__device__ inline void chunk_codes(uint4 x, uint32_t meta, float r, float one, uint32_t& c0, uint32_t& c1) {
+  const h2v zs = hb(meta);                    // (s, z)
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  uint32_t c[2] = {0u, 0u};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    lo = min(lo, min(k[i] & 0xFFFFu, k[i] >> 16));
-    hi = max(hi, max(k[i] & 0xFFFFu, k[i] >> 16));
+  for (int e = 0; e < 8; ++e) {
+    float q = quotient_of(hb(w[e / 2])[e & 1], zs[1], zs[0], r, one);
+    if (CLAMP) q = fminf(q, (float)(L - 1));
+    c[e / 4] = __builtin_amdgcn_cvt_pk_u8_f32(q, e & 3, c[e / 4]);
   }
-#pragma unroll
-  for (int o = 1; o < G / 8; o <<= 1) {
-    const uint32_t f = (uint32_t)__shfl_xor((int)(lo | (hi << 16)), o, 16);
-    lo = min(lo, f & 0xFFFFu);
-    hi = max(hi, f >> 16);
-  }
-  mn = f16_from_key16(lo);
-  mx = f16_from_key16(hi);
+  c0 = c[0];
+  c1 = c[1];
 }
 
 template <int L, int G>
 __global__ __launch_bounds__(kQThreads) void k_quant_rows(QuantArgs a) {
   using P = RowPack<L>;
-  constexpr int NV = P::NV, KW = P::KW, LO = P::LO, NG = kD / G, SL = P::SL, ROWS = P::ROWS;
-  constexpr int RPT = (SL + 15) / 16;              // rows per thread
+  constexpr int NV = P::NV, KW = P::KW, NG = kD / G, SL = P::SL, ROWS = P::ROWS;
+  constexpr int CPG = G / 32;                      // chunks per group per lane
+  constexpr int LPG = 4 / NG;                      // lanes of a quad per owned group
+  constexpr int NP = (SL + 63) / 64;               // rows per thread
   constexpr int CW = kD / 4 + 1;                   // dwords per code row (+1: bank spread)
+  static_assert(NG >= 1 && NG <= 4, "group of 32, 64 or 128 channels");
   __shared__ uint32_t codes[SL][CW];               // byte codes, [slot][channel]
   __shared__ int tok[256];
   const int tid = threadIdx.x, u = blockIdx.y;
   const int b = u / a.Hkv, h = u % a.Hkv;
   const int s0 = blockIdx.x * SL;
-  const int l16 = tid & 15, rg = tid >> 4;
+  const int q = tid & 3, rp = tid >> 2;            // lane in quad, row of the pass
   {
     const int s = s0 + tid;
     tok[tid] = (tid < SL && s < a.n) ? (a.inv ? a.inv[(size_t)b * a.inv_cap + s] : s) : -1;
@@ -200,61 +279,81 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows(QuantArgs a) {
   float one = 1.0f;
   asm volatile("" : "+v"(one));
   const int tiled = a.tiles * kTile;
+  const int gown = q / LPG;                        // the group whose scale this lane forms
   for (int kv = a.kwords ? 0 : 1; kv < 2; ++kv) {
-    const uint16_t* base = (kv ? a.v : a.k) + b * a.sb + h * a.sh + 8 * l16;
-    uint4 x[RPT];
+    const uint16_t* base = (kv ? a.v : a.k) + b * a.sb + h * a.sh + 8 * q;
+    uint4 x[NP][4];
 #pragma unroll
-    for (int k = 0; k < RPT; ++k) {
-      const int r = rg + 16 * k;
-      const int t = r < SL ? tok[r] : -1;
-      x[k] = t >= 0 ? *reinterpret_cast<const uint4*>(base + (int64_t)t * a.st) : make_uint4(0u, 0u, 0u, 0u);
+    for (int p = 0; p < NP; ++p) {
+      const int t = tok[rp + 64 * p];              // -1: no token (values 0, codes 0)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        x[p][i] = t >= 0 ? *reinterpret_cast<const uint4*>(base + (int64_t)t * a.st + 32 * i)
+                         : make_uint4(0u, 0u, 0u, 0u);
     }
     uint32_t* mp = kv ? a.vmeta : a.kmeta;
 #pragma unroll
-    for (int k = 0; k < RPT; ++k) {
-      const int r = rg + 16 * k;                   // uniform over the 16 lanes of the row
-      if (r >= SL) continue;
-      const int s = s0 + r;
-      const bool valid = tok[r] >= 0;
-      uint32_t mn, mx;
-      row_group_minmax<G>(x[k], mn, mx);
+    for (int p = 0; p < NP; ++p) {
+      const int r = rp + 64 * p;
+      // group extremes over the quad, then lane q keeps group gown
+      uint32_t e[NG];
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        uint32_t v = chunk_extremes<CPG>(&x[p][g * CPG]);
+        v = hmin(v, quad_perm<kQuadXor1>(v));
+        e[g] = hmin(v, quad_perm<kQuadXor2>(v));
+      }
+      uint32_t eo = e[0];
+#pragma unroll
+      for (int g = 1; g < NG; ++g) eo = gown == g ? e[g] : eo;
+      const uint32_t mn = eo & 0xFFFFu, mx = (eo >> 16) ^ 0x8000u;
       GroupQ gq = group_setup(mn, mx, L);
       if (gq.s == 0.0f) gq.r = 0.0f;               // all codes 0
-      // codes as bytes: the packed u8 conversion rounds to nearest even
-      const uint32_t w4[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
-      uint32_t c[2] = {0u, 0u};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const h2v pr = h2_from_bits(w4[e / 2]);
-        const float q = fminf(quotient_of(pr[e & 1], gq, one), (float)(L - 1));
-        c[e / 4] = __builtin_amdgcn_cvt_pk_u8_f32(q, e & 3, c[e / 4]);
+      const uint32_t meta = gq.s_bits | (mn << 16);
+      const bool sub = (gq.s_bits & 0x7C00u) == 0u;    // zero or subnormal scale
+      if (r < SL && (q % LPG) == 0) {
+        const int s = s0 + r;
+        if (s < tiled) mp[(((size_t)u * a.tiles + s / kTile) * NG + gown) * kTile + (s % kTile)] = meta;
       }
-      codes[r][2 * l16] = valid ? c[0] : 0u;
-      codes[r][2 * l16 + 1] = valid ? c[1] : 0u;
-      if ((l16 % (G / 8)) == 0 && s < tiled) {
-        const int g = l16 / (G / 8);
-        mp[(((size_t)u * a.tiles + s / kTile) * NG + g) * kTile + (s % kTile)] =
-            valid ? (gq.s_bits | (mn << 16)) : 0u;
+      // every group's (meta, r) from its owner lane
+      uint32_t gm[NG], gr[NG];
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        if (NG == 1) { gm[g] = meta; gr[g] = __float_as_uint(gq.r); continue; }
+        if (g * LPG == 0) { gm[g] = quad_bcast<0>(meta); gr[g] = quad_bcast<0>(__float_as_uint(gq.r)); }
+        else if (g * LPG == 1) { gm[g] = quad_bcast<1>(meta); gr[g] = quad_bcast<1>(__float_as_uint(gq.r)); }
+        else if (g * LPG == 2) { gm[g] = quad_bcast<2>(meta); gr[g] = quad_bcast<2>(__float_as_uint(gq.r)); }
+        else { gm[g] = quad_bcast<3>(meta); gr[g] = quad_bcast<3>(__float_as_uint(gq.r)); }
+      }
+      uint32_t c[4][2];
+      if (__builtin_expect(__ballot(sub && gq.s != 0.0f) != 0ull, 0)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          chunk_codes<L, true>(x[p][i], gm[i / CPG], __uint_as_float(gr[i / CPG]), one, c[i][0], c[i][1]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          chunk_codes<L, false>(x[p][i], gm[i / CPG], __uint_as_float(gr[i / CPG]), one, c[i][0], c[i][1]);
+      }
+      if (r < SL) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          codes[r][8 * i + 2 * q] = c[i][0];
+          codes[r][8 * i + 2 * q + 1] = c[i][1];
+        }
       }
     }
     __syncthreads();
     if (kv == 0) {
-      // key row words: task (word w, slot r), slots fastest
-      for (int task = tid; task < KW * SL; task += kQThreads) {
-        const int w = task / SL, r = task % SL, s = s0 + r;
-        if (s >= tiled) continue;
-        const uint8_t* cb = reinterpret_cast<const uint8_t*>(&codes[r][0]);
-        float lo = 0.f, hi = 0.f;
+      // key row words: one slot per thread, its code row read once
+      if (tid < SL && s0 + tid < tiled) {
+        const int s = s0 + tid;
+        uint32_t row[CW];
 #pragma unroll
-        for (int jj = NV - 1; jj >= 0; --jj) {
-          const int d = w * NV + jj;
-          if (d >= kD) continue;
-          const float cf = (float)cb[d];
-          if (jj >= LO) hi = __builtin_fmaf(hi, (float)L, cf);
-          else lo = __builtin_fmaf(lo, (float)L, cf);
-        }
-        a.kwords[(((size_t)u * a.tiles + s / kTile) * KW + w) * kTile + (s % kTile)] =
-            __umul24((uint32_t)hi, P::LPOW_LO) + (uint32_t)lo;
+        for (int j = 0; j < CW; ++j) row[j] = codes[tid][j];
+        uint32_t* dst = a.kwords + (((size_t)u * a.tiles + s / kTile) * KW) * kTile + (s % kTile);
+#pragma unroll
+        for (int w = 0; w < KW; ++w) dst[w * kTile] = P::key_word(row, w);
       }
     } else {
       // value column words: task (word row rr, channels 4 d4 .. 4 d4 + 3)
@@ -262,24 +361,11 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows(QuantArgs a) {
       for (int task = tid; task < ROWS * (kD / 4); task += kQThreads) {
         const int rr = task / (kD / 4), d4 = task % (kD / 4);
         if (r0 + rr >= a.vrows) continue;
-        float lo[4] = {0.f, 0.f, 0.f, 0.f}, hi[4] = {0.f, 0.f, 0.f, 0.f};
+        uint32_t col[NV];
 #pragma unroll
-        for (int jj = NV - 1; jj >= 0; --jj) {
-          const uint32_t c4 = codes[rr * NV + jj][d4];
-          const float cf[4] = {(float)(c4 & 0xFFu), (float)((c4 >> 8) & 0xFFu),
-                               (float)((c4 >> 16) & 0xFFu), (float)(c4 >> 24)};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (jj >= LO) hi[e] = __builtin_fmaf(hi[e], (float)L, cf[e]);
-            else lo[e] = __builtin_fmaf(lo[e], (float)L, cf[e]);
-          }
-        }
-        uint4 wv;
-        wv.x = __umul24((uint32_t)hi[0], P::LPOW_LO) + (uint32_t)lo[0];
-        wv.y = __umul24((uint32_t)hi[1], P::LPOW_LO) + (uint32_t)lo[1];
-        wv.z = __umul24((uint32_t)hi[2], P::LPOW_LO) + (uint32_t)lo[2];
-        wv.w = __umul24((uint32_t)hi[3], P::LPOW_LO) + (uint32_t)lo[3];
-        *reinterpret_cast<uint4*>(&a.vwords[((size_t)u * a.vrows + r0 + rr) * kD + 4 * d4]) = wv;
+        for (int jj = 0; jj < NV; ++jj) col[jj] = codes[rr * NV + jj][d4];
+        *reinterpret_cast<uint4*>(&a.vwords[((size_t)u * a.vrows + r0 + rr) * kD + 4 * d4]) =
+            P::value_words(col);
       }
     }
     __syncthreads();

@@ -60,6 +60,19 @@ def test_tiered_quantize_and_decode(w):
     _check_tiered(w, inp, run)
 
 
+@pytest.mark.parametrize("lh,ll,g", [(4, 3, 128), (7, 6, 64), (8, 7, 32), (5, 4, 64)])
+def test_tiered_level_pairs(lh, ll, g):
+    """Every grid size 3..8 and group size of the tiered path (codes per
+    word 20, 16, 13, 12, 11, 10), with decode over the result."""
+    w = C[1].shrink(name=f"levels_{lh}_{ll}_g{g}", batch=2, kv_heads=2, q_heads=8, tokens=1201,
+                    levels_hi=lh, levels_lo=ll, group=g)
+    log(f"case {w.name}")
+    inp = synth.make_inputs(w)
+    run = GpuRun(w, inp)
+    run.quantize()
+    _check_tiered(w, inp, run)
+
+
 @pytest.mark.parametrize("T,n_hi", [(1, 0), (1, 1), (17, 0), (17, 17), (193, 96), (640, 320)])
 def test_tiered_edge_sizes(T, n_hi):
     w = C[1].shrink(name=f"edge_T{T}_n{n_hi}", batch=2, kv_heads=1, q_heads=4, tokens=T,
@@ -86,6 +99,12 @@ def test_tiered_ties_zeros_and_constant_groups():
     inp.k[1, 30, 1, :8] = np.float16(-0.0)
     inp.v[0, 40, 0, 3] = np.float16(-0.0)
     inp.v[0, 40, 0, 4] = np.float16(0.0)
+    # tiny ranges: subnormal fp16 scales far below range / (L - 1), so the
+    # quotient exceeds the top level and the code must be clamped
+    tiny = np.float16(2.0 ** -24)
+    inp.k[0, 50:60, 1, :32] = (np.arange(32) % 8).astype(np.float16) * tiny
+    inp.v[1, 61:70, 0, 64:96] = (np.arange(32) % 7).astype(np.float16) * tiny - np.float16(3e-7)
+    inp.k[1, 71:80, 0, 96:128] = np.linspace(-4e-7, 5e-7, 32).astype(np.float16)
     run = GpuRun(w, inp)
     run.quantize()
     _check_tiered(w, inp, run)
