@@ -29,7 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-DECODE_SOURCES = ("decode.hip", "decode_mfma.hip", "digits.h", "tiling.h", "common.h", "internal.h")
+DECODE_SOURCES = ("decode.hip", "decode_mfma.hip", "unpack.h", "digits.h", "tiling.h", "common.h", "internal.h")
 QUANTIZE_SOURCES = ("quantize.hip", "rank.hip", "digits.h", "tiling.h", "common.h", "internal.h")
 
 
