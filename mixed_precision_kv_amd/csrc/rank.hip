@@ -2,18 +2,19 @@
 // by a model-internal score; the top n_hi take the higher of two adjacent
 // grids; every token is kept).
 //
-// Rank = position in the stable descending order of the fp32 score.  It is
-// computed with a least-significant-digit radix sort (4 passes of 8 bits) of
-// the order-preserving u32 key, carrying the token index; each pass is
-// stable, so equal scores stay in token order.  One sort segment per
-// sequence, cut into blocks of kSortTile keys.  Per pass: per-(digit,
-// block) counts -> stable scatter, each block deriving its own output
-// offsets from the counts (wave ballots give each element its rank among
-// equal digits of its wave, LDS counters order the waves and the rounds).
-// The first pass's counts come from the kernel that forms the keys; the last
-// pass writes the ranks and the ascending score array instead of keys.
-// Slots (index among same-tier tokens in token order) come from one scan per
-// sequence.
+// Rank = position in the stable descending order of the fp32 score, i.e. the
+// ascending order of an order-preserving u32 key with ties in token order.
+// Sequences of up to kMergeMaxT tokens: each block of kSortTile tokens is
+// sorted in LDS (4 stable passes of 8 bits), then each sorted element's rank
+// is its position in its own block plus, for every other block, the number
+// of that block's keys that precede it (binary search over the sequence's
+// sorted keys, all held in one workgroup's LDS): keys that are smaller, and
+// equal keys of earlier blocks.  Longer sequences: a least-significant-digit
+// radix sort over the whole sequence (4 passes of 8 bits, per-(digit, block)
+// counts -> stable scatter, each block deriving its own output offsets from
+// the counts; wave ballots give each element its rank among equal digits of
+// its wave).  Slots (index among same-tier tokens in token order) come from
+// one scan per sequence.
 #include "common.h"
 #include "internal.h"
 
@@ -188,9 +189,10 @@ __global__ __launch_bounds__(256) void k_rank_scatter(ScatterArgs a) {
 }
 
 // Slot = index among same-tier tokens in token order.  Workgroup (seg, b)
-// owns tokens [seg * kSlotSeg, (seg + 1) * kSlotSeg); earlier segments'
-// high-tier counts give its base; wave w owns a contiguous quarter, read in
+// owns tokens [seg * SEG, (seg + 1) * SEG); earlier segments' high-tier
+// counts give its base; wave w owns a contiguous quarter, read in
 // 64-token chunks (coalesced) with ballots for the in-chunk prefix.
+template <int SEG>
 __global__ __launch_bounds__(256) void k_rank_slots(const int32_t* __restrict__ ranks,
                                                     const uint32_t* __restrict__ segcnt,
                                                     uint32_t* __restrict__ tokmap,
@@ -198,7 +200,7 @@ __global__ __launch_bounds__(256) void k_rank_slots(const int32_t* __restrict__ 
                                                     int32_t* __restrict__ inv_lo,
                                                     int32_t* __restrict__ counters, int T, int n_hi,
                                                     int cap, int cap_hi, int cap_lo, int nseg, int B) {
-  constexpr int kChunks = kSlotSeg / 4 / 64;          // 64-token chunks per wave
+  constexpr int kChunks = SEG / 4 / 64;               // 64-token chunks per wave
   __shared__ uint32_t wtot[4];
   __shared__ uint32_t segbase;
   const int tid = threadIdx.x;
@@ -216,7 +218,7 @@ __global__ __launch_bounds__(256) void k_rank_slots(const int32_t* __restrict__ 
       counters[b * 4 + 3] = 0;
     }
   }
-  const int t0 = seg * kSlotSeg + w * (kSlotSeg / 4);
+  const int t0 = seg * SEG + w * (SEG / 4);
   const int32_t* rb = ranks + (size_t)b * T;
   uint64_t m[kChunks];
   uint32_t mine = 0;
@@ -249,6 +251,207 @@ __global__ __launch_bounds__(256) void k_rank_slots(const int32_t* __restrict__ 
   }
 }
 
+// ---------------- sequences of up to kMergeMaxT tokens ----------------
+
+constexpr int kBlkSort = 4096;               // keys per block of the block sort
+constexpr int kBlkThreads = 1024;            // 16 waves x 4 chunks of 64
+
+// Stable sort of one block of kBlkSort keys in LDS, 4 passes of 8 bits.
+// Wave w owns elements [256 w, 256 w + 256) in 64-element chunks, in order;
+// an element goes to (keys with a smaller digit) + (same digit in earlier
+// waves) + (same digit earlier in its own wave, from the wave's running
+// counts).  Out of range elements carry the largest key and the largest
+// indices, so they sort last.  Also clears the block's high-tier counts.
+__global__ __launch_bounds__(kBlkThreads) void k_rank_block_sort(const float* __restrict__ scores,
+                                                                 uint32_t* __restrict__ skeys,
+                                                                 uint32_t* __restrict__ sidx,
+                                                                 uint32_t* __restrict__ hicnt, int T,
+                                                                 int ld, int nblk, int B) {
+  constexpr int NW = kBlkThreads / 64;
+  __shared__ uint32_t kb[kBlkSort];
+  __shared__ uint16_t ib[kBlkSort];
+  __shared__ uint32_t wrun[NW][256];         // per wave: running count of each digit
+  __shared__ uint32_t wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int b, blk;
+  if (!seq_block(nblk, B, b, blk)) return;
+  {
+    const int nseg = (T + kSortTile - 1) / kSortTile, seg = blk * (kBlkSort / kSortTile) + tid;
+    if (tid < kBlkSort / kSortTile && seg < nseg) hicnt[(size_t)b * nseg + seg] = 0u;
+  }
+  const int base = blk * kBlkSort, nb = min(kBlkSort, T - base);
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint32_t key[4], ix[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int e = 256 * w + 64 * c + lane;
+    key[c] = e < nb ? score_desc_key(scores[(size_t)b * T + base + e]) : 0xFFFFFFFFu;
+    ix[c] = (uint32_t)e;
+  }
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 8 * pass;
+    for (int i = tid; i < NW * 256; i += kBlkThreads) (&wrun[0][0])[i] = 0u;
+    __syncthreads();
+    uint32_t d[4], pin[4];                   // digit; rank among equal digits of the wave
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      d[c] = (key[c] >> shift) & 255u;
+      uint64_t peers = ~0ull;
+#pragma unroll
+      for (int bit = 0; bit < 8; ++bit) {
+        const bool on = (d[c] >> bit) & 1u;
+        const uint64_t bb = __ballot(on);
+        peers &= on ? bb : ~bb;
+      }
+      const uint64_t below = peers & lt_mask;
+      const uint32_t before = wrun[w][d[c]];   // this digit in earlier chunks of the wave
+      pin[c] = before + (uint32_t)__popcll(below);
+      if (below == 0ull) wrun[w][d[c]] = before + (uint32_t)__popcll(peers);
+    }
+    __syncthreads();
+    // threads 0..255 (digit tid): exclusive scan of the totals, per-wave bases
+    uint32_t tw[NW], tot = 0, inc = 0;
+    if (tid < 256) {
+#pragma unroll
+      for (int x = 0; x < NW; ++x) { tw[x] = wrun[x][tid]; tot += tw[x]; }
+      inc = tot;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_up((int)inc, o);
+        if (lane >= o) inc += y;
+      }
+      if (lane == 63) wsum[w] = inc;
+    }
+    __syncthreads();
+    if (tid < 256) {
+      uint32_t run = inc - tot;
+      for (int x = 0; x < w; ++x) run += wsum[x];
+#pragma unroll
+      for (int x = 0; x < NW; ++x) { wrun[x][tid] = run; run += tw[x]; }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t pos = wrun[w][d[c]] + pin[c];
+      kb[pos] = key[c];
+      ib[pos] = (uint16_t)ix[c];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int e = 256 * w + 64 * c + lane;
+      key[c] = kb[e];
+      ix[c] = ib[e];
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int e = 256 * w + 64 * c + lane;
+    if (e < nb) {
+      skeys[(size_t)b * ld + base + e] = key[c];
+      sidx[(size_t)b * ld + base + e] = (uint32_t)base + ix[c];
+    }
+  }
+}
+
+struct MergeArgs {
+  const uint32_t* skeys;        // sorted keys per block, [b][ld] (ld: T rounded up to 4)
+  const uint32_t* sidx;         // their token indices
+  const float* scores;
+  int32_t* ranks;
+  int32_t* ranks_out;
+  float* sorted_asc;
+  uint32_t* hicnt;              // high-tier tokens per kSortTile tokens, [b][ceil(T / kSortTile)]
+  int T, ld, nblk, n_hi, cap, B;
+};
+
+// LDS word of sorted key i: one pad word per 32 and per 1024 keys, so that
+// the probes of one binary-search step (indices that differ by multiples of
+// the step) fall in different banks.
+__device__ inline int sk_slot(int i) { return i + (i >> 5) + (i >> 10); }
+constexpr int kSkWords = kMergeMaxT + kMergeMaxT / 32 + kMergeMaxT / 1024;
+
+// Entries of the sorted block at `first` that precede key x: entries < xe
+// with xe = x + 1 when the block holds earlier tokens (equal keys count),
+// else xe = x.  Entries past the block's end hold the largest key, which
+// never counts.  Fixed trip count, no branches.
+__device__ inline int count_before(const uint32_t* sk, int first, uint32_t xe) {
+  const uint32_t* blk = sk + sk_slot(first);          // first: a multiple of 1024
+  int pos = 0;
+#pragma unroll
+  for (int step = kBlkSort / 2; step > 0; step >>= 1) {
+    const uint32_t y = blk[sk_slot(pos + step - 1)];
+    pos += y < xe ? step : 0;
+  }
+  return pos + (blk[sk_slot(pos)] < xe ? 1 : 0);
+}
+
+// Rank of 1024 sorted elements of one block (quarter q): the element's
+// position in its block plus the entries of every other block that precede
+// it.  One thread per element; the sequence's sorted keys sit in LDS.
+__global__ __launch_bounds__(1024) void k_rank_merge(MergeArgs a) {
+  __shared__ uint32_t sk[kSkWords];
+  __shared__ uint32_t whi[kBlkSort / kSortTile];
+  const int tid = threadIdx.x;
+  int b, bq;
+  if (!seq_block(a.nblk * 4, a.B, b, bq)) return;
+  const int blk = bq >> 2, p = (bq & 3) * 1024 + tid;   // sorted position in the block
+  {
+    // the sequence's sorted keys into LDS: 16-byte loads, all in flight
+    const uint32_t* src = a.skeys + (size_t)b * a.ld;
+    const int n4 = a.T >> 2;
+    const uint4* src4 = reinterpret_cast<const uint4*>(src);
+    uint4 v[kMergeMaxT / 4 / 1024];
+#pragma unroll
+    for (int k = 0; k < kMergeMaxT / 4 / 1024; ++k) {
+      const int i = tid + 1024 * k;
+      if (i < n4) v[k] = src4[i];
+    }
+#pragma unroll
+    for (int k = 0; k < kMergeMaxT / 4 / 1024; ++k) {
+      const int i = tid + 1024 * k;
+      if (i < n4) {
+        const int o = sk_slot(4 * i);        // 4 i .. 4 i + 3 share their pad count
+        sk[o] = v[k].x; sk[o + 1] = v[k].y; sk[o + 2] = v[k].z; sk[o + 3] = v[k].w;
+      }
+    }
+    if (tid < (a.T & 3)) sk[sk_slot(4 * n4 + tid)] = src[4 * n4 + tid];
+    for (int i = a.T + tid; i < a.nblk * kBlkSort; i += 1024) sk[sk_slot(i)] = 0xFFFFFFFFu;
+  }
+  __syncthreads();
+  const int base = blk * kBlkSort, nb = min(kBlkSort, a.T - base);
+  const bool valid = p < nb;
+  const uint32_t x = sk[sk_slot(base + (valid ? p : 0))];
+  int r = p;
+  constexpr int NI = kMergeMaxT / kBlkSort;            // blocks of the longest sequence
+  int c[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const bool use = i < a.nblk && i != blk;
+    const int n = use ? min(kBlkSort, a.T - i * kBlkSort) : 0;
+    // equal keys of earlier blocks count; x = 0xFFFFFFFF: every entry does
+    if (i < blk && x == 0xFFFFFFFFu) c[i] = use ? n : 0;
+    else c[i] = use ? count_before(sk, i * kBlkSort, i < blk ? x + 1u : x) : 0;
+  }
+#pragma unroll
+  for (int i = 0; i < NI; ++i) r += c[i];
+  if (tid < kBlkSort / kSortTile) whi[tid] = 0u;
+  __syncthreads();
+  if (valid) {
+    const uint32_t tok = a.sidx[(size_t)b * a.ld + base + p];
+    a.ranks[(size_t)b * a.T + tok] = r;
+    if (a.ranks_out) a.ranks_out[(size_t)b * a.T + tok] = r;
+    a.sorted_asc[(size_t)b * a.cap + (a.T - 1 - r)] = a.scores[(size_t)b * a.T + tok];
+    if (r < a.n_hi) atomicAdd(&whi[(tok - base) / kSortTile], 1u);
+  }
+  __syncthreads();
+  // high-tier tokens per kSortTile-token range of the block
+  const int nseg = (a.T + kSortTile - 1) / kSortTile, seg = base / kSortTile + tid;
+  if (tid < kBlkSort / kSortTile && seg < nseg && whi[tid])
+    atomicAdd(&a.hicnt[(size_t)b * nseg + seg], whi[tid]);
+}
+
 bool launch_rank_tiers(const kvq_layout* L, uint8_t* cache, const float* scores, int T, int n_hi,
                        int32_t* ranks_out, uint8_t* ws, const QuantWs& plan, void* stream) {
   hipStream_t s = (hipStream_t)stream;
@@ -263,6 +466,27 @@ bool launch_rank_tiers(const kvq_layout* L, uint8_t* cache, const float* scores,
   int32_t* inv_hi = (int32_t*)(ws + plan.inv[0]);
   int32_t* inv_lo = (int32_t*)(ws + plan.inv[1]);
   const dim3 gblk = seq_grid(nblk, B);
+  uint32_t* tokmap = (uint32_t*)(cache + L->tokmap);
+  int32_t* counters = (int32_t*)(cache + L->counters);
+  if (T <= kMergeMaxT) {
+    const int nb4 = ceil_div(T, kBlkSort);
+    const int ld = (T + 3) & ~3;             // 16-byte aligned rows of sorted keys
+    k_rank_block_sort<<<seq_grid(nb4, B), kBlkThreads, 0, s>>>(scores, keys[0], idx[0], segcnt, T, ld, nb4,
+                                                               B);
+    MergeArgs m;
+    m.skeys = keys[0];
+    m.sidx = idx[0];
+    m.scores = scores;
+    m.ranks = ranks;
+    m.ranks_out = ranks_out;
+    m.sorted_asc = (float*)(cache + L->sorted);
+    m.hicnt = segcnt;
+    m.T = T; m.ld = ld; m.nblk = nb4; m.n_hi = n_hi; m.cap = L->cfg.capacity; m.B = B;
+    k_rank_merge<<<seq_grid(4 * nb4, B), 1024, 0, s>>>(m);
+    k_rank_slots<kSortTile><<<gblk, 256, 0, s>>>(ranks, segcnt, tokmap, inv_hi, inv_lo, counters, T, n_hi,
+                                                 L->cfg.capacity, L->cap[0], L->cap[1], nblk, B);
+    return hipGetLastError() == hipSuccess;
+  }
   k_rank_keys<<<gblk, kSortThreads, 0, s>>>(scores, keys[0], hist, segcnt, T, nblk, nseg, B);
   int cur = 0;
   for (int pass = 0; pass < 4; ++pass) {
@@ -283,9 +507,9 @@ bool launch_rank_tiers(const kvq_layout* L, uint8_t* cache, const float* scores,
     k_rank_scatter<<<gblk, kSortThreads, 0, s>>>(a);
     cur ^= 1;
   }
-  k_rank_slots<<<seq_grid(nseg, B), 256, 0, s>>>(ranks, segcnt, (uint32_t*)(cache + L->tokmap),
-                                                 inv_hi, inv_lo, (int32_t*)(cache + L->counters), T,
-                                                 n_hi, L->cfg.capacity, L->cap[0], L->cap[1], nseg, B);
+  k_rank_slots<kSlotSeg><<<seq_grid(nseg, B), 256, 0, s>>>(ranks, segcnt, tokmap, inv_hi, inv_lo, counters,
+                                                          T, n_hi, L->cfg.capacity, L->cap[0], L->cap[1],
+                                                          nseg, B);
   return hipGetLastError() == hipSuccess;
 }
 
