@@ -52,6 +52,18 @@ def packed_decode_bytes(lay, counts):
     return total
 
 
+def kchan_decode_bytes(lay, T):
+    """Algorithmic bytes one per-channel-key decode reads: key words, key
+    (scale, zero) per (channel, block), sparse entries, value words and
+    (scale, zero), the fp16 window, the query and the output."""
+    c = lay.cfg
+    D, U = c.head_dim, c.batch * c.kv_heads
+    n_q = c.k_block * ((T - c.window) // c.k_block)
+    per_unit = (n_q * lay.kw[0] * 4 + (n_q // c.k_block) * D * 4 + n_q * c.sparse_per_vec * 4
+                + -(-n_q // lay.vnv) * D * 4 + n_q * (D // c.v_group) * 4 + (T - n_q) * D * 2 * 2)
+    return U * per_unit + 2 * c.batch * c.q_heads * D * 2
+
+
 def quantize_bytes(w, lay):
     """Algorithmic bytes of quantize: fp16 K and V and the scores read once;
     packed cache, token map, sorted scores and ranks written once."""
@@ -127,6 +139,109 @@ def cpu_baseline(w, inp, scale, max_units, workers):
 
 
 # ------------------------------------------------------------------- main ---
+def _timed(torch, stream, fn, iters):
+    """Median and spread (ms) of fn(i) over iters calls, HIP events on `stream`."""
+    import numpy as np
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for i in range(iters):
+        evs[i][0].record(stream)
+        fn(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in evs])
+    return float(np.median(t)), float(np.percentile(t, 10)), float(np.percentile(t, 90))
+
+
+def sweep_one(w, args, torch, np, kvq, synth, dev):
+    """Quantize and decode (and, for the append workload, append + decode per
+    generation step) of one workload, inputs resident in HBM."""
+    print(f"[sweep] {w.name}: generating inputs", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(w)
+    lay = kvq.layout_init(kvq.config_for(w))
+    stream = torch.cuda.current_stream()
+    k = torch.from_numpy(inp.k).to(dev)
+    v = torch.from_numpy(inp.v).to(dev)
+    scores = None if inp.scores is None else torch.from_numpy(inp.scores).to(dev)
+    q = torch.from_numpy(inp.q).to(dev)
+    out = torch.empty_like(q)
+    max_len = w.tokens + w.append_steps
+    wsq = torch.empty(max(1, kvq.workspace_bytes(lay, kvq.OP_QUANTIZE, w.tokens)), dtype=torch.uint8, device=dev)
+    wsd = torch.empty(max(1, kvq.workspace_bytes(lay, kvq.OP_DECODE, max_len)), dtype=torch.uint8, device=dev)
+    R = 1 if w.append_steps else max(1, math.ceil(1.0e9 / lay.total_bytes))
+    caches = [torch.zeros(lay.total_bytes, dtype=torch.uint8, device=dev) for _ in range(R)]
+    scale = 1.0 / math.sqrt(w.head_dim)
+    tiered = w.mode == synth.TIERED
+
+    def quantize(i):
+        kvq.quantize(lay, caches[i % R], k, v, scores, w.tokens, w.n_hi if tiered else 0, None, wsq,
+                     stream=stream)
+
+    def decode(i, c=None):
+        kvq.decode_attn(lay, caches[i % R] if c is None else c, q, scale, max_len, out, wsd, stream=stream)
+
+    for i in range(R):
+        quantize(i)
+    torch.cuda.synchronize()
+    q_ms = _timed(torch, stream, quantize, 10)
+    rd = 2 * w.batch * w.tokens * w.kv_heads * w.head_dim * 2
+    if tiered:
+        counts = [[w.n_hi, w.tokens - w.n_hi]] * w.batch
+        dec_bytes = packed_decode_bytes(lay, counts)
+        q_bytes = quantize_bytes(w, lay)
+    else:
+        dec_bytes = kchan_decode_bytes(lay, w.tokens)
+        q_bytes = rd + dec_bytes - 2 * w.batch * w.q_heads * w.head_dim * 2
+    for i in range(R):
+        quantize(i)
+    for i in range(3):
+        decode(i)
+    d_ms = _timed(torch, stream, decode, 30)
+    res = {"workload": w.name, "config": {"batch": w.batch, "kv_heads": w.kv_heads, "q_heads": w.q_heads,
+                                           "context": w.tokens, "mode": w.mode},
+           "quantize": {"ms": q_ms[0], "ms_p10": q_ms[1], "ms_p90": q_ms[2], "bytes": q_bytes,
+                        "gbs": round(q_bytes / (q_ms[0] * 1e-3) / 1e9, 1),
+                        "frac_hbm": round(q_bytes / (q_ms[0] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+           "decode": {"ms": d_ms[0], "ms_p10": d_ms[1], "ms_p90": d_ms[2], "bytes": dec_bytes,
+                      "gbs": round(dec_bytes / (d_ms[0] * 1e-3) / 1e9, 1),
+                      "frac_hbm": round(dec_bytes / (d_ms[0] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                      "ctx_tokens_per_s_per_qhead": w.batch * w.q_heads * w.tokens / (d_ms[0] * 1e-3),
+                      "replicas": R}}
+    if w.append_steps:
+        # generation: each step appends one token per sequence, then decodes
+        quantize(0)
+        torch.cuda.synchronize()
+        steps = [dict(k=torch.from_numpy(st["k_new"]).to(dev), v=torch.from_numpy(st["v_new"]).to(dev),
+                      s=torch.from_numpy(st["score_new"]).to(dev), q=torch.from_numpy(st["q"]).to(dev))
+                 for st in inp.steps]
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in steps]
+        for i, st in enumerate(steps):
+            ev[i][0].record(stream)
+            kvq.append(lay, caches[0], st["k"], st["v"], st["s"], stream=stream)
+            ev[i][1].record(stream)
+            kvq.decode_attn(lay, caches[0], st["q"], scale, max_len, out, wsd, stream=stream)
+            ev[i][2].record(stream)
+        torch.cuda.synchronize()
+        a_t = np.array([e[0].elapsed_time(e[1]) for e in ev])
+        dd_t = np.array([e[1].elapsed_time(e[2]) for e in ev])
+        raw = caches[0][lay.counters:lay.counters + w.batch * 16].cpu().numpy().tobytes()
+        cnt = np.frombuffer(raw, dtype=np.int32).reshape(w.batch, 4)
+        end_counts = [[int(cnt[b, 1]), int(cnt[b, 2])] for b in range(w.batch)]
+        start_bytes = dec_bytes
+        end_bytes = packed_decode_bytes(lay, end_counts)
+        mid_bytes = 0.5 * (start_bytes + end_bytes)
+        res["append"] = {"steps": len(steps), "append_ms": float(np.median(a_t)),
+                         "decode_ms": float(np.median(dd_t)),
+                         "step_ms": float(np.median(a_t + dd_t)),
+                         "decode_gbs": round(mid_bytes / (float(np.median(dd_t)) * 1e-3) / 1e9, 1),
+                         "decode_frac_hbm": round(mid_bytes / (float(np.median(dd_t)) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "final_length": int(cnt[0, 0])}
+    print(f"[sweep] {w.name}: quantize {q_ms[0] * 1e3:.1f} us, decode {d_ms[0] * 1e3:.1f} us",
+          file=sys.stderr, flush=True)
+    del caches, k, v
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -137,6 +252,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="decode cache replicas (0: auto, >= 1 GB)")
     ap.add_argument("--cpu-units", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time quantize / decode (and append) of every workload; one JSON line each")
     ap.add_argument("--only", choices=["all", "decode", "quantize", "copy"], default="all",
                     help="profiling aid: run just one kernel family (no JSON line)")
     args = ap.parse_args()
@@ -150,6 +267,10 @@ def main():
     from mixed_precision_kv_amd import kvq, synth
 
     dev = torch.device("cuda:0")
+    if args.sweep:
+        for cw in synth.CONFIGS:
+            print(json.dumps(sweep_one(cw, args, torch, np, kvq, synth, dev)), flush=True)
+        return
     w = synth.BY_NAME[args.config]
     assert w.mode == "tiered", "the step bench covers the tiered workloads"
     print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)

@@ -291,67 +291,73 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_kchan(DecodeArgs a) {
   finish_partial(part, sm, sl, accs);
 }
 
-// Log-sum-exp merge of every chunk partial of one (unit, head) -> fp16 output.
-// Thread (slice sl, quad q) owns chunks c = sl, sl + 8, ... and channels
-// 4q..4q+3; it issues all its loads (running max m_c, sum l_c, four acc
-// values, 16-byte aligned: 132 floats per head) before using any, so one
-// memory round trip serves a batch of up to kMergeBatch chunks.  The largest
-// m_c (M) is found across slices through LDS, then each thread weights its
-// chunks by 2^(m_c - M) and the slices are summed.
-constexpr int kMergeThreads = 256;
-constexpr int kMergeSlices = kMergeThreads / 32;
+// Log-sum-exp merge of every chunk partial of one (unit, head) -> fp16 output,
+// in one pass.  Thread (slice sl, quad q) owns chunks c = sl, sl + S, ... and
+// channels 4q..4q+3; it issues the loads of a batch of kMergeBatch chunks
+// (running max m_c, sum l_c, four acc values, 16-byte aligned: 132 floats
+// per head) before using any, so one memory round trip serves the batch, and
+// keeps its own running max, rescaling what it has summed when the max
+// grows.  The slices are then combined through LDS against the largest max.
 constexpr int kMergeBatch = 8;                // chunks per thread per round trip
-__global__ __launch_bounds__(kMergeThreads) void k_merge(const float* __restrict__ part,
-                                                         uint16_t* __restrict__ out, int nch_total,
-                                                         int Hkv) {
-  __shared__ float smax[kMergeSlices];
-  __shared__ float4 racc[kMergeSlices][32];
-  __shared__ float rl[kMergeSlices];
+
+template <int THREADS>
+__global__ __launch_bounds__(THREADS) void k_merge(const float* __restrict__ part,
+                                                   uint16_t* __restrict__ out, int nch_total,
+                                                   int Hkv) {
+  constexpr int S = THREADS / 32;             // slices
+  __shared__ float smax[S];
+  __shared__ float4 racc[S][32];
+  __shared__ float rl[S];
   const int u = blockIdx.x, hh = blockIdx.y, t = threadIdx.x;
   const int b = u / Hkv, hk = u % Hkv;
   const float* pu = part + (size_t)u * nch_total * kGqa * kPartStride + hh * kPartStride;
   const size_t cs = (size_t)kGqa * kPartStride;
   const int q = t & 31, sl = t >> 5;
-  // pass 1: the largest running max over all chunks
-  float M = -INFINITY;
-  for (int c = sl; c < nch_total; c += kMergeSlices) M = fmaxf(M, pu[c * cs]);
-  if (q == 0) smax[sl] = M;
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < kMergeSlices; ++k) M = fmaxf(M, smax[k]);
-  // pass 2: weighted sums, kMergeBatch chunks per round trip
+  float M = -INFINITY, lsum = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  float lsum = 0.f;
-  for (int c0 = sl; c0 < nch_total; c0 += kMergeSlices * kMergeBatch) {
+  for (int c0 = sl; c0 < nch_total; c0 += S * kMergeBatch) {
     float mv[kMergeBatch], lv[kMergeBatch];
     float4 av[kMergeBatch];
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) {
-      const int c = c0 + k * kMergeSlices;
+      const int c = c0 + k * S;
       const bool ok = c < nch_total;
       const float* pc = pu + (size_t)(ok ? c : 0) * cs;
       mv[k] = ok ? pc[0] : -INFINITY;
       lv[k] = pc[1];
       av[k] = *reinterpret_cast<const float4*>(pc + 4 + 4 * q);
     }
+    float mb = M;
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) mb = fmaxf(mb, mv[k]);
+    const float f = (M == -INFINITY) ? 0.f : exp2f(M - mb);   // rescale of what is summed so far
+    lsum *= f;
+    o.x *= f; o.y *= f; o.z *= f; o.w *= f;
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) {
-      const float w = (mv[k] == -INFINITY) ? 0.f : exp2f(mv[k] - M);
+      const float w = (mv[k] == -INFINITY) ? 0.f : exp2f(mv[k] - mb);
       lsum = __builtin_fmaf(lv[k], w, lsum);
       o.x = __builtin_fmaf(av[k].x, w, o.x);
       o.y = __builtin_fmaf(av[k].y, w, o.y);
       o.z = __builtin_fmaf(av[k].z, w, o.z);
       o.w = __builtin_fmaf(av[k].w, w, o.w);
     }
+    M = mb;
   }
-  racc[sl][q] = o;
-  if (q == 0) rl[sl] = lsum;
+  if (q == 0) smax[sl] = M;
+  __syncthreads();
+  float Mg = smax[0];
+#pragma unroll
+  for (int k = 1; k < S; ++k) Mg = fmaxf(Mg, smax[k]);
+  const float f = (M == -INFINITY) ? 0.f : exp2f(M - Mg);
+  racc[sl][q] = make_float4(o.x * f, o.y * f, o.z * f, o.w * f);
+  if (q == 0) rl[sl] = lsum * f;
   __syncthreads();
   if (t < 32) {
     float4 r = racc[0][t];
     float l = rl[0];
 #pragma unroll
-    for (int k = 1; k < kMergeSlices; ++k) {
+    for (int k = 1; k < S; ++k) {
       const float4 x = racc[k][t];
       r.x += x.x; r.y += x.y; r.z += x.z; r.w += x.w;
       l += rl[k];
@@ -362,6 +368,12 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(const float* __restrict
     po[2] = f2h_rne(r.z / l);
     po[3] = f2h_rne(r.w / l);
   }
+}
+
+// 8 slices for few chunks per unit, 32 for many (long contexts over few units)
+static void launch_merge(const float* part, uint16_t* out, int U, int nch, int Hkv, hipStream_t s) {
+  if (nch <= 8 * kMergeBatch) k_merge<256><<<dim3(U, kGqa), 256, 0, s>>>(part, out, nch, Hkv);
+  else k_merge<1024><<<dim3(U, kGqa), 1024, 0, s>>>(part, out, nch, Hkv);
 }
 
 bool launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, float scale,
@@ -409,7 +421,7 @@ bool launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, flo
       pa.c = a.scale_log2;
       if (nchp[p] > 0 && !launch_decode_pool(lv[p], pa, c.group, nchp[p], U, stream)) return false;
     }
-    k_merge<<<dim3(U, kGqa), kMergeThreads, 0, s>>>((const float*)ws, (uint16_t*)out, nch_used, c.kv_heads);
+    launch_merge((const float*)ws, (uint16_t*)out, U, nch_used, c.kv_heads, s);
     return hipGetLastError() == hipSuccess;
   } else {
     a.kwords[0] = (const uint32_t*)(cache + L->k_words[0]);
@@ -429,7 +441,7 @@ bool launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, flo
     const int gx = nch0 > 1 ? nch0 : 1;
     k_decode_kchan<<<dim3(gx, U, 2), kDecThreads, 0, s>>>(a);
   }
-  k_merge<<<dim3(U, kGqa), kMergeThreads, 0, s>>>((const float*)ws, (uint16_t*)out, nch, c.kv_heads);
+  launch_merge((const float*)ws, (uint16_t*)out, U, nch, c.kv_heads, s);
   return hipGetLastError() == hipSuccess;
 }
 

@@ -178,7 +178,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       float sum = 0.f;
-      for (int d = 32 * j; d < 32 * j + 32; ++d) sum += qf[h][d];
+#pragma unroll
+      for (int d = 0; d < 32; ++d) sum += qf[h][32 * j + d];
       qc[h] = sum * a.c;
     }
     h8 aq[KM];

@@ -141,11 +141,17 @@ struct BitUnpack {
   static constexpr int NH8 = NOUT / 8;
   static constexpr int word_of(int t) { return D::word_of(t); }
   static constexpr int digit_of(int t) { return D::digit_of(t); }
+  // inverse of (word_of, digit_of): digits k and k + NV/2 of a word share a
+  // register, words are blocks of NV outputs
   static constexpr int pos_of(int word, int digit) {
-    for (int t = 0; t < NOUT; ++t)
-      if (D::word_of(t) == word && D::digit_of(t) == digit) return t;
-    return -1;
+    return word * NV + (digit < NV / 2 ? 2 * digit : 2 * (digit - NV / 2) + 1);
   }
+  static constexpr bool pos_ok() {
+    for (int t = 0; t < NV * NW; ++t)
+      if (pos_of(D::word_of(t), D::digit_of(t)) != t) return false;
+    return true;
+  }
+  static_assert(pos_ok(), "operand position map");
   __device__ static inline void fill(uint2*, int, int) {}
   __device__ static inline void run(const uint32_t (&w)[NW], const uint2*, h8 (&out)[NH8]) {
     _Float16 dg[NOUT];
