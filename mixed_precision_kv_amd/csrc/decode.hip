@@ -127,69 +127,6 @@ __device__ inline void load_q(const uint16_t* q, int b, int hk, int Hkv, float (
   }
 }
 
-__global__ __launch_bounds__(kDecThreads) void k_decode_tiered(DecodeArgs a) {
-  __shared__ float qf[kGqa][kD];
-  __shared__ float qsum[kGqa][4];
-  __shared__ float sc[kGqa][640];
-  __shared__ float red[kGqa * kD];
-  __shared__ float accs[kGqa * kD];
-  __shared__ float sm[kGqa], sl[kGqa];
-  const int tid = threadIdx.x;
-  const int c = blockIdx.x, u = blockIdx.y, p = blockIdx.z;
-  const int b = u / a.Hkv, hk = u % a.Hkv;
-  const int nchp = p ? (a.nch_total - a.nch0) : a.nch0;
-  if (c >= nchp) return;
-  float* part = a.part + ((size_t)u * a.nch_total + (p ? a.nch0 : 0) + c) * kGqa * kPartStride;
-  const int n = a.counters[b * 4 + 1 + p];
-  const int CH = a.chunk[p];
-  const int s_begin = c * CH, s_end = min(n, s_begin + CH);
-  if (s_begin >= s_end) { write_empty(part); return; }
-  const int L = a.L[p], nv = a.nv[p], kw = a.kw[p], tiles = a.tiles[p];
-  const int G = a.group, NG = kD / G;
-  load_q(a.q, b, hk, a.Hkv, qf);
-  __syncthreads();
-  if (tid < kGqa * NG) {
-    const int hh = tid / NG, g = tid % NG;
-    float s = 0.f;
-    for (int d = g * G; d < (g + 1) * G; ++d) s += qf[hh][d];
-    qsum[hh][g] = s;
-  }
-  __syncthreads();
-  // scores: one thread per slot
-  for (int s = s_begin + tid; s < s_end; s += kDecThreads) {
-    float part_g[kGqa][4];
-    for (int hh = 0; hh < kGqa; ++hh)
-      for (int g = 0; g < 4; ++g) part_g[hh][g] = 0.f;
-    const uint32_t* kp = a.kwords[p] + ((size_t)u * tiles + s / kTile) * kw * kTile + (s % kTile);
-    for (int w = 0; w < kw; ++w) {
-      uint32_t word = kp[w * kTile];
-      for (int j = 0; j < nv; ++j) {
-        const int d = w * nv + j;
-        if (d >= kD) break;
-        const float cf = (float)(word % (uint32_t)L);
-        word /= (uint32_t)L;
-        const int g = d / G;
-        for (int hh = 0; hh < kGqa; ++hh) part_g[hh][g] = __builtin_fmaf(qf[hh][d], cf, part_g[hh][g]);
-      }
-    }
-    const uint32_t* mp = a.kmeta[p] + ((size_t)u * tiles + s / kTile) * NG * kTile + (s % kTile);
-    float sco[kGqa] = {0.f, 0.f, 0.f, 0.f};
-    for (int g = 0; g < NG; ++g) {
-      const uint32_t meta = mp[g * kTile];
-      const float sg = h2f(meta & 0xFFFFu), zg = h2f(meta >> 16);
-      for (int hh = 0; hh < kGqa; ++hh)
-        sco[hh] += __builtin_fmaf(sg, part_g[hh][g], zg * qsum[hh][g]);
-    }
-    for (int hh = 0; hh < kGqa; ++hh) sc[hh][s - s_begin] = sco[hh] * a.scale_log2;
-  }
-  __syncthreads();
-  chunk_softmax(sc, s_end - s_begin, sm, sl);
-  __syncthreads();
-  value_pass(a.vwords[p], a.vmeta[p], u, a.vrows[p], tiles, L, nv, G, s_begin, s_end, sc, red, accs);
-  __syncthreads();
-  finish_partial(part, sm, sl, accs);
-}
-
 // kchan: blockIdx.z == 0 -> quantized tokens (per-channel keys + sparse),
 // blockIdx.z == 1 -> the fp16 window (a single chunk).
 __global__ __launch_bounds__(kDecThreads) void k_decode_kchan(DecodeArgs a) {

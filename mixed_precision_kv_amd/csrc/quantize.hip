@@ -506,6 +506,181 @@ __global__ __launch_bounds__(256) void k_kchan_keys(const uint16_t* __restrict__
   }
 }
 
+// Data-parallel form of the same block step for grids of 3..8 levels and at
+// most two sparse entries per key vector.  Sixteen lanes per token row (eight
+// channels each, eight rows per lane): the row's largest magnitudes come from
+// a 16-lane butterfly over keys (|x| bits << 16 | 0xFFFF - channel, so ties
+// go to the lower channel); the owning lane writes each sparse entry and
+// zeroes it.  Per-channel extremes are packed IEEE minimum/maximum (-0 below
+// +0) over the lane's rows, reduced over the row groups in LDS; each channel
+// gets its scale and zero once; codes use the exact quotient and go to LDS as
+// bytes; key words are integer Horner over 4-digit chunks.
+__device__ inline uint32_t u4_get16(const uint4& v, int i) {
+  const uint32_t w = i < 2 ? v.x : i < 4 ? v.y : i < 6 ? v.z : v.w;
+  return (i & 1) ? (w >> 16) : (w & 0xFFFFu);
+}
+__device__ inline void u4_zero16(uint4& v, int i) {
+  const uint32_t m = (i & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+  if (i < 2) v.x &= m;
+  else if (i < 4) v.y &= m;
+  else if (i < 6) v.z &= m;
+  else v.w &= m;
+}
+__device__ inline void top2_insert(uint32_t k, uint32_t& a1, uint32_t& a2) {
+  a2 = max(a2, min(a1, k));
+  a1 = max(a1, k);
+}
+
+struct KchanArgs {
+  const uint16_t* k;
+  int64_t sb, st, sh;
+  int Hkv, tiles, kblocks, cap;
+  uint32_t* kwords;
+  uint32_t* kmeta;
+  uint32_t* sparse;
+};
+
+template <int L, int SPV>
+__global__ __launch_bounds__(256) void k_kchan_keys_fast(KchanArgs a) {
+  using P = RowPack<L>;
+  constexpr int KW = P::KW, CW = kD / 4 + 1;
+  static_assert(SPV >= 0 && SPV <= 2, "at most two sparse entries per vector");
+  __shared__ uint32_t codes[128][CW];
+  __shared__ uint32_t red_mn[16][kD / 2], red_mx[16][kD / 2];
+  __shared__ uint32_t cmeta[kD];
+  __shared__ float crcp[kD];
+  __shared__ int clamp_any;
+  const int tid = threadIdx.x, l16 = tid & 15, rg = tid >> 4;
+  const int blk = blockIdx.x, u = blockIdx.y;
+  const int b = u / a.Hkv, h = u % a.Hkv;
+  const int t0 = blk * 128;
+  if (tid == 0) clamp_any = 0;
+  const uint16_t* base = a.k + b * a.sb + h * a.sh + 8 * l16;
+  uint4 x[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p)
+    x[p] = *reinterpret_cast<const uint4*>(base + (int64_t)(t0 + 16 * p + rg) * a.st);
+  // sparse entries: the SPV largest magnitudes of each row
+  if (SPV > 0) {
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      uint32_t a1 = 0u, a2 = 0u;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t ch = 8 * l16 + i;
+        top2_insert(((u4_get16(x[p], i) & 0x7FFFu) << 16) | (0xFFFFu - ch), a1, a2);
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const uint32_t b1 = (uint32_t)__shfl_xor((int)a1, o, 16);
+        const uint32_t b2 = (uint32_t)__shfl_xor((int)a2, o, 16);
+        a2 = max(min(a1, b1), max(a2, b2));
+        a1 = max(a1, b1);
+      }
+      const int c1 = 0xFFFF - (int)(a1 & 0xFFFFu), c2 = 0xFFFF - (int)(a2 & 0xFFFFu);
+      const int t = t0 + 16 * p + rg;
+      uint32_t* sp = a.sparse + ((size_t)u * a.cap + t) * SPV;
+#pragma unroll
+      for (int e = 0; e < SPV; ++e) {
+        const int c = e == 0 ? c1 : c2;
+        const int slot = SPV == 1 ? 0 : (c == min(c1, c2) ? 0 : 1);
+        if ((c >> 3) == l16) {
+          sp[slot] = ((uint32_t)c << 16) | u4_get16(x[p], c & 7);
+          u4_zero16(x[p], c & 7);
+        }
+      }
+    }
+  }
+  // per-channel extremes over the lane's rows, then over the row groups
+  {
+    uint32_t mn[4] = {x[0].x, x[0].y, x[0].z, x[0].w}, mx[4] = {x[0].x, x[0].y, x[0].z, x[0].w};
+#pragma unroll
+    for (int p = 1; p < 8; ++p) {
+      const uint32_t w[4] = {x[p].x, x[p].y, x[p].z, x[p].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) { mn[k] = hmin(mn[k], w[k]); mx[k] = hmax(mx[k], w[k]); }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) { red_mn[rg][4 * l16 + k] = mn[k]; red_mx[rg][4 * l16 + k] = mx[k]; }
+  }
+  __syncthreads();
+  if (tid < kD / 2) {
+    uint32_t mn = red_mn[0][tid], mx = red_mx[0][tid];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) { mn = hmin(mn, red_mn[r][tid]); mx = hmax(mx, red_mx[r][tid]); }
+    bool sub = false;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int ch = 2 * tid + e;
+      const uint32_t cmn = e ? (mn >> 16) : (mn & 0xFFFFu), cmx = e ? (mx >> 16) : (mx & 0xFFFFu);
+      GroupQ g = group_setup(cmn, cmx, L);
+      if (g.s == 0.0f) g.r = 0.0f;
+      const uint32_t meta = g.s_bits | (cmn << 16);
+      a.kmeta[((size_t)u * a.kblocks + blk) * kD + ch] = meta;
+      cmeta[ch] = meta;
+      crcp[ch] = g.r;
+      sub |= (g.s_bits & 0x7C00u) == 0u && g.s != 0.0f;
+    }
+    if (sub) atomicOr(&clamp_any, 1);
+  }
+  __syncthreads();
+  {
+    float one = 1.0f;
+    asm volatile("" : "+v"(one));
+    uint32_t m[8];
+    float r[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { m[i] = cmeta[8 * l16 + i]; r[i] = crcp[8 * l16 + i]; }
+    const bool clampq = clamp_any != 0;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const uint32_t w[4] = {x[p].x, x[p].y, x[p].z, x[p].w};
+      uint32_t c[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const h2v zs = hb(m[e]);                       // (s, z)
+        float q = quotient_of(hb(w[e / 2])[e & 1], zs[1], zs[0], r[e], one);
+        if (clampq) q = fminf(q, (float)(L - 1));
+        c[e / 4] = __builtin_amdgcn_cvt_pk_u8_f32(q, e & 3, c[e / 4]);
+      }
+      codes[16 * p + rg][2 * l16] = c[0];
+      codes[16 * p + rg][2 * l16 + 1] = c[1];
+    }
+  }
+  __syncthreads();
+  if (tid < 128) {
+    const int s = t0 + tid;
+    uint32_t row[CW];
+#pragma unroll
+    for (int j = 0; j < CW; ++j) row[j] = codes[tid][j];
+    uint32_t* dst = a.kwords + (((size_t)u * a.tiles + s / kTile) * KW) * kTile + (s % kTile);
+#pragma unroll
+    for (int w = 0; w < KW; ++w) dst[w * kTile] = P::key_word(row, w);
+  }
+}
+
+template <int L>
+static bool launch_kchan_keys_L(const KchanArgs& a, int spv, dim3 grid, hipStream_t s) {
+  switch (spv) {
+    case 0: k_kchan_keys_fast<L, 0><<<grid, 256, 0, s>>>(a); return true;
+    case 1: k_kchan_keys_fast<L, 1><<<grid, 256, 0, s>>>(a); return true;
+    case 2: k_kchan_keys_fast<L, 2><<<grid, 256, 0, s>>>(a); return true;
+  }
+  return false;
+}
+
+static bool launch_kchan_keys_fast(const KchanArgs& a, int L, int spv, dim3 grid, hipStream_t s) {
+  switch (L) {
+    case 3: return launch_kchan_keys_L<3>(a, spv, grid, s);
+    case 4: return launch_kchan_keys_L<4>(a, spv, grid, s);
+    case 5: return launch_kchan_keys_L<5>(a, spv, grid, s);
+    case 6: return launch_kchan_keys_L<6>(a, spv, grid, s);
+    case 7: return launch_kchan_keys_L<7>(a, spv, grid, s);
+    case 8: return launch_kchan_keys_L<8>(a, spv, grid, s);
+  }
+  return false;
+}
+
 __global__ __launch_bounds__(256) void k_kchan_window(const uint16_t* __restrict__ k,
                                                       const uint16_t* __restrict__ v, int64_t sb,
                                                       int64_t st, int64_t sh, int Hkv, int nq,
@@ -549,7 +724,16 @@ bool launch_quantize_kchan(const kvq_layout* L, uint8_t* cache, const void* k, c
   k_kchan_counters<<<ceil_div(c.batch, 64), 64, 0, s>>>((int32_t*)(cache + L->counters), c.batch,
                                                         T, nq);
   if (nq > 0) {
-    k_kchan_keys<<<dim3(nq / c.k_block, U), 256, 0, s>>>(
+    KchanArgs ka;
+    ka.k = (const uint16_t*)k;
+    ka.sb = sb; ka.st = st; ka.sh = sh;
+    ka.Hkv = c.kv_heads; ka.tiles = L->tiles[0]; ka.kblocks = L->kblocks; ka.cap = c.capacity;
+    ka.kwords = (uint32_t*)(cache + L->k_words[0]);
+    ka.kmeta = (uint32_t*)(cache + L->k_meta[0]);
+    ka.sparse = (uint32_t*)(cache + L->sparse);
+    const dim3 grid(nq / c.k_block, U);
+    if (!launch_kchan_keys_fast(ka, c.k_levels, c.sparse_per_vec, grid, s))
+      k_kchan_keys<<<grid, 256, 0, s>>>(
         (const uint16_t*)k, sb, st, sh, c.kv_heads, c.k_levels, L->nv[0], L->kw[0], L->tiles[0],
         L->kblocks, c.capacity, c.sparse_per_vec, (uint32_t*)(cache + L->k_words[0]),
         (uint32_t*)(cache + L->k_meta[0]), (uint32_t*)(cache + L->sparse));

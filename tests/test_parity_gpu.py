@@ -152,6 +152,28 @@ def test_kchan_quantize_and_decode(T):
     _check_kchan(w, inp, run)
 
 
+def test_kchan_outlier_ties_and_degenerate_blocks():
+    """Sparse outliers under magnitude ties (lower channel wins, +x and -x
+    tie), all-zero and -0 key rows (channels 0 and 1 are taken), constant
+    channels (scale 0) and tiny channel ranges (subnormal scales)."""
+    w = C[4].shrink(name="c5_edges", batch=1, kv_heads=2, q_heads=8, tokens=640)
+    log(f"case {w.name}")
+    inp = synth.make_inputs(w)
+    k = inp.k
+    k[0, 3, 0, :] = np.float16(0.0)                          # all zero
+    k[0, 4, 0, :] = np.float16(-0.0)                         # all -0
+    k[0, 5, 0, 40] = np.float16(7.0)                         # three-way tie for the top
+    k[0, 5, 0, 20] = np.float16(-7.0)
+    k[0, 5, 0, 90] = np.float16(7.0)
+    k[0, 6, 1, :] = np.float16(1.5)                          # every magnitude equal
+    k[0, 128:256, 1, 17] = np.float16(0.25)                  # constant channel in a block
+    k[0, 256:384, 0, 33] = (np.arange(128) % 8).astype(np.float16) * np.float16(2.0 ** -24)
+    k[0, 384:512, 1, 64] = np.float16(-0.0)
+    run = GpuRun(w, inp)
+    run.quantize()
+    _check_kchan(w, inp, run)
+
+
 def test_append_then_decode_small():
     """Generation-time quantization: every step's tier decision, slot, words
     and the attention after it, against the running-median oracle."""
