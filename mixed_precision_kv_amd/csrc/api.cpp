@@ -25,7 +25,7 @@ int decode_chunks(const kvq_layout* L, int max_len, int* nch0, int* nch1) {
   } else {
     int nq = kchan_nq(L, max_len);
     *nch0 = ceil_div(nq, decode_chunk_kchan(L));
-    *nch1 = 1;  // the fp16 window
+    *nch1 = ceil_div(L->win_cap, kWinChunk);   // the fp16 window
   }
   return *nch0 + *nch1;
 }

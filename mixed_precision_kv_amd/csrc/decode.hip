@@ -40,6 +40,8 @@ struct DecodeArgs {
   const uint16_t* kwin;
   const uint16_t* vwin;
   int vL, vnv, vgroup, spv, cap, kblocks, win_cap;
+  int zbase;              // kchan: 1 -> the grid covers the fp16 window only
+  int nwch;               // kchan: window chunks of kWinChunk tokens
 };
 
 __device__ inline float wave_max(float v) {
@@ -138,9 +140,9 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_kchan(DecodeArgs a) {
   __shared__ float accs[kGqa * kD];
   __shared__ float sm[kGqa], sl[kGqa];
   const int tid = threadIdx.x;
-  const int c = blockIdx.x, u = blockIdx.y, z = blockIdx.z;
+  const int c = blockIdx.x, u = blockIdx.y, z = blockIdx.z + a.zbase;
   const int b = u / a.Hkv, hk = u % a.Hkv;
-  const int nchp = z ? 1 : a.nch0;
+  const int nchp = z ? a.nwch : a.nch0;
   if (c >= nchp) return;
   float* part = a.part + ((size_t)u * a.nch_total + (z ? a.nch0 : 0) + c) * kGqa * kPartStride;
   const int nq = a.counters[b * 4 + 1];
@@ -148,23 +150,37 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_kchan(DecodeArgs a) {
   load_q(a.q, b, hk, a.Hkv, qf);
   __syncthreads();
   if (z == 1) {
-    if (nwin <= 0) { write_empty(part); return; }
-    const uint16_t* kwp = a.kwin + (size_t)u * a.win_cap * kD;
-    const uint16_t* vwp = a.vwin + (size_t)u * a.win_cap * kD;
-    for (int i = tid; i < nwin; i += kDecThreads) {
+    // window chunk c: tokens [kWinChunk c, kWinChunk (c + 1)) of the fp16 window
+    const int w0 = c * kWinChunk, nwin_c = min(kWinChunk, nwin - w0);
+    if (nwin_c <= 0) { write_empty(part); return; }
+    const uint16_t* kwp = a.kwin + ((size_t)u * a.win_cap + w0) * kD;
+    const uint16_t* vwp = a.vwin + ((size_t)u * a.win_cap + w0) * kD;
+    // one thread per window token: its row as sixteen 16-byte loads, all in flight
+    for (int i = tid; i < nwin_c; i += kDecThreads) {
+      const uint4* kr = reinterpret_cast<const uint4*>(kwp + (size_t)i * kD);
+      uint4 kv[kD / 8];
+#pragma unroll
+      for (int c8 = 0; c8 < kD / 8; ++c8) kv[c8] = kr[c8];
       float sco[kGqa] = {0.f, 0.f, 0.f, 0.f};
-      for (int d = 0; d < kD; ++d) {
-        const float kv = h2f(kwp[(size_t)i * kD + d]);
-        for (int hh = 0; hh < kGqa; ++hh) sco[hh] = __builtin_fmaf(qf[hh][d], kv, sco[hh]);
+#pragma unroll
+      for (int c8 = 0; c8 < kD / 8; ++c8) {
+        const uint32_t wv[4] = {kv[c8].x, kv[c8].y, kv[c8].z, kv[c8].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = h2f(e & 1 ? (wv[e / 2] >> 16) : (wv[e / 2] & 0xFFFFu));
+#pragma unroll
+          for (int hh = 0; hh < kGqa; ++hh) sco[hh] = __builtin_fmaf(qf[hh][8 * c8 + e], x, sco[hh]);
+        }
       }
       for (int hh = 0; hh < kGqa; ++hh) sc[hh][i] = sco[hh] * a.scale_log2;
     }
     __syncthreads();
-    chunk_softmax(sc, nwin, sm, sl);
+    chunk_softmax(sc, nwin_c, sm, sl);
     __syncthreads();
     const int d = tid & (kD - 1), half = tid >> 7;
     float acc[kGqa] = {0.f, 0.f, 0.f, 0.f};
-    for (int i = half; i < nwin; i += 2) {
+#pragma unroll 16
+    for (int i = half; i < nwin_c; i += 2) {
       const float vv = h2f(vwp[(size_t)i * kD + d]);
       for (int hh = 0; hh < kGqa; ++hh) acc[hh] = __builtin_fmaf(sc[hh][i], vv, acc[hh]);
     }
@@ -372,11 +388,17 @@ bool launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, flo
     a.vL = c.v_levels; a.vnv = L->vnv; a.vgroup = c.v_group; a.spv = c.sparse_per_vec;
     a.cap = c.capacity; a.kblocks = L->kblocks; a.win_cap = L->win_cap;
     a.sparse = (const uint32_t*)(cache + L->sparse);
+    a.nwch = nch1;
     a.kwin = (const uint16_t*)(cache + L->k_win);
     a.vwin = (const uint16_t*)(cache + L->v_win);
     if (L->win_cap > 640) return false;
-    const int gx = nch0 > 1 ? nch0 : 1;
-    k_decode_kchan<<<dim3(gx, U, 2), kDecThreads, 0, s>>>(a);
+    if (launch_decode_kchan_mfma(L, cache, q, a.scale_log2, a.part, nch0, nch, stream)) {
+      a.zbase = 1;                            // the window only
+      k_decode_kchan<<<dim3(nch1, U, 1), kDecThreads, 0, s>>>(a);
+    } else {
+      const int gx = nch0 > nch1 ? nch0 : nch1;
+      k_decode_kchan<<<dim3(gx, U, 2), kDecThreads, 0, s>>>(a);
+    }
   }
   launch_merge((const float*)ws, (uint16_t*)out, U, nch, c.kv_heads, s);
   return hipGetLastError() == hipSuccess;

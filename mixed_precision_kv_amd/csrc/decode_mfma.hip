@@ -461,4 +461,275 @@ bool launch_decode_pool(int L, const PoolArgs& a, int G, int nch, int U, void* s
   return false;
 }
 
+// ===================== per-channel keys on the matrix cores =====================
+// Quantized part of the per-channel-key cache (KVQuant summary, "techniques":
+// per-channel keys in 128-token blocks, per-vector dense-and-sparse outliers;
+// SKVQ, Abstract: 2-bit keys) for 4-level keys, 3-level values and value
+// groups of 32.  A workgroup (four waves) owns a 640-token chunk: five key
+// blocks, forty key tiles, four value units of 160 slots.
+//   keys:   each wave scores ten 16-token tiles.  The per-channel scale sits
+//           in the A operand: rows 0..3 hold fp16(4 q_h[d] s_d) and rows 4..7
+//           the fp16 remainder of 4 q_h[d] s_d (exact in fp32), so hi + lo
+//           carries the product to about 2^-22; the digits as fp16 are 1 + c/4,
+//           and sum_d q_h[d] (z_d - 4 s_d) per block is added in fp32, as are
+//           the sparse entries q_h[ch] * value.
+//   softmax over the chunk's 640 scores (wave h: head h), weights 2^6 p as
+//           fp16 rounded half up, in the value operand's order.
+//   values: wave w runs value unit w through the same column-word matrix
+//           path as the tiered pools; the four units are summed in LDS.
+struct KchanDecArgs {
+  const int32_t* counters;
+  const uint16_t* q;
+  float* part;
+  const uint32_t* kwords;       // [u][tile][8][16]
+  const uint32_t* kmeta;        // [u][key block][128]
+  const uint32_t* sparse;       // [u][cap][spv]
+  const uint32_t* vwords;       // [u][row][128]
+  const uint32_t* vmeta;        // [u][tile][NG][16]
+  int Hkv, tiles, kblocks, vrows, cap, spv, nch_total;
+  float c;                      // softmax scale * log2(e)
+};
+
+constexpr int kKcCH = 640, kKcKB = 128, kKcNB = kKcCH / kKcKB, kKcTW = kKcCH / 16 / 4;
+
+template <int VL, int G>
+__global__ __launch_bounds__(256) void k_decode_kchan_mfma(KchanDecArgs a) {
+  using DKc = Digits<4, 2>;                  // key words j and j + 4 of a lane
+  constexpr int NVV = cpw(VL), R = 2, VU = 4 * R * NVV;
+  using DV = Unpack<VL, R>;
+  constexpr int VM = DV::NH8, VK = VM * 8, NG = kD / G;
+  static_assert(VU * 4 == kKcCH, "one value unit per wave");
+  static_assert(VK == R * DV::PW || !DV::kTable, "value operand without padding");
+  static_assert(G == 32, "value groups of 32 channels");
+  __shared__ float qf[kGqa][kD];
+  __shared__ __attribute__((aligned(16))) _Float16 atab[kKcNB][4][4][8][8];   // [blk][m][j][row][i]
+  __shared__ float aoff[kKcNB][kGqa];
+  __shared__ uint32_t kms[kKcNB * kKcKB];
+  __shared__ float sc[kGqa][kKcCH];
+  __shared__ __attribute__((aligned(16))) _Float16 pw[kGqa][4 * 4 * VK];
+  __shared__ __attribute__((aligned(16))) _Float16 vsl[NG][4 * 4 * VK];
+  __shared__ __attribute__((aligned(16))) _Float16 vzl[NG][4 * 4 * VK];
+  __shared__ uint2 ctab[DV::kTableEntries];
+  __shared__ float red[4][kGqa][kD];
+  __shared__ float zr[4][16];
+  __shared__ float hm[kGqa], hl[kGqa];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int n = lane & 15, j = lane >> 4;
+  const int c = blockIdx.x, u = blockIdx.y;
+  const int b = u / a.Hkv, hk = u % a.Hkv;
+  float* part = a.part + ((size_t)u * a.nch_total + c) * kGqa * kPartF;
+  const int nq = a.counters[b * 4 + 1];
+  const int s_begin = c * kKcCH, s_end = min(nq, s_begin + kKcCH);
+  if (s_begin >= s_end) {
+    for (int i = tid; i < kGqa * kPartF; i += 256) part[i] = (i % kPartF == 0) ? -INFINITY : 0.f;
+    return;
+  }
+  // ---- every load of the chunk goes out first
+  const BufRes rK = make_res(a.kwords + (size_t)u * a.tiles * 8 * 16, a.tiles * 8 * 16 * 4);
+  const BufRes rKM = make_res(a.kmeta + (size_t)u * a.kblocks * kKcKB, a.kblocks * kKcKB * 4);
+  const BufRes rS = make_res(a.sparse + (size_t)u * a.cap * a.spv, a.cap * a.spv * 4);
+  const BufRes rV = make_res(a.vwords + (size_t)u * a.vrows * kD, a.vrows * kD * 4);
+  const BufRes rVM = make_res(a.vmeta + (size_t)u * a.tiles * NG * 16, a.tiles * NG * 16 * 4);
+  const int tile0 = s_begin / 16;
+  uint32_t kw[kKcTW][2], sp[kKcTW];
+#pragma unroll
+  for (int i = 0; i < kKcTW; ++i) {
+    const int t = kKcTW * w + i;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) kw[i][x] = bload(rK, (((tile0 + t) * 8 + j + 4 * x) * 16 + n) * 4u);
+    sp[i] = j < a.spv ? bload(rS, ((uint32_t)(s_begin + 16 * t + n) * a.spv + j) * 4u) : 0u;
+  }
+  uint32_t km[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const int e = tid + 256 * k;
+    km[k] = e < kKcNB * kKcKB ? bload(rKM, (uint32_t)((s_begin / kKcKB) * kKcKB + e) * 4u) : 0u;
+  }
+  constexpr int VMETA = VU / 16 * NG * 16 / 64;            // value meta words per lane
+  uint32_t vw[8][R], vm[VMETA];
+  {
+    const int row0 = (s_begin + VU * w) / NVV + j * R;
+#pragma unroll
+    for (int v = 0; v < 8; ++v)
+#pragma unroll
+      for (int r2 = 0; r2 < R; ++r2) vw[v][r2] = bload(rV, ((row0 + r2) * kD + 16 * v + n) * 4u);
+    const int mt0 = (s_begin + VU * w) / 16;
+#pragma unroll
+    for (int k = 0; k < VMETA; ++k) vm[k] = bload(rVM, (uint32_t)(mt0 * NG * 16 + lane + 64 * k) * 4u);
+  }
+  // ---- set-up: query, digit table, key-scale operand tables
+  for (int i = tid; i < kGqa * kD; i += 256)
+    qf[i / kD][i % kD] = h2f(a.q[((size_t)b * a.Hkv * kGqa + hk * kGqa) * kD + i]);
+  DV::fill(ctab, tid, 256);
+#pragma unroll
+  for (int k = 0; k < 3; ++k)
+    if (tid + 256 * k < kKcNB * kKcKB) kms[tid + 256 * k] = km[k];
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const int e = tid + 256 * k;
+    if (e < kKcNB * kKcKB) {
+      const int blk = e / kKcKB, ch = e % kKcKB;
+      const float sg = h2f(km[k] & 0xFFFFu);
+      // operand position of channel ch: word jj + 4 (m/2), digit d
+      const int word = ch >> 4, d = ch & 15;
+      const int tt = d < 8 ? 2 * d : 2 * (d - 8) + 1;      // output index within the word
+      const int jj = word & 3, m = 2 * (word >> 2) + (tt >> 3), i = tt & 7;
+#pragma unroll
+      for (int h = 0; h < kGqa; ++h) {
+        const float A = 4.0f * qf[h][ch] * sg;             // exact: two 11-bit significands
+        const _Float16 hi = (_Float16)A;
+        atab[blk][m][jj][h][i] = hi;
+        atab[blk][m][jj][4 + h][i] = (_Float16)(A - (float)hi);
+      }
+    }
+  }
+  if (tid < kKcNB * kGqa) {
+    const int blk = tid >> 2, h = tid & 3;
+    float o = 0.f;
+    for (int ch = 0; ch < kKcKB; ++ch) {
+      const uint32_t mw = kms[blk * kKcKB + ch];
+      const float sg = h2f(mw & 0xFFFFu), zg = h2f(mw >> 16);
+      o = __builtin_fmaf(qf[h][ch], __builtin_fmaf(-4.0f, sg, zg), o);
+    }
+    aoff[blk][h] = o;
+  }
+  __syncthreads();
+  // ---- keys: ten tiles per wave
+#pragma unroll
+  for (int i = 0; i < kKcTW; ++i) {
+    const int t = kKcTW * w + i, blk = t >> 3;
+    _Float16 dg[DKc::NOUT];
+    DKc::run(kw[i], dg);
+    f4 pr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      h8 bk, ak;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bk[e] = dg[8 * m + e];
+      ak = n < 8 ? *reinterpret_cast<const h8*>(&atab[blk][m][j][n][0]) : (h8){0, 0, 0, 0, 0, 0, 0, 0};
+      pr = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, bk, pr, 0, 0, 0);
+    }
+    // lane (n, 0): rows 0..3 (hi), lane (n, 1): rows 4..7 (lo); sparse entry j
+    if (j < a.spv) {
+      const int ch = (int)(sp[i] >> 16) & (kD - 1);
+      const float val = h2f(sp[i] & 0xFFFFu);
+#pragma unroll
+      for (int h = 0; h < kGqa; ++h) pr[h] = __builtin_fmaf(qf[h][ch], val, pr[h]);
+    }
+    const int s = s_begin + 16 * t + n;
+#pragma unroll
+    for (int h = 0; h < kGqa; ++h) {
+      const float x = pr[h] + __shfl_xor(pr[h], 16);
+      const float scv = s < s_end ? (x + aoff[blk][h]) * a.c : -INFINITY;
+      if (j == (h >> 1)) sc[h][16 * t + n] = scv;
+    }
+  }
+  __syncthreads();
+  // ---- softmax over the chunk (wave w: head w) and value meta staging
+  {
+    const int h = w;
+    float mx = -INFINITY;
+    for (int i = lane; i < kKcCH; i += 64) mx = fmaxf(mx, sc[h][i]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    float l = 0.f;
+    for (int i = lane; i < kKcCH; i += 64) {
+      const float p = __builtin_amdgcn_exp2f(sc[h][i] - mx);
+      l += p;
+      const int unit = i / VU, rem = i % VU, jj = rem / (R * NVV), rr = rem % (R * NVV);
+      const float xq = __uint_as_float(__float_as_uint(p * kAScale) + 0x1000u);
+      pw[h][unit * 4 * VK + jj * VK + DV::pos_of(rr / NVV, rr % NVV)] =
+          __builtin_bit_cast(h2v, __builtin_amdgcn_cvt_pkrtz(xq, xq))[0];
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
+    if (lane == 0) { hm[h] = mx; hl[h] = l; }
+#pragma unroll
+    for (int k = 0; k < VMETA; ++k) {
+      const int e = lane + 64 * k;
+      const int g = (e % (NG * 16)) / 16, sl = (e / (NG * 16)) * 16 + (e % 16);   // slot in the unit
+      const int jj = sl / (R * NVV), rr = sl % (R * NVV);
+      const int pos = w * 4 * VK + jj * VK + DV::pos_of(rr / NVV, rr % NVV);
+      const bool ok = s_begin + VU * w + sl < s_end;
+      vsl[g][pos] = __builtin_bit_cast(_Float16, (uint16_t)(ok ? (vm[k] & 0xFFFFu) : 0u));
+      vzl[g][pos] = __builtin_bit_cast(_Float16, (uint16_t)(ok ? (vm[k] >> 16) : 0u));
+    }
+  }
+  __syncthreads();
+  // ---- values: wave w runs unit w
+  {
+    const int h = n & 3, g = n >> 2;
+    float zacc = 0.f;
+    h8 av[VM];
+#pragma unroll
+    for (int m = 0; m < VM; ++m) {
+      const int pos = w * 4 * VK + j * VK + 8 * m;
+      const h8 p16 = *reinterpret_cast<const h8*>(&pw[h][pos]);
+      const h8 sv = *reinterpret_cast<const h8*>(&vsl[g][pos]);
+      const h8 zv = *reinterpret_cast<const h8*>(&vzl[g][pos]);
+      av[m] = p16 * sv;
+#pragma unroll
+      for (int e = 0; e < 8; e += 2)
+        zacc = __builtin_amdgcn_fdot2((h2v){p16[e], p16[e + 1]}, (h2v){zv[e], zv[e + 1]}, zacc, false);
+    }
+    f4 acc[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      acc[v] = (f4){0.f, 0.f, 0.f, 0.f};
+      h8 bv[VM];
+      DV::run(vw[v], ctab, bv);
+#pragma unroll
+      for (int m = 0; m < VM; ++m) acc[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[m], bv[m], acc[v], 0, 0, 0);
+    }
+    float zs = zacc;
+    zs += __shfl_xor(zs, 16);
+    zs += __shfl_xor(zs, 32);
+    if (lane < 16) zr[w][lane] = zs;
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      if ((v >> 1) != j) continue;             // channels 16v..16v+15 are in group v/2
+#pragma unroll
+      for (int hh = 0; hh < kGqa; ++hh) red[w][hh][16 * v + n] = acc[v][hh] + zr[w][4 * j + hh];
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < kGqa * kD; i += 256) {
+    const int hh = i / kD, d = i % kD;
+    part[hh * kPartF + 4 + d] = (red[0][hh][d] + red[1][hh][d] + red[2][hh][d] + red[3][hh][d]) * (1.0f / kAScale);
+  }
+  if (tid < kGqa) {
+    part[tid * kPartF + 0] = hm[tid];
+    part[tid * kPartF + 1] = hl[tid];
+  }
+}
+
+// Matrix-core decode of the quantized per-channel-key part when its shape
+// is the one above (4-level keys, 3-level values, groups of 32, blocks of
+// 128, at most two sparse entries); false: not this shape.
+bool launch_decode_kchan_mfma(const kvq_layout* L, const uint8_t* cache, const void* q, float c,
+                              float* part, int nch0, int nch_total, void* stream) {
+  const kvq_config& cf = L->cfg;
+  if (cf.k_levels != 4 || cf.v_levels != 3 || cf.v_group != 32 || cf.k_block != kKcKB ||
+      cf.sparse_per_vec > 2 || L->kw[0] != 8 || decode_chunk_kchan(L) != kKcCH)
+    return false;
+  KchanDecArgs a;
+  a.counters = (const int32_t*)(cache + L->counters);
+  a.q = (const uint16_t*)q;
+  a.part = part;
+  a.kwords = (const uint32_t*)(cache + L->k_words[0]);
+  a.kmeta = (const uint32_t*)(cache + L->k_meta[0]);
+  a.sparse = (const uint32_t*)(cache + L->sparse);
+  a.vwords = (const uint32_t*)(cache + L->v_words[0]);
+  a.vmeta = (const uint32_t*)(cache + L->v_meta[0]);
+  a.Hkv = cf.kv_heads; a.tiles = L->tiles[0]; a.kblocks = L->kblocks; a.vrows = L->vrows[0];
+  a.cap = cf.capacity; a.spv = cf.sparse_per_vec; a.nch_total = nch_total;
+  a.c = c;
+  if (nch0 > 0)
+    k_decode_kchan_mfma<3, 32><<<dim3(nch0, cf.batch * cf.kv_heads), 256, 0, (hipStream_t)stream>>>(a);
+  return true;
+}
+
 }  // namespace kvq

@@ -17,6 +17,7 @@ inline int lcm_i(int a, int b) { return a / gcd_i(a, b) * b; }
 inline int decode_chunk_kchan(const kvq_layout* L) {
   return lcm_i(lcm_i(L->cfg.k_block, 16), L->vnv);
 }
+constexpr int kWinChunk = 16;   // fp16-window tokens per decode workgroup
 inline int kchan_nq(const kvq_layout* L, int T) {
   int kb = L->cfg.k_block;
   int n = (T - L->cfg.window) / kb;
@@ -61,5 +62,9 @@ struct PoolArgs {
 // (uses the kernel's occupancy; falls back to 8 macro tiles).
 int decode_pool_chunk(int L, int G, int U, int slots_per_unit);
 bool launch_decode_pool(int L, const PoolArgs& a, int G, int nch, int U, void* stream);
+// Matrix-core decode of the quantized part of a per-channel-key cache;
+// false when the configuration is not the one it is built for.
+bool launch_decode_kchan_mfma(const kvq_layout* L, const uint8_t* cache, const void* q, float c,
+                              float* part, int nch0, int nch_total, void* stream);
 
 }  // namespace kvq
