@@ -584,15 +584,20 @@ __global__ __launch_bounds__(256) void k_decode_kchan_mfma(KchanDecArgs a) {
       }
     }
   }
-  if (tid < kKcNB * kGqa) {
-    const int blk = tid >> 2, h = tid & 3;
+  // sum_d q_h[d] (z_d - 4 s_d) per (block, head): wave w takes pairs w, w + 4, ...;
+  // lanes hold channels l and l + 64 (fixed reduction order)
+  for (int pr = w; pr < kKcNB * kGqa; pr += 4) {
+    const int blk = pr >> 2, h = pr & 3;
     float o = 0.f;
-    for (int ch = 0; ch < kKcKB; ++ch) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int ch = lane + 64 * k;
       const uint32_t mw = kms[blk * kKcKB + ch];
-      const float sg = h2f(mw & 0xFFFFu), zg = h2f(mw >> 16);
-      o = __builtin_fmaf(qf[h][ch], __builtin_fmaf(-4.0f, sg, zg), o);
+      o = __builtin_fmaf(qf[h][ch], __builtin_fmaf(-4.0f, h2f(mw & 0xFFFFu), h2f(mw >> 16)), o);
     }
-    aoff[blk][h] = o;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) o += __shfl_xor(o, off);
+    if (lane == 0) aoff[blk][h] = o;
   }
   __syncthreads();
   // ---- keys: ten tiles per wave
