@@ -778,6 +778,8 @@ struct AppendArgs {
   int capacity, Hkv, G;
 };
 
+constexpr int kAppendBatch = 16;              // sorted-score elements per thread per round trip
+
 template <int G>
 __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
   constexpr int NG = kD / G;
@@ -812,9 +814,19 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
   const int tier = s_tier, len = s_len, slot = s_slot;
   const int L = a.L[tier], nv = a.nv[tier], kw = a.kw[tier], tiles = a.tiles[tier],
             vrows = a.vrows[tier];
-  // position of the new score: number of present scores <= snew
+  // position of the new score: number of present scores <= snew (sixteen
+  // loads per thread in flight per round trip)
   uint32_t le = 0;
-  for (int i = tid; i < len; i += 256) le += (srt[i] <= snew) ? 1u : 0u;
+  for (int i0 = 0; i0 < len; i0 += 256 * kAppendBatch) {
+    float x[kAppendBatch];
+#pragma unroll
+    for (int k = 0; k < kAppendBatch; ++k) {
+      const int i = i0 + 256 * k + tid;
+      x[k] = i < len ? srt[i] : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < kAppendBatch; ++k) le += (i0 + 256 * k + tid < len && x[k] <= snew) ? 1u : 0u;
+  }
   atomicAdd(&s_le, le);
   // quantize every (head, k/v, group)
   for (int task = tid; task < a.Hkv * 2 * NG; task += 256) {
@@ -844,14 +856,21 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
     uint32_t* wp = &a.vwords[tier][((size_t)u * vrows + r) * kD + d];
     *wp = *wp + pw * (uint32_t)codes[1][h][d];
   }
-  // insert the score: shift srt[pos..len) up by one, highest chunk first
-  for (int hi = len; hi > (int)pos; hi -= 256) {
-    const int i = hi - 1 - tid;
-    float val = 0.0f;
-    const bool act = i >= (int)pos;
-    if (act) val = srt[i];
+  // insert the score: shift srt[pos..len) up by one, highest chunk first;
+  // a chunk is read whole before any of it is written
+  for (int hi = len; hi > (int)pos; hi -= 256 * kAppendBatch) {
+    float val[kAppendBatch];
+#pragma unroll
+    for (int k = 0; k < kAppendBatch; ++k) {
+      const int i = hi - 1 - tid - 256 * k;
+      val[k] = i >= (int)pos ? srt[i] : 0.0f;
+    }
     __syncthreads();
-    if (act) srt[i + 1] = val;
+#pragma unroll
+    for (int k = 0; k < kAppendBatch; ++k) {
+      const int i = hi - 1 - tid - 256 * k;
+      if (i >= (int)pos) srt[i + 1] = val[k];
+    }
     __syncthreads();
   }
   if (tid == 0) {
