@@ -8,7 +8,7 @@
 namespace kvq {
 
 constexpr int kSortTile = 1024;   // keys per radix-sort block (256 threads x 4)
-constexpr int kSlotSeg = 4096;    // tokens per slot-scan workgroup
+constexpr int kSlotSeg = 1024;    // tokens per slot-scan workgroup
 constexpr int kMaxSortLen = 1 << 18;   // longest ranked sequence (tokens)
 constexpr int kMergeMaxT = 32768;      // up to this length: block sort + merge rank (keys in LDS)
 

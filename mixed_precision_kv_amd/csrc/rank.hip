@@ -24,18 +24,24 @@ constexpr int kSortThreads = 256;
 constexpr int kSortItems = kSortTile / kSortThreads;   // 4, striped
 
 // Workgroups are handed to the 8 XCDs round-robin by linear id, and each XCD
-// has its own L2.  The sort kernels run on a 1-D grid of 8 * ceil(B / 8) *
-// nblk workgroups mapped so that every block of sequence b runs on XCD b % 8:
-// the scattered 4-byte writes of one sequence then meet in one L2 instead of
-// partial lines in several.
+// has its own L2.  The sort kernels run on a 1-D grid of X * ceil(B / X) *
+// nblk workgroups, X = min(B, 8), mapped so that every block of sequence b
+// runs on the XCDs congruent to b mod X: with 8 or more sequences each one's
+// scattered 4-byte writes meet in one L2, and fewer sequences still spread
+// over every XCD.
 constexpr int kXcds = 8;
+__host__ __device__ inline int seq_group(int B) { return B < kXcds ? B : kXcds; }
 __device__ inline bool seq_block(int nblk, int B, int& b, int& blk) {
-  const int id = blockIdx.x, x = id % kXcds, k = id / kXcds;
-  b = x + kXcds * (k / nblk);
+  const int X = seq_group(B);
+  const int id = blockIdx.x, x = id % X, k = id / X;
+  b = x + X * (k / nblk);
   blk = k % nblk;
   return b < B;
 }
-static inline dim3 seq_grid(int nblk, int B) { return dim3(kXcds * ((B + kXcds - 1) / kXcds) * nblk); }
+static inline dim3 seq_grid(int nblk, int B) {
+  const int X = seq_group(B);
+  return dim3(X * ((B + X - 1) / X) * nblk);
+}
 
 // hist layout: [b][pass][blk][digit].  The first kernel forms the keys and
 // the pass-0 counts, and zeroes the per-segment counts of high-tier tokens
@@ -102,6 +108,7 @@ struct ScatterArgs {
 };
 
 // One pass of the stable LSD sort.
+constexpr int kCountBatch = 32;              // block counts per thread per round trip
 __global__ __launch_bounds__(256) void k_rank_scatter(ScatterArgs a) {
   __shared__ uint32_t goff[256];
   __shared__ uint32_t cnt[4][256];
@@ -115,15 +122,15 @@ __global__ __launch_bounds__(256) void k_rank_scatter(ScatterArgs a) {
   const bool last = a.pass == 3;
   {
     // output offset of (digit tid, this block) = keys with a smaller digit +
-    // keys with this digit in earlier blocks (counts read 16 blocks per trip)
+    // keys with this digit in earlier blocks (counts read kCountBatch blocks per trip)
     const uint32_t* hp = a.hist + ((size_t)b * 4 + a.pass) * a.nblk * 256;
     uint32_t before = 0, total = 0;
-    for (int j0 = 0; j0 < a.nblk; j0 += 16) {
-      uint32_t c[16];
+    for (int j0 = 0; j0 < a.nblk; j0 += kCountBatch) {
+      uint32_t c[kCountBatch];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) c[k] = (j0 + k < a.nblk) ? hp[(size_t)(j0 + k) * 256 + tid] : 0u;
+      for (int k = 0; k < kCountBatch; ++k) c[k] = (j0 + k < a.nblk) ? hp[(size_t)(j0 + k) * 256 + tid] : 0u;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
+      for (int k = 0; k < kCountBatch; ++k) {
         total += c[k];
         before += (j0 + k < blk) ? c[k] : 0u;
       }
@@ -202,15 +209,20 @@ __global__ __launch_bounds__(256) void k_rank_slots(const int32_t* __restrict__ 
                                                     int cap, int cap_hi, int cap_lo, int nseg, int B) {
   constexpr int kChunks = SEG / 4 / 64;               // 64-token chunks per wave
   __shared__ uint32_t wtot[4];
-  __shared__ uint32_t segbase;
+  __shared__ uint32_t wbase[4];
   const int tid = threadIdx.x;
   int b, seg;
   if (!seq_block(nseg, B, b, seg)) return;
   const int lane = tid & 63, w = tid >> 6;
-  if (tid == 0) {
+  {
+    // high-tier tokens of the earlier segments, summed by every thread
     uint32_t p = 0;
-    for (int k = 0; k < seg; ++k) p += segcnt[(size_t)b * nseg + k];
-    segbase = p;
+    for (int k = tid; k < seg; k += 256) p += segcnt[(size_t)b * nseg + k];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) p += (uint32_t)__shfl_xor((int)p, o);
+    if (lane == 0) wbase[w] = p;
+  }
+  if (tid == 0) {
     if (seg == 0) {
       counters[b * 4 + 0] = T;
       counters[b * 4 + 1] = n_hi;
@@ -230,7 +242,7 @@ __global__ __launch_bounds__(256) void k_rank_slots(const int32_t* __restrict__ 
   }
   if (lane == 0) wtot[w] = mine;
   __syncthreads();
-  uint32_t pre = segbase;
+  uint32_t pre = wbase[0] + wbase[1] + wbase[2] + wbase[3];
   for (int k = 0; k < w; ++k) pre += wtot[k];
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
