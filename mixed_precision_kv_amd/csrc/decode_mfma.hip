@@ -493,7 +493,7 @@ struct KchanDecArgs {
 constexpr int kKcCH = 640, kKcKB = 128, kKcNB = kKcCH / kKcKB, kKcTW = kKcCH / 16 / 4;
 
 template <int VL, int G>
-__global__ __launch_bounds__(256) void k_decode_kchan_mfma(KchanDecArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_decode_kchan_mfma(KchanDecArgs a) {
   using DKc = Digits<4, 2>;                  // key words j and j + 4 of a lane
   constexpr int NVV = cpw(VL), R = 2, VU = 4 * R * NVV;
   using DV = Unpack<VL, R>;
@@ -502,69 +502,89 @@ __global__ __launch_bounds__(256) void k_decode_kchan_mfma(KchanDecArgs a) {
   static_assert(VK == R * DV::PW || !DV::kTable, "value operand without padding");
   static_assert(G == 32, "value groups of 32 channels");
   __shared__ float qf[kGqa][kD];
-  __shared__ __attribute__((aligned(16))) _Float16 atab[kKcNB][4][4][8][8];   // [blk][m][j][row][i]
   __shared__ float aoff[kKcNB][kGqa];
-  __shared__ uint32_t kms[kKcNB * kKcKB];
-  __shared__ float sc[kGqa][kKcCH];
-  __shared__ __attribute__((aligned(16))) _Float16 pw[kGqa][4 * 4 * VK];
-  __shared__ __attribute__((aligned(16))) _Float16 vsl[NG][4 * 4 * VK];
-  __shared__ __attribute__((aligned(16))) _Float16 vzl[NG][4 * 4 * VK];
   __shared__ uint2 ctab[DV::kTableEntries];
-  __shared__ float red[4][kGqa][kD];
   __shared__ float zr[4][16];
   __shared__ float hm[kGqa], hl[kGqa];
+  // Two overlays (each region's users are separated by a barrier):
+  //   A: key-operand tables and staged key scales (set-up, keys), then the
+  //      value weights, scales and zeros (softmax, values);
+  //   B: the chunk's scores (keys, softmax), then the per-wave outputs.
+  typedef _Float16 Atab[kKcNB][4][4][8][8];               // [blk][m][j][row][i]
+  typedef _Float16 VOp[4 * 4 * VK];
+  constexpr int kAKey = sizeof(Atab) + kKcNB * kKcKB * 4;
+  constexpr int kAVal = (kGqa + 2 * NG) * (int)sizeof(VOp);
+  constexpr int kB = (kGqa * kKcCH > 4 * kGqa * kD ? kGqa * kKcCH : 4 * kGqa * kD) * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t ovA[kAKey > kAVal ? kAKey : kAVal];
+  __shared__ __attribute__((aligned(16))) uint8_t ovB[kB];
+  Atab& atab = *reinterpret_cast<Atab*>(ovA);
+  uint32_t* kms = reinterpret_cast<uint32_t*>(ovA + sizeof(Atab));
+  VOp* pw = reinterpret_cast<VOp*>(ovA);                      // [kGqa]
+  VOp* vsl = pw + kGqa;                                       // [NG]
+  VOp* vzl = vsl + NG;                                        // [NG]
+  float (*sc)[kKcCH] = reinterpret_cast<float (*)[kKcCH]>(ovB);
+  float (*red)[kGqa][kD] = reinterpret_cast<float (*)[kGqa][kD]>(ovB);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int n = lane & 15, j = lane >> 4;
-  const int c = blockIdx.x, u = blockIdx.y;
+  const int u = blockIdx.y;
   const int b = u / a.Hkv, hk = u % a.Hkv;
-  float* part = a.part + ((size_t)u * a.nch_total + c) * kGqa * kPartF;
   const int nq = a.counters[b * 4 + 1];
-  const int s_begin = c * kKcCH, s_end = min(nq, s_begin + kKcCH);
-  if (s_begin >= s_end) {
-    for (int i = tid; i < kGqa * kPartF; i += 256) part[i] = (i % kPartF == 0) ? -INFINITY : 0.f;
-    return;
-  }
-  // ---- every load of the chunk goes out first
   const BufRes rK = make_res(a.kwords + (size_t)u * a.tiles * 8 * 16, a.tiles * 8 * 16 * 4);
   const BufRes rKM = make_res(a.kmeta + (size_t)u * a.kblocks * kKcKB, a.kblocks * kKcKB * 4);
   const BufRes rS = make_res(a.sparse + (size_t)u * a.cap * a.spv, a.cap * a.spv * 4);
   const BufRes rV = make_res(a.vwords + (size_t)u * a.vrows * kD, a.vrows * kD * 4);
   const BufRes rVM = make_res(a.vmeta + (size_t)u * a.tiles * NG * 16, a.tiles * NG * 16 * 4);
-  const int tile0 = s_begin / 16;
-  uint32_t kw[kKcTW][2], sp[kKcTW];
-#pragma unroll
-  for (int i = 0; i < kKcTW; ++i) {
-    const int t = kKcTW * w + i;
-#pragma unroll
-    for (int x = 0; x < 2; ++x) kw[i][x] = bload(rK, (((tile0 + t) * 8 + j + 4 * x) * 16 + n) * 4u);
-    sp[i] = j < a.spv ? bload(rS, ((uint32_t)(s_begin + 16 * t + n) * a.spv + j) * 4u) : 0u;
-  }
-  uint32_t km[3];
-#pragma unroll
-  for (int k = 0; k < 3; ++k) {
-    const int e = tid + 256 * k;
-    km[k] = e < kKcNB * kKcKB ? bload(rKM, (uint32_t)((s_begin / kKcKB) * kKcKB + e) * 4u) : 0u;
-  }
   constexpr int VMETA = VU / 16 * NG * 16 / 64;            // value meta words per lane
-  uint32_t vw[8][R], vm[VMETA];
-  {
-    const int row0 = (s_begin + VU * w) / NVV + j * R;
+  // every word a lane reads for its chunk (out-of-range offsets read 0)
+  struct Chunk {
+    uint32_t kw[kKcTW][2], sp[kKcTW], km[3], vw[8][R], vm[VMETA];
+  };
+  auto load_chunk = [&](Chunk& d, int c) {
+    const int s0 = c * kKcCH, tile0 = s0 / 16;
+#pragma unroll
+    for (int i = 0; i < kKcTW; ++i) {
+      const int t = kKcTW * w + i;
+#pragma unroll
+      for (int x = 0; x < 2; ++x) d.kw[i][x] = bload(rK, (((tile0 + t) * 8 + j + 4 * x) * 16 + n) * 4u);
+      d.sp[i] = j < a.spv ? bload(rS, ((uint32_t)(s0 + 16 * t + n) * a.spv + j) * 4u) : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const int e = tid + 256 * k;
+      d.km[k] = e < kKcNB * kKcKB ? bload(rKM, (uint32_t)((s0 / kKcKB) * kKcKB + e) * 4u) : 0u;
+    }
+    const int row0 = (s0 + VU * w) / NVV + j * R;
 #pragma unroll
     for (int v = 0; v < 8; ++v)
 #pragma unroll
-      for (int r2 = 0; r2 < R; ++r2) vw[v][r2] = bload(rV, ((row0 + r2) * kD + 16 * v + n) * 4u);
-    const int mt0 = (s_begin + VU * w) / 16;
+      for (int r2 = 0; r2 < R; ++r2) d.vw[v][r2] = bload(rV, ((row0 + r2) * kD + 16 * v + n) * 4u);
+    const int mt0 = (s0 + VU * w) / 16;
 #pragma unroll
-    for (int k = 0; k < VMETA; ++k) vm[k] = bload(rVM, (uint32_t)(mt0 * NG * 16 + lane + 64 * k) * 4u);
+    for (int k = 0; k < VMETA; ++k) d.vm[k] = bload(rVM, (uint32_t)(mt0 * NG * 16 + lane + 64 * k) * 4u);
+  };
+  const int c = blockIdx.x;
+  float* part = a.part + ((size_t)u * a.nch_total + c) * kGqa * kPartF;
+  const int s_begin = c * kKcCH, s_end = min(nq, s_begin + kKcCH);
+  if (s_begin >= s_end) {
+    for (int i = tid; i < kGqa * kPartF; i += 256) part[i] = (i % kPartF == 0) ? -INFINITY : 0.f;
+    return;
   }
-  // ---- set-up: query, digit table, key-scale operand tables
+  // ---- every load of the chunk goes out first, then the set-up
+  Chunk cur;
+  load_chunk(cur, c);
   for (int i = tid; i < kGqa * kD; i += 256)
     qf[i / kD][i % kD] = h2f(a.q[((size_t)b * a.Hkv * kGqa + hk * kGqa) * kD + i]);
   DV::fill(ctab, tid, 256);
+  const auto& kw = cur.kw;
+  const auto& sp = cur.sp;
+  const auto& km = cur.km;
+  const auto& vw = cur.vw;
+  const auto& vm = cur.vm;
 #pragma unroll
   for (int k = 0; k < 3; ++k)
     if (tid + 256 * k < kKcNB * kKcKB) kms[tid + 256 * k] = km[k];
   __syncthreads();
+  // ---- key-scale operand tables of the chunk's five blocks
 #pragma unroll
   for (int k = 0; k < 3; ++k) {
     const int e = tid + 256 * k;
