@@ -78,6 +78,10 @@ __device__ inline BufRes make_res(const void* base, uint32_t bytes) {
 __device__ inline uint32_t bload(BufRes r, uint32_t byte_off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, 0);
 }
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ inline u32x2 bload2(BufRes r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, (int)byte_off, 0, 0);
+}
 
 // Two waves per workgroup, one per load stream (the vector-memory counter is
 // in-order, so each stream is issued in the order it is consumed):
@@ -468,9 +472,10 @@ bool launch_decode_pool(int L, const PoolArgs& a, int G, int nch, int U, void* s
 // groups of 32.  A workgroup (four waves) owns a 640-token chunk: five key
 // blocks, forty key tiles, four value units of 160 slots.
 //   keys:   each wave scores ten 16-token tiles.  The per-channel scale sits
-//           in the A operand: rows 0..3 hold fp16(4 q_h[d] s_d) and rows 4..7
+//           in the A operand: row 2h holds fp16(4 q_h[d] s_d) and row 2h + 1
 //           the fp16 remainder of 4 q_h[d] s_d (exact in fp32), so hi + lo
-//           carries the product to about 2^-22; the digits as fp16 are 1 + c/4,
+//           carries the product to about 2^-22 and both land in one lane of
+//           the result; the digits as fp16 are 1 + c/4,
 //           and sum_d q_h[d] (z_d - 4 s_d) per block is added in fp32, as are
 //           the sparse entries q_h[ch] * value.
 //   softmax over the chunk's 640 scores (wave h: head h), weights 2^6 p as
@@ -535,32 +540,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   const BufRes rV = make_res(a.vwords + (size_t)u * a.vrows * kD, a.vrows * kD * 4);
   const BufRes rVM = make_res(a.vmeta + (size_t)u * a.tiles * NG * 16, a.tiles * NG * 16 * 4);
   constexpr int VMETA = VU / 16 * NG * 16 / 64;            // value meta words per lane
-  // every word a lane reads for its chunk (out-of-range offsets read 0)
+  // every word a lane reads for its chunk (out-of-range offsets read 0), in
+  // the order it is needed: the vector-memory counter is in order
   struct Chunk {
-    uint32_t kw[kKcTW][2], sp[kKcTW], km[3], vw[8][R], vm[VMETA];
+    uint32_t km[3], sp[kKcTW][2], kw[kKcTW][2], vm[VMETA], vw[8][R];
   };
   auto load_chunk = [&](Chunk& d, int c) {
     const int s0 = c * kKcCH, tile0 = s0 / 16;
-#pragma unroll
-    for (int i = 0; i < kKcTW; ++i) {
-      const int t = kKcTW * w + i;
-#pragma unroll
-      for (int x = 0; x < 2; ++x) d.kw[i][x] = bload(rK, (((tile0 + t) * 8 + j + 4 * x) * 16 + n) * 4u);
-      d.sp[i] = j < a.spv ? bload(rS, ((uint32_t)(s0 + 16 * t + n) * a.spv + j) * 4u) : 0u;
-    }
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
       const int e = tid + 256 * k;
       d.km[k] = e < kKcNB * kKcKB ? bload(rKM, (uint32_t)((s0 / kKcKB) * kKcKB + e) * 4u) : 0u;
     }
+    // lanes (n, 0) and (n, 1) score token n: both take its sparse entries
+#pragma unroll
+    for (int i = 0; i < kKcTW; ++i) {
+      const uint32_t tok = (uint32_t)(s0 + 16 * (kKcTW * w + i) + n);
+      d.sp[i][0] = d.sp[i][1] = 0u;
+      if (j < 2) {
+        if (a.spv == 2) {
+          const u32x2 e = bload2(rS, tok * 8u);
+          d.sp[i][0] = e[0];
+          d.sp[i][1] = e[1];
+        } else if (a.spv == 1) {
+          d.sp[i][0] = bload(rS, tok * 4u);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kKcTW; ++i) {
+      const int t = kKcTW * w + i;
+#pragma unroll
+      for (int x = 0; x < 2; ++x) d.kw[i][x] = bload(rK, (((tile0 + t) * 8 + j + 4 * x) * 16 + n) * 4u);
+    }
+    const int mt0 = (s0 + VU * w) / 16;
+#pragma unroll
+    for (int k = 0; k < VMETA; ++k) d.vm[k] = bload(rVM, (uint32_t)(mt0 * NG * 16 + lane + 64 * k) * 4u);
     const int row0 = (s0 + VU * w) / NVV + j * R;
 #pragma unroll
     for (int v = 0; v < 8; ++v)
 #pragma unroll
       for (int r2 = 0; r2 < R; ++r2) d.vw[v][r2] = bload(rV, ((row0 + r2) * kD + 16 * v + n) * 4u);
-    const int mt0 = (s0 + VU * w) / 16;
-#pragma unroll
-    for (int k = 0; k < VMETA; ++k) d.vm[k] = bload(rVM, (uint32_t)(mt0 * NG * 16 + lane + 64 * k) * 4u);
   };
   const int c = blockIdx.x;
   float* part = a.part + ((size_t)u * a.nch_total + c) * kGqa * kPartF;
@@ -569,11 +589,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     for (int i = tid; i < kGqa * kPartF; i += 256) part[i] = (i % kPartF == 0) ? -INFINITY : 0.f;
     return;
   }
-  // ---- every load of the chunk goes out first, then the set-up
+  // ---- the query (two channels a thread), then every load of the chunk
+  static_assert(kGqa * kD == 2 * 256, "one query word per thread");
+  const uint32_t qw =
+      reinterpret_cast<const uint32_t*>(a.q + ((size_t)b * a.Hkv * kGqa + hk * kGqa) * kD)[tid];
   Chunk cur;
   load_chunk(cur, c);
-  for (int i = tid; i < kGqa * kD; i += 256)
-    qf[i / kD][i % kD] = h2f(a.q[((size_t)b * a.Hkv * kGqa + hk * kGqa) * kD + i]);
+  qf[tid / (kD / 2)][2 * (tid % (kD / 2))] = h2f(qw & 0xFFFFu);
+  qf[tid / (kD / 2)][2 * (tid % (kD / 2)) + 1] = h2f(qw >> 16);
   DV::fill(ctab, tid, 256);
   const auto& kw = cur.kw;
   const auto& sp = cur.sp;
@@ -599,8 +622,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       for (int h = 0; h < kGqa; ++h) {
         const float A = 4.0f * qf[h][ch] * sg;             // exact: two 11-bit significands
         const _Float16 hi = (_Float16)A;
-        atab[blk][m][jj][h][i] = hi;
-        atab[blk][m][jj][4 + h][i] = (_Float16)(A - (float)hi);
+        atab[blk][m][jj][2 * h][i] = hi;
+        atab[blk][m][jj][2 * h + 1][i] = (_Float16)(A - (float)hi);
       }
     }
   }
@@ -635,19 +658,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       ak = n < 8 ? *reinterpret_cast<const h8*>(&atab[blk][m][j][n][0]) : (h8){0, 0, 0, 0, 0, 0, 0, 0};
       pr = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, bk, pr, 0, 0, 0);
     }
-    // lane (n, 0): rows 0..3 (hi), lane (n, 1): rows 4..7 (lo); sparse entry j
-    if (j < a.spv) {
-      const int ch = (int)(sp[i] >> 16) & (kD - 1);
-      const float val = h2f(sp[i] & 0xFFFFu);
+    // lane (n, j), j < 2: rows 4j..4j+3 = (hi, lo) of heads 2j and 2j + 1,
+    // plus the token's sparse entries
+    if (j < 2) {
+      float x0 = pr[0] + pr[1], x1 = pr[2] + pr[3];
 #pragma unroll
-      for (int h = 0; h < kGqa; ++h) pr[h] = __builtin_fmaf(qf[h][ch], val, pr[h]);
-    }
-    const int s = s_begin + 16 * t + n;
-#pragma unroll
-    for (int h = 0; h < kGqa; ++h) {
-      const float x = pr[h] + __shfl_xor(pr[h], 16);
-      const float scv = s < s_end ? (x + aoff[blk][h]) * a.c : -INFINITY;
-      if (j == (h >> 1)) sc[h][16 * t + n] = scv;
+      for (int e = 0; e < 2; ++e) {
+        if (e < a.spv) {
+          const int ch = (int)(sp[i][e] >> 16) & (kD - 1);
+          const float val = h2f(sp[i][e] & 0xFFFFu);
+          x0 = __builtin_fmaf(qf[2 * j][ch], val, x0);
+          x1 = __builtin_fmaf(qf[2 * j + 1][ch], val, x1);
+        }
+      }
+      const bool ok = s_begin + 16 * t + n < s_end;
+      sc[2 * j][16 * t + n] = ok ? (x0 + aoff[blk][2 * j]) * a.c : -INFINITY;
+      sc[2 * j + 1][16 * t + n] = ok ? (x1 + aoff[blk][2 * j + 1]) * a.c : -INFINITY;
     }
   }
   __syncthreads();
@@ -738,7 +764,8 @@ bool launch_decode_kchan_mfma(const kvq_layout* L, const uint8_t* cache, const v
                               float* part, int nch0, int nch_total, void* stream) {
   const kvq_config& cf = L->cfg;
   if (cf.k_levels != 4 || cf.v_levels != 3 || cf.v_group != 32 || cf.k_block != kKcKB ||
-      cf.sparse_per_vec > 2 || L->kw[0] != 8 || decode_chunk_kchan(L) != kKcCH)
+      cf.sparse_per_vec > 2 || L->kw[0] != 8 || decode_chunk_kchan(L) != kKcCH ||
+      ((uintptr_t)q & 3) != 0)     // the query is read a word at a time
     return false;
   KchanDecArgs a;
   a.counters = (const int32_t*)(cache + L->counters);

@@ -199,12 +199,14 @@ __device__ inline uint32_t bh(h2v x) { return __builtin_bit_cast(uint32_t, x); }
 // packed fp16 IEEE-2019 minimum / maximum
 __device__ inline uint32_t hmin(uint32_t x, uint32_t y) { return bh(__builtin_elementwise_minimum(hb(x), hb(y))); }
 __device__ inline uint32_t hmax(uint32_t x, uint32_t y) { return bh(__builtin_elementwise_maximum(hb(x), hb(y))); }
-// value of lane (quad base + pattern) via a DPP quad permute
+// value of another lane of the same 16-lane row via a DPP move: a quad
+// permute (CTRL < 0x100) or a row pattern such as the mirrors below
 template <int CTRL>
 __device__ inline uint32_t quad_perm(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
 constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E;    // quad_perm [1,0,3,2], [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141, kRowMirror = 0x140;   // lane i <-> 7 - i (per 8), 15 - i
 template <int O>
 __device__ inline uint32_t quad_bcast(uint32_t v) { return quad_perm<O * 0x55>(v); }
 
@@ -509,7 +511,7 @@ __global__ __launch_bounds__(256) void k_kchan_keys(const uint16_t* __restrict__
 // Data-parallel form of the same block step for grids of 3..8 levels and at
 // most two sparse entries per key vector.  Sixteen lanes per token row (eight
 // channels each, eight rows per lane): the row's largest magnitudes come from
-// a 16-lane butterfly over keys (|x| bits << 16 | 0xFFFF - channel, so ties
+// a 16-lane DPP exchange over keys (|x| bits << 16 | 0xFFFF - channel, so ties
 // go to the lower channel); the owning lane writes each sparse entry and
 // zeroes it.  Per-channel extremes are packed IEEE minimum/maximum (-0 below
 // +0) over the lane's rows, reduced over the row groups in LDS; each channel
@@ -570,13 +572,15 @@ __global__ __launch_bounds__(256) void k_kchan_keys_fast(KchanArgs a) {
         const uint32_t ch = 8 * l16 + i;
         top2_insert(((u4_get16(x[p], i) & 0x7FFFu) << 16) | (0xFFFFu - ch), a1, a2);
       }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        const uint32_t b1 = (uint32_t)__shfl_xor((int)a1, o, 16);
-        const uint32_t b2 = (uint32_t)__shfl_xor((int)a2, o, 16);
+      // merge with the partner's (disjoint) top two: pairs, quads, halves, rows
+      auto merge = [&](uint32_t b1, uint32_t b2) {
         a2 = max(min(a1, b1), max(a2, b2));
         a1 = max(a1, b1);
-      }
+      };
+      merge(quad_perm<kQuadXor1>(a1), quad_perm<kQuadXor1>(a2));
+      merge(quad_perm<kQuadXor2>(a1), quad_perm<kQuadXor2>(a2));
+      merge(quad_perm<kRowHalfMirror>(a1), quad_perm<kRowHalfMirror>(a2));
+      merge(quad_perm<kRowMirror>(a1), quad_perm<kRowMirror>(a2));
       const int c1 = 0xFFFF - (int)(a1 & 0xFFFFu), c2 = 0xFFFF - (int)(a2 & 0xFFFFu);
       const int t = t0 + 16 * p + rg;
       uint32_t* sp = a.sparse + ((size_t)u * a.cap + t) * SPV;
