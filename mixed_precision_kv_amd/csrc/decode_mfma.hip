@@ -655,7 +655,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       h8 bk, ak;
 #pragma unroll
       for (int e = 0; e < 8; ++e) bk[e] = dg[8 * m + e];
-      ak = n < 8 ? *reinterpret_cast<const h8*>(&atab[blk][m][j][n][0]) : (h8){0, 0, 0, 0, 0, 0, 0, 0};
+      // rows 8..15 repeat rows 0..7: they only reach result rows no lane reads
+      ak = *reinterpret_cast<const h8*>(&atab[blk][m][j][n & 7][0]);
       pr = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, bk, pr, 0, 0, 0);
     }
     // lane (n, j), j < 2: rows 4j..4j+3 = (hi, lo) of heads 2j and 2j + 1,
