@@ -254,7 +254,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="time quantize / decode (and append) of every workload; one JSON line each")
-    ap.add_argument("--sweep-only", default="", help="with --sweep: just this workload")
+    ap.add_argument("--sweep-only", default="", help="with --sweep: just these workloads (comma-separated)")
     ap.add_argument("--only", choices=["all", "decode", "quantize", "copy"], default="all",
                     help="profiling aid: run just one kernel family (no JSON line)")
     args = ap.parse_args()
@@ -270,7 +270,7 @@ def main():
     dev = torch.device("cuda:0")
     if args.sweep:
         for cw in synth.CONFIGS:
-            if args.sweep_only and cw.name != args.sweep_only:
+            if args.sweep_only and cw.name not in args.sweep_only.split(","):
                 continue
             print(json.dumps(sweep_one(cw, args, torch, np, kvq, synth, dev)), flush=True)
         return

@@ -15,6 +15,12 @@ typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 
 __device__ inline h2v h2_from_bits(uint32_t b) { return __builtin_bit_cast(h2v, b); }
 
+// (x & m) | c in one instruction (three-input bitwise op, truth table 0xEA
+// for inputs with patterns 0xF0, 0xCC, 0xAA)
+__device__ inline uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(x, m, c, 0xEA);
+}
+
 __host__ __device__ constexpr uint32_t ipow(uint32_t L, int k) {
   uint32_t p = 1;
   for (int i = 0; i < k; ++i) p *= L;
@@ -41,7 +47,7 @@ struct Digits<4, NW> {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const uint32_t s = k <= 4 ? (w[i] << (8 - 2 * k)) : (w[i] >> (2 * k - 8));
-        const h2v v = h2_from_bits((s & 0x03000300u) | 0x3C003C00u);
+        const h2v v = h2_from_bits(and_or(s, 0x03000300u, 0x3C003C00u));
         out[16 * i + 2 * k] = v[0];
         out[16 * i + 2 * k + 1] = v[1];
       }
@@ -67,7 +73,7 @@ struct Digits<8, NW> {
 #pragma unroll
       for (int k = 0; k < 5; ++k) {
         const uint32_t s = k <= 2 ? (x << (7 - 3 * k)) : (x >> (3 * k - 7));
-        const h2v v = h2_from_bits((s & 0x03800380u) | 0x3C003C00u);
+        const h2v v = h2_from_bits(and_or(s, 0x03800380u, 0x3C003C00u));
         out[10 * i + 2 * k] = v[0];
         out[10 * i + 2 * k + 1] = v[1];
       }
