@@ -40,9 +40,17 @@ struct DecodeArgs {
   const uint16_t* kwin;
   const uint16_t* vwin;
   int vL, vnv, vgroup, spv, cap, kblocks, win_cap;
-  int zbase;              // kchan: 1 -> the grid covers the fp16 window only
   int nwch;               // kchan: window chunks of kWinChunk tokens
 };
+
+// sum over the 16 lanes of a DPP row (every lane gets it)
+__device__ inline float row_sum16(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x128, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x124, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x122, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x121, 0xF, 0xF, false));
+  return v;
+}
 
 __device__ inline float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -140,49 +148,61 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_kchan(DecodeArgs a) {
   __shared__ float accs[kGqa * kD];
   __shared__ float sm[kGqa], sl[kGqa];
   const int tid = threadIdx.x;
-  const int c = blockIdx.x, u = blockIdx.y, z = blockIdx.z + a.zbase;
+  const int c = blockIdx.x, u = blockIdx.y, z = blockIdx.z;
   const int b = u / a.Hkv, hk = u % a.Hkv;
   const int nchp = z ? a.nwch : a.nch0;
   if (c >= nchp) return;
   float* part = a.part + ((size_t)u * a.nch_total + (z ? a.nch0 : 0) + c) * kGqa * kPartStride;
-  const int nq = a.counters[b * 4 + 1];
-  const int nwin = a.counters[b * 4 + 2];
-  load_q(a.q, b, hk, a.Hkv, qf);
-  __syncthreads();
   if (z == 1) {
-    // window chunk c: tokens [kWinChunk c, kWinChunk (c + 1)) of the fp16 window
-    const int w0 = c * kWinChunk, nwin_c = min(kWinChunk, nwin - w0);
-    if (nwin_c <= 0) { write_empty(part); return; }
+    // window chunk c: tokens [kWinChunk c, kWinChunk (c + 1)) of the fp16 window.
+    // Every row of the window's capacity is read before the valid count
+    // arrives (rows past it are masked below), then the query
+    const int w0 = c * kWinChunk, ncap = min(kWinChunk, a.win_cap - w0);
     const uint16_t* kwp = a.kwin + ((size_t)u * a.win_cap + w0) * kD;
     const uint16_t* vwp = a.vwin + ((size_t)u * a.win_cap + w0) * kD;
-    // one thread per window token: its row as sixteen 16-byte loads, all in flight
-    for (int i = tid; i < nwin_c; i += kDecThreads) {
-      const uint4* kr = reinterpret_cast<const uint4*>(kwp + (size_t)i * kD);
-      uint4 kv[kD / 8];
+    // scores: sixteen lanes per token (one DPP row), eight channels each
+    static_assert(kWinChunk * 16 == kDecThreads, "one 16-lane row per window token");
+    const int i = tid >> 4, c8 = tid & 15;
+    uint4 kv = make_uint4(0u, 0u, 0u, 0u);
+    if (i < ncap) kv = *reinterpret_cast<const uint4*>(kwp + (size_t)i * kD + 8 * c8);
+    // values: thread (half, d) takes tokens half, half + 2, ...
+    const int d = tid & (kD - 1), half = tid >> 7;
+    uint16_t vr[kWinChunk / 2];
 #pragma unroll
-      for (int c8 = 0; c8 < kD / 8; ++c8) kv[c8] = kr[c8];
+    for (int k = 0; k < kWinChunk / 2; ++k) {
+      const int t = half + 2 * k;
+      vr[k] = t < ncap ? vwp[(size_t)t * kD + d] : (uint16_t)0;
+    }
+    const int nwin_c = min(kWinChunk, a.counters[b * 4 + 2] - w0);
+    if (nwin_c <= 0) { write_empty(part); return; }
+    load_q(a.q, b, hk, a.Hkv, qf);
+    __syncthreads();
+    {
+      const uint32_t wv[4] = {kv.x, kv.y, kv.z, kv.w};
       float sco[kGqa] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c8 = 0; c8 < kD / 8; ++c8) {
-        const uint32_t wv[4] = {kv[c8].x, kv[c8].y, kv[c8].z, kv[c8].w};
+      for (int e = 0; e < 8; ++e) {
+        const float x = h2f(e & 1 ? (wv[e / 2] >> 16) : (wv[e / 2] & 0xFFFFu));
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = h2f(e & 1 ? (wv[e / 2] >> 16) : (wv[e / 2] & 0xFFFFu));
-#pragma unroll
-          for (int hh = 0; hh < kGqa; ++hh) sco[hh] = __builtin_fmaf(qf[hh][8 * c8 + e], x, sco[hh]);
-        }
+        for (int hh = 0; hh < kGqa; ++hh) sco[hh] = __builtin_fmaf(qf[hh][8 * c8 + e], x, sco[hh]);
       }
-      for (int hh = 0; hh < kGqa; ++hh) sc[hh][i] = sco[hh] * a.scale_log2;
+#pragma unroll
+      for (int hh = 0; hh < kGqa; ++hh) {
+        const float t = row_sum16(sco[hh]);
+        if (c8 == 0) sc[hh][i] = i < nwin_c ? t * a.scale_log2 : -INFINITY;
+      }
     }
     __syncthreads();
     chunk_softmax(sc, nwin_c, sm, sl);
     __syncthreads();
-    const int d = tid & (kD - 1), half = tid >> 7;
     float acc[kGqa] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 16
-    for (int i = half; i < nwin_c; i += 2) {
-      const float vv = h2f(vwp[(size_t)i * kD + d]);
-      for (int hh = 0; hh < kGqa; ++hh) acc[hh] = __builtin_fmaf(sc[hh][i], vv, acc[hh]);
+#pragma unroll
+    for (int k = 0; k < kWinChunk / 2; ++k) {
+      const int t = half + 2 * k;
+      if (t < nwin_c) {
+        const float vv = h2f(vr[k]);
+        for (int hh = 0; hh < kGqa; ++hh) acc[hh] = __builtin_fmaf(sc[hh][t], vv, acc[hh]);
+      }
     }
     if (half == 1)
       for (int hh = 0; hh < kGqa; ++hh) red[hh * kD + d] = acc[hh];
@@ -193,6 +213,9 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_kchan(DecodeArgs a) {
     finish_partial(part, sm, sl, accs);
     return;
   }
+  const int nq = a.counters[b * 4 + 1];
+  load_q(a.q, b, hk, a.Hkv, qf);
+  __syncthreads();
   const int CH = a.chunk[0];
   const int s_begin = c * CH, s_end = min(nq, s_begin + CH);
   if (s_begin >= s_end) { write_empty(part); return; }
@@ -392,10 +415,7 @@ bool launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, flo
     a.kwin = (const uint16_t*)(cache + L->k_win);
     a.vwin = (const uint16_t*)(cache + L->v_win);
     if (L->win_cap > 640) return false;
-    if (launch_decode_kchan_mfma(L, cache, q, a.scale_log2, a.part, nch0, nch, stream)) {
-      a.zbase = 1;                            // the window only
-      k_decode_kchan<<<dim3(nch1, U, 1), kDecThreads, 0, s>>>(a);
-    } else {
+    if (!launch_decode_kchan_mfma(L, cache, q, a.scale_log2, a.part, nch0, nch1, nch, stream)) {
       const int gx = nch0 > nch1 ? nch0 : nch1;
       k_decode_kchan<<<dim3(gx, U, 2), kDecThreads, 0, s>>>(a);
     }

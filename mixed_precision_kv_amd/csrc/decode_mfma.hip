@@ -491,11 +491,97 @@ struct KchanDecArgs {
   const uint32_t* sparse;       // [u][cap][spv]
   const uint32_t* vwords;       // [u][row][128]
   const uint32_t* vmeta;        // [u][tile][NG][16]
+  const uint16_t* kwin;         // fp16 window [u][win_cap][128]
+  const uint16_t* vwin;
   int Hkv, tiles, kblocks, vrows, cap, spv, nch_total;
+  int nch0, win_cap;            // quantized chunks per unit; window capacity
   float c;                      // softmax scale * log2(e)
 };
 
 constexpr int kKcCH = 640, kKcKB = 128, kKcNB = kKcCH / kKcKB, kKcTW = kKcCH / 16 / 4;
+
+// Chunk c of the fp16 window (tokens kWinChunk c ..), as extra workgroups of
+// the same launch.  Scores: sixteen lanes per token (one DPP row), eight
+// channels each; values: thread (half, d) takes tokens half, half + 2, ...
+// Rows up to the window's capacity are read before the valid count arrives
+// (rows past it are masked), then the query.  lds: 4 x 16 scores, then
+// 4 x 128 partial sums.
+__device__ inline void kchan_window_chunk(const KchanDecArgs& a, int c, int u, int b, int hk,
+                                          float (*qf)[kD], float* lds, float* hm, float* hl) {
+  static_assert(kWinChunk * 16 == 256, "one 16-lane row per window token");
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  float (*wsc)[kWinChunk] = reinterpret_cast<float (*)[kWinChunk]>(lds);
+  float (*wred)[kD] = reinterpret_cast<float (*)[kD]>(lds + kGqa * kWinChunk);
+  float* part = a.part + ((size_t)u * a.nch_total + a.nch0 + c) * kGqa * kPartF;
+  const int w0 = c * kWinChunk, ncap = min(kWinChunk, a.win_cap - w0);
+  const uint16_t* kwp = a.kwin + ((size_t)u * a.win_cap + w0) * kD;
+  const uint16_t* vwp = a.vwin + ((size_t)u * a.win_cap + w0) * kD;
+  const int i = tid >> 4, c8 = tid & 15;
+  uint4 kv = make_uint4(0u, 0u, 0u, 0u);
+  if (i < ncap) kv = *reinterpret_cast<const uint4*>(kwp + (size_t)i * kD + 8 * c8);
+  const int d = tid & (kD - 1), half = tid >> 7;
+  uint16_t vr[kWinChunk / 2];
+#pragma unroll
+  for (int k = 0; k < kWinChunk / 2; ++k) {
+    const int t = half + 2 * k;
+    vr[k] = t < ncap ? vwp[(size_t)t * kD + d] : (uint16_t)0;
+  }
+  const int nwin_c = min(kWinChunk, a.counters[b * 4 + 2] - w0);
+  if (nwin_c <= 0) {
+    for (int e = tid; e < kGqa * kPartF; e += 256) part[e] = (e % kPartF == 0) ? -INFINITY : 0.f;
+    return;
+  }
+  for (int e = tid; e < kGqa * kD; e += 256)
+    qf[e / kD][e % kD] = h2f(a.q[((size_t)b * a.Hkv * kGqa + hk * kGqa) * kD + e]);
+  __syncthreads();
+  {
+    const uint32_t wv[4] = {kv.x, kv.y, kv.z, kv.w};
+    float sco[kGqa] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = h2f(e & 1 ? (wv[e / 2] >> 16) : (wv[e / 2] & 0xFFFFu));
+#pragma unroll
+      for (int hh = 0; hh < kGqa; ++hh) sco[hh] = __builtin_fmaf(qf[hh][8 * c8 + e], x, sco[hh]);
+    }
+#pragma unroll
+    for (int hh = 0; hh < kGqa; ++hh) {
+      const float t = row_sum16(sco[hh]);
+      if (c8 == 0) wsc[hh][i] = i < nwin_c ? t * a.c : -INFINITY;
+    }
+  }
+  __syncthreads();
+  {
+    // softmax of head w over the chunk: lanes 0..15 of wave w
+    const float x = wsc[w][lane & 15];
+    const float mx = row_max16(x);
+    const float p = __builtin_amdgcn_exp2f(x - mx);
+    const float l = row_sum16(p);
+    if (lane < kWinChunk) wsc[w][lane] = p;
+    if (lane == 0) { hm[w] = mx; hl[w] = l; }
+  }
+  __syncthreads();
+  float acc[kGqa] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < kWinChunk / 2; ++k) {
+    const int t = half + 2 * k;
+    if (t < nwin_c) {
+      const float vv = h2f(vr[k]);
+#pragma unroll
+      for (int hh = 0; hh < kGqa; ++hh) acc[hh] = __builtin_fmaf(wsc[hh][t], vv, acc[hh]);
+    }
+  }
+  if (half == 1)
+#pragma unroll
+    for (int hh = 0; hh < kGqa; ++hh) wred[hh][d] = acc[hh];
+  __syncthreads();
+  if (half == 0)
+#pragma unroll
+    for (int hh = 0; hh < kGqa; ++hh) part[hh * kPartF + 4 + d] = acc[hh] + wred[hh][d];
+  if (tid < kGqa) {
+    part[tid * kPartF + 0] = hm[tid];
+    part[tid * kPartF + 1] = hl[tid];
+  }
+}
 
 template <int VL, int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_decode_kchan_mfma(KchanDecArgs a) {
@@ -533,6 +619,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   const int n = lane & 15, j = lane >> 4;
   const int u = blockIdx.y;
   const int b = u / a.Hkv, hk = u % a.Hkv;
+  if ((int)blockIdx.x >= a.nch0) {
+    kchan_window_chunk(a, blockIdx.x - a.nch0, u, b, hk, qf, reinterpret_cast<float*>(ovB), hm, hl);
+    return;
+  }
   const int nq = a.counters[b * 4 + 1];
   const BufRes rK = make_res(a.kwords + (size_t)u * a.tiles * 8 * 16, a.tiles * 8 * 16 * 4);
   const BufRes rKM = make_res(a.kmeta + (size_t)u * a.kblocks * kKcKB, a.kblocks * kKcKB * 4);
@@ -762,7 +852,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 // is the one above (4-level keys, 3-level values, groups of 32, blocks of
 // 128, at most two sparse entries); false: not this shape.
 bool launch_decode_kchan_mfma(const kvq_layout* L, const uint8_t* cache, const void* q, float c,
-                              float* part, int nch0, int nch_total, void* stream) {
+                              float* part, int nch0, int nwch, int nch_total, void* stream) {
   const kvq_config& cf = L->cfg;
   if (cf.k_levels != 4 || cf.v_levels != 3 || cf.v_group != 32 || cf.k_block != kKcKB ||
       cf.sparse_per_vec > 2 || L->kw[0] != 8 || decode_chunk_kchan(L) != kKcCH ||
@@ -779,9 +869,12 @@ bool launch_decode_kchan_mfma(const kvq_layout* L, const uint8_t* cache, const v
   a.vmeta = (const uint32_t*)(cache + L->v_meta[0]);
   a.Hkv = cf.kv_heads; a.tiles = L->tiles[0]; a.kblocks = L->kblocks; a.vrows = L->vrows[0];
   a.cap = cf.capacity; a.spv = cf.sparse_per_vec; a.nch_total = nch_total;
+  a.kwin = (const uint16_t*)(cache + L->k_win);
+  a.vwin = (const uint16_t*)(cache + L->v_win);
+  a.nch0 = nch0; a.win_cap = L->win_cap;
   a.c = c;
-  if (nch0 > 0)
-    k_decode_kchan_mfma<3, 32><<<dim3(nch0, cf.batch * cf.kv_heads), 256, 0, (hipStream_t)stream>>>(a);
+  if (nch0 + nwch > 0)
+    k_decode_kchan_mfma<3, 32><<<dim3(nch0 + nwch, cf.batch * cf.kv_heads), 256, 0, (hipStream_t)stream>>>(a);
   return true;
 }
 

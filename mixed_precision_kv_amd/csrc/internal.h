@@ -62,9 +62,10 @@ struct PoolArgs {
 // (uses the kernel's occupancy; falls back to 8 macro tiles).
 int decode_pool_chunk(int L, int G, int U, int slots_per_unit);
 bool launch_decode_pool(int L, const PoolArgs& a, int G, int nch, int U, void* stream);
-// Matrix-core decode of the quantized part of a per-channel-key cache;
-// false when the configuration is not the one it is built for.
+// Matrix-core decode of a per-channel-key cache: nch0 quantized chunks and
+// nwch fp16-window chunks per unit in one launch; false when the
+// configuration is not the one it is built for.
 bool launch_decode_kchan_mfma(const kvq_layout* L, const uint8_t* cache, const void* q, float c,
-                              float* part, int nch0, int nch_total, void* stream);
+                              float* part, int nch0, int nwch, int nch_total, void* stream);
 
 }  // namespace kvq
