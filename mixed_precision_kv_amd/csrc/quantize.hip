@@ -635,7 +635,8 @@ __global__ __launch_bounds__(256) void k_kchan_keys_fast(KchanArgs a) {
     float r[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) { m[i] = cmeta[8 * l16 + i]; r[i] = crcp[8 * l16 + i]; }
-    const bool clampq = clamp_any != 0;
+    // the top-level clamp matters only where some scale is subnormal
+    const float top = clamp_any != 0 ? (float)(L - 1) : INFINITY;
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
       const uint32_t w[4] = {x[p].x, x[p].y, x[p].z, x[p].w};
@@ -643,8 +644,7 @@ __global__ __launch_bounds__(256) void k_kchan_keys_fast(KchanArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const h2v zs = hb(m[e]);                       // (s, z)
-        float q = quotient_of(hb(w[e / 2])[e & 1], zs[1], zs[0], r[e], one);
-        if (clampq) q = fminf(q, (float)(L - 1));
+        const float q = fminf(quotient_of(hb(w[e / 2])[e & 1], zs[1], zs[0], r[e], one), top);
         c[e / 4] = __builtin_amdgcn_cvt_pk_u8_f32(q, e & 3, c[e / 4]);
       }
       codes[16 * p + rg][2 * l16] = c[0];
@@ -685,14 +685,24 @@ static bool launch_kchan_keys_fast(const KchanArgs& a, int L, int spv, dim3 grid
   return false;
 }
 
+// Copies the last nwin tokens of every unit into the fp16 window (zeros
+// past them) and, in workgroup (0, 0), sets the per-sequence counters.
 __global__ __launch_bounds__(256) void k_kchan_window(const uint16_t* __restrict__ k,
                                                       const uint16_t* __restrict__ v, int64_t sb,
                                                       int64_t st, int64_t sh, int Hkv, int nq,
                                                       int nwin, int win_cap,
                                                       uint16_t* __restrict__ kwin,
-                                                      uint16_t* __restrict__ vwin) {
+                                                      uint16_t* __restrict__ vwin,
+                                                      int32_t* __restrict__ counters, int B) {
   const int u = blockIdx.y;
   const int b = u / Hkv, h = u % Hkv;
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int s = threadIdx.x; s < B; s += 256) {
+      counters[s * 4 + 0] = nq + nwin;
+      counters[s * 4 + 1] = nq;
+      counters[s * 4 + 2] = nwin;
+      counters[s * 4 + 3] = 0;
+    }
   for (int e = blockIdx.x * 256 + threadIdx.x; e < win_cap * (kD / 8); e += gridDim.x * 256) {
     const int i = e / (kD / 8), c8 = (e % (kD / 8)) * 8;
     uint4 kr = make_uint4(0, 0, 0, 0), vr = make_uint4(0, 0, 0, 0);
@@ -707,16 +717,6 @@ __global__ __launch_bounds__(256) void k_kchan_window(const uint16_t* __restrict
   }
 }
 
-__global__ void k_kchan_counters(int32_t* counters, int B, int T, int nq) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b < B) {
-    counters[b * 4 + 0] = T;
-    counters[b * 4 + 1] = nq;
-    counters[b * 4 + 2] = T - nq;
-    counters[b * 4 + 3] = 0;
-  }
-}
-
 bool launch_quantize_kchan(const kvq_layout* L, uint8_t* cache, const void* k, const void* v,
                            int64_t sb, int64_t st, int64_t sh, int T, void* stream) {
   hipStream_t s = (hipStream_t)stream;
@@ -725,8 +725,6 @@ bool launch_quantize_kchan(const kvq_layout* L, uint8_t* cache, const void* k, c
   const int nq = kchan_nq(L, T);
   const int nwin = T - nq;
   if (nwin > L->win_cap) return false;
-  k_kchan_counters<<<ceil_div(c.batch, 64), 64, 0, s>>>((int32_t*)(cache + L->counters), c.batch,
-                                                        T, nq);
   if (nq > 0) {
     KchanArgs ka;
     ka.k = (const uint16_t*)k;
@@ -756,9 +754,10 @@ bool launch_quantize_kchan(const kvq_layout* L, uint8_t* cache, const void* k, c
   a.vwords = (uint32_t*)(cache + L->v_words[0]);
   a.vmeta = (uint32_t*)(cache + L->v_meta[0]);
   if (!launch_pool(a, c.v_group, U, s)) return false;
-  k_kchan_window<<<dim3(ceil_div(L->win_cap * (kD / 8), 256), U), 256, 0, s>>>(
+  k_kchan_window<<<dim3(std::max(1, ceil_div(L->win_cap * (kD / 8), 256)), U), 256, 0, s>>>(
       (const uint16_t*)k, (const uint16_t*)v, sb, st, sh, c.kv_heads, nq, nwin, L->win_cap,
-      (uint16_t*)(cache + L->k_win), (uint16_t*)(cache + L->v_win));
+      (uint16_t*)(cache + L->k_win), (uint16_t*)(cache + L->v_win),
+      (int32_t*)(cache + L->counters), c.batch);
   return hipGetLastError() == hipSuccess;
 }
 
