@@ -274,6 +274,21 @@ def decode_unit(q_group: np.ndarray, k_hat: np.ndarray, v_hat: np.ndarray, scale
     return attention_fp64(q_group, k_hat, v_hat, scale)
 
 
+def attention_lse_fp64(q: np.ndarray, k_hat: np.ndarray, v_hat: np.ndarray, scale: float):
+    """Attention of a block of query rows over the whole cache, with each
+    row's log-sum-exp, fp64: the cached history of one KV head read by several
+    new query tokens at once (a multi-turn continuation re-reading the cache,
+    [SemKV] Abstract).  Rows are independent; no mask, since every cached
+    token precedes the new ones.  q [R][D] -> (o [R][D], lse [R]) with
+    lse = ln sum_t exp(scale q . k^_t), so that a caller can merge o with
+    attention over the new tokens themselves."""
+    s = (q.astype(F64) @ k_hat.astype(F64).T) * F64(scale)   # [R][N]
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    l = p.sum(axis=1, keepdims=True)
+    return (p @ v_hat.astype(F64)) / l, (m + np.log(l))[:, 0]
+
+
 def row_rel_err(o: np.ndarray, r: np.ndarray) -> float:
     """Error measure for attention outputs: max over rows of
     max|o - r| / max|r| (rows are the last-but-one axis)."""

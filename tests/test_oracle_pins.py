@@ -295,6 +295,39 @@ def test_attention_brute_force_and_closed_forms():
     assert np.allclose(O.attention_fp64(q[:1], k2, v, 1.0)[0], v[4], atol=1e-9)
 
 
+def test_attention_lse_brute_force_and_closed_forms():
+    rng = np.random.default_rng(22)
+    R, N, D = 6, 11, 16
+    q = rng.standard_normal((R, D))
+    k = rng.standard_normal((N, D))
+    v = rng.standard_normal((N, D))
+    o, lse = O.attention_lse_fp64(q, k, v, 0.3)
+    # the output rows are plain attention, row by row
+    assert np.allclose(o, _naive_attention(q, k, v, 0.3), rtol=1e-12, atol=1e-13)
+    # log-sum-exp by brute force: pure-Python sum of exponentials, no shift
+    for r in range(R):
+        sc = [0.3 * math.fsum(float(q[r, d]) * float(k[t, d]) for d in range(D)) for t in range(N)]
+        assert abs(lse[r] - math.log(math.fsum(math.exp(x) for x in sc))) < 1e-12
+    # identical keys: lse = score + ln N and the output is the mean value
+    kk = np.repeat(k[:1], N, 0)
+    o2, lse2 = O.attention_lse_fp64(q, kk, v, 0.3)
+    assert np.allclose(lse2, 0.3 * (q @ k[0]) + math.log(N), atol=1e-13)
+    assert np.allclose(o2, np.repeat(v.mean(0, keepdims=True), R, 0), atol=1e-14)
+    # one token: lse is its score, the output its value
+    o3, lse3 = O.attention_lse_fp64(q, k[:1], v[:1], 0.3)
+    assert np.allclose(lse3, 0.3 * (q @ k[0]), atol=1e-14)
+    assert np.allclose(o3, np.repeat(v[:1], R, 0), atol=1e-15)
+    # huge scores do not overflow (the shift by the row maximum)
+    o4, lse4 = O.attention_lse_fp64(q * 1e3, k, v, 1.0)
+    assert np.all(np.isfinite(lse4)) and np.all(np.isfinite(o4))
+    # splitting the keys in two and merging by log-sum-exp gives the whole
+    oa, la = O.attention_lse_fp64(q, k[:5], v[:5], 0.3)
+    ob, lb = O.attention_lse_fp64(q, k[5:], v[5:], 0.3)
+    lm = np.logaddexp(la, lb)
+    om = oa * np.exp(la - lm)[:, None] + ob * np.exp(lb - lm)[:, None]
+    assert np.allclose(lm, lse, atol=1e-13) and np.allclose(om, o, atol=1e-13)
+
+
 def test_row_rel_err_definition():
     r = np.array([[1.0, -2.0, 0.5]])
     o = np.array([[1.0, -2.002, 0.5]])
