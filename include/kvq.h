@@ -209,6 +209,28 @@ kvq_status kvq_decode_attn(const kvq_layout* lay, const void* cache,
                            const void* q, float softmax_scale, int32_t max_len,
                            void* out, void* ws, size_t ws_bytes, void* stream);
 
+/* Workspace bytes of kvq_decode_attn_multi for n_queries query tokens per
+ * sequence and sequences of at most max_len tokens; 0 on bad arguments. */
+size_t kvq_multi_workspace_bytes(const kvq_layout* lay, int32_t n_queries, int32_t max_len);
+
+/* Attention of a block of new query tokens per sequence over the whole packed
+ * cache: the quantized history read again when a conversation continues
+ * (SemKV, Abstract: the cache reappears across turns).  Every query row reads
+ * every cached token (no mask: the cache precedes the new tokens); rows are
+ * independent.  Four query tokens share each expansion of the packed words
+ * on the matrix cores.  Tiered mode only.
+ *   q:         device fp16 [B][n_queries][Hq][D].
+ *   n_queries: 1 .. 4096.
+ *   out:       device fp16 [B][n_queries][Hq][D] (round to nearest even).
+ *   lse:       device fp32 [B][n_queries][Hq] or NULL: ln sum_t exp(scale q.k^_t)
+ *              of each row, for merging with attention over the new tokens.
+ *   ws:        device workspace >= kvq_multi_workspace_bytes(lay, n_queries, max_len).
+ * Returns KVQ_ERR_UNSUPPORTED for the per-channel-key mode. */
+kvq_status kvq_decode_attn_multi(const kvq_layout* lay, const void* cache,
+                                 const void* q, int32_t n_queries, float softmax_scale,
+                                 int32_t max_len, void* out, float* lse,
+                                 void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

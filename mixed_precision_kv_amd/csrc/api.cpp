@@ -204,3 +204,31 @@ extern "C" kvq_status kvq_decode_attn(const kvq_layout* lay, const void* cache, 
     return KVQ_ERR_LAUNCH;
   return KVQ_OK;
 }
+
+extern "C" size_t kvq_multi_workspace_bytes(const kvq_layout* lay, int32_t n_queries,
+                                            int32_t max_len) {
+  if (!lay || n_queries < 1 || n_queries > 4096 || max_len < 1 || max_len > lay->cfg.capacity)
+    return 0;
+  if (lay->cfg.mode != KVQ_MODE_TIERED) return 0;
+  return decode_mq_ws_bytes(lay, n_queries, max_len);
+}
+
+extern "C" kvq_status kvq_decode_attn_multi(const kvq_layout* lay, const void* cache, const void* q,
+                                            int32_t n_queries, float softmax_scale, int32_t max_len,
+                                            void* out, float* lse, void* ws, size_t ws_bytes,
+                                            void* stream) {
+  if (!lay || !cache || !q || !out) return KVQ_ERR_ARG;
+  if (!aligned16(cache) || !aligned16(q) || !aligned16(out)) return KVQ_ERR_ARG;
+  if (lse && ((uintptr_t)lse & 3u)) return KVQ_ERR_ARG;
+  if (n_queries < 1 || n_queries > 4096) return KVQ_ERR_ARG;
+  if (!(softmax_scale > 0.0f) || softmax_scale > 1e30f) return KVQ_ERR_ARG;
+  if (max_len < 1) return KVQ_ERR_ARG;
+  if (max_len > lay->cfg.capacity) return KVQ_ERR_CAPACITY;
+  if (lay->cfg.mode != KVQ_MODE_TIERED) return KVQ_ERR_UNSUPPORTED;
+  size_t need = kvq_multi_workspace_bytes(lay, n_queries, max_len);
+  if (!ws || !aligned16(ws) || ws_bytes < need) return KVQ_ERR_WORKSPACE;
+  if (!launch_decode_mq(lay, (const uint8_t*)cache, q, n_queries, softmax_scale, max_len, out, lse,
+                        (uint8_t*)ws, stream))
+    return KVQ_ERR_LAUNCH;
+  return KVQ_OK;
+}

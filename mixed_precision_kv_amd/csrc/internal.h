@@ -62,6 +62,24 @@ struct PoolArgs {
 // (uses the kernel's occupancy; falls back to 8 macro tiles).
 int decode_pool_chunk(int L, int G, int U, int slots_per_unit);
 bool launch_decode_pool(int L, const PoolArgs& a, int G, int nch, int U, void* stream);
+// One tier pool of the multi-query kernel: four query tokens per workgroup.
+struct PoolMqArgs {
+  const int32_t* counters;
+  const uint16_t* q;            // [B][M][Hq][D]
+  float* part;                  // [unit][query group][chunk][16 rows][4 + D]
+  const uint32_t* kwords;
+  const uint32_t* kmeta;
+  const uint32_t* vwords;
+  const uint32_t* vmeta;
+  int pool, Hkv, M, nqg, tiles, vrows, nch_total, part_off;
+  int chunk;          // slots per workgroup (a whole number of macro tiles)
+  float c;            // softmax scale * log2(e)
+};
+// Attention of M query tokens per sequence over a tiered cache (output and
+// log-sum-exp); false when a launch failed or the mode is not tiered.
+bool launch_decode_mq(const kvq_layout* L, const uint8_t* cache, const void* q, int M, float scale,
+                      int max_len, void* out, float* lse, uint8_t* ws, void* stream);
+size_t decode_mq_ws_bytes(const kvq_layout* L, int M, int max_len);
 // Matrix-core decode of a per-channel-key cache: nch0 quantized chunks and
 // nwch fp16-window chunks per unit in one launch; false when the
 // configuration is not the one it is built for.

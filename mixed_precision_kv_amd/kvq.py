@@ -72,6 +72,11 @@ def lib() -> ctypes.CDLL:
         L.kvq_decode_attn.argtypes = [cp(KvqLayout), vp, vp, ctypes.c_float, _i32, vp, vp,
                                       ctypes.c_size_t, vp]
         L.kvq_decode_attn.restype = ctypes.c_int
+        L.kvq_multi_workspace_bytes.argtypes = [cp(KvqLayout), _i32, _i32]
+        L.kvq_multi_workspace_bytes.restype = ctypes.c_size_t
+        L.kvq_decode_attn_multi.argtypes = [cp(KvqLayout), vp, vp, _i32, ctypes.c_float, _i32, vp, vp,
+                                            vp, ctypes.c_size_t, vp]
+        L.kvq_decode_attn_multi.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -150,3 +155,17 @@ def decode_attn(lay, cache, q, scale, max_len, out, ws, ws_bytes=None, stream=No
     st = lib().kvq_decode_attn(ctypes.byref(lay), _ptr(cache), _ptr(q), float(scale), max_len,
                                _ptr(out), _ptr(ws), ws_bytes, _stream(stream))
     _check(st, "kvq_decode_attn")
+
+
+def multi_workspace_bytes(lay: KvqLayout, n_queries: int, max_len: int) -> int:
+    return int(lib().kvq_multi_workspace_bytes(ctypes.byref(lay), n_queries, max_len))
+
+
+def decode_attn_multi(lay, cache, q, n_queries, scale, max_len, out, lse, ws, ws_bytes=None,
+                      stream=None):
+    if ws_bytes is None:
+        ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = lib().kvq_decode_attn_multi(ctypes.byref(lay), _ptr(cache), _ptr(q), n_queries, float(scale),
+                                     max_len, _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
+                                     _stream(stream))
+    _check(st, "kvq_decode_attn_multi")

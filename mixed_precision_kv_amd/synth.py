@@ -164,3 +164,11 @@ def make_inputs(w: Workload, steps: Optional[int] = None) -> Inputs:
         st.append(dict(k_new=_draw_f16(c[0], (B, H, D)), v_new=_draw_f16(c[1], (B, H, D)),
                        score_new=_draw_scores(c[2], (B,), 1.0), q=_draw_f16(c[3], (B, Hq, D))))
     return Inputs(k=k, v=v, scores=scores, q=q, steps=st)
+
+
+def make_queries(w: Workload, n_queries: int, seed: int = 1) -> np.ndarray:
+    """A block of new query tokens per sequence, fp16 N(0,1) [B][M][Hq][D]
+    (the next turn's tokens reading the cache); a stream of its own, so the
+    cache inputs of the workload are unchanged."""
+    ss = np.random.SeedSequence([w.seed, 1000 + seed])
+    return _draw_f16(ss, (w.batch, n_queries, w.q_heads, w.head_dim))

@@ -25,7 +25,8 @@ def declared_symbols():
 def test_exports_every_declared_symbol():
     names = declared_symbols()
     assert {"kvq_layout_init", "kvq_workspace_bytes", "kvq_status_str", "kvq_quantize",
-            "kvq_append", "kvq_decode_attn"} <= set(names)
+            "kvq_append", "kvq_decode_attn", "kvq_multi_workspace_bytes",
+            "kvq_decode_attn_multi"} <= set(names)
     L = kvq.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -157,6 +158,36 @@ def test_decode_validation(over, status):
         kvq.decode_attn(lay, a["cache"], a["q"], a["scale"], a["max_len"], a["out"], a["ws"],
                         ws_bytes=a["ws_bytes"], stream=0)
     assert e.value.status == status
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(cache=0), 1), (dict(q=FAKE + 2), 1), (dict(out=0), 1), (dict(lse=FAKE + 2), 1),
+    (dict(n_queries=0), 1), (dict(n_queries=4097), 1), (dict(scale=-1.0), 1),
+    (dict(max_len=0), 1), (dict(max_len=4097), 3), (dict(ws=0), 4), (dict(ws_bytes=64), 4),
+])
+def test_decode_multi_validation(over, status):
+    lay = kvq.layout_init(_cfg())
+    a = dict(cache=FAKE, q=FAKE, n_queries=8, scale=0.088, max_len=4096, out=FAKE, lse=None,
+             ws=FAKE, ws_bytes=1 << 40)
+    a.update(over)
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.decode_attn_multi(lay, a["cache"], a["q"], a["n_queries"], a["scale"], a["max_len"],
+                              a["out"], a["lse"], a["ws"], ws_bytes=a["ws_bytes"], stream=0)
+    assert e.value.status == status
+
+
+def test_decode_multi_workspace_and_mode():
+    lay = kvq.layout_init(_cfg())
+    one = kvq.multi_workspace_bytes(lay, 4, 4096)
+    assert one > 0 and kvq.multi_workspace_bytes(lay, 5, 4096) == 2 * one   # four queries a group
+    assert kvq.multi_workspace_bytes(lay, 0, 4096) == 0
+    assert kvq.multi_workspace_bytes(lay, 4, 4097) == 0
+    lay5 = kvq.layout_init(kvq.config_for(synth.CONFIGS[4]))
+    assert kvq.multi_workspace_bytes(lay5, 4, 1024) == 0
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.decode_attn_multi(lay5, FAKE, FAKE, 4, 0.088, 1024, FAKE, None, FAKE, ws_bytes=1 << 40,
+                              stream=0)
+    assert e.value.status == 2
 
 
 def test_status_strings():
