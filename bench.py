@@ -29,7 +29,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-DECODE_SOURCES = ("decode.hip", "decode_mfma.hip", "unpack.h", "digits.h", "tiling.h", "common.h", "internal.h")
+MFMA_F16_PEAK_TFLOPS = 2500.0      # dense fp16 matrix-core peak
+DECODE_SOURCES = ("decode.hip", "decode_mfma.hip", "mfma_util.h", "unpack.h", "digits.h", "tiling.h",
+                  "common.h", "internal.h")
 QUANTIZE_SOURCES = ("quantize.hip", "rank.hip", "digits.h", "tiling.h", "common.h", "internal.h")
 
 
@@ -206,6 +208,28 @@ def sweep_one(w, args, torch, np, kvq, synth, dev):
                       "frac_hbm": round(dec_bytes / (d_ms[0] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                       "ctx_tokens_per_s_per_qhead": w.batch * w.q_heads * w.tokens / (d_ms[0] * 1e-3),
                       "replicas": R}}
+    if tiered and args.multi_queries > 0:
+        # a block of M new query tokens per sequence over the same caches
+        M = args.multi_queries
+        qm = torch.from_numpy(synth.make_queries(w, M)).to(dev)
+        om = torch.empty_like(qm)
+        lse = torch.empty((w.batch, M, w.q_heads), dtype=torch.float32, device=dev)
+        wsm = torch.empty(max(1, kvq.multi_workspace_bytes(lay, M, max_len)), dtype=torch.uint8, device=dev)
+
+        def multi(i):
+            kvq.decode_attn_multi(lay, caches[i % R], qm, M, scale, max_len, om, lse, wsm, stream=stream)
+
+        for i in range(3):
+            multi(i)
+        m_ms = _timed(torch, stream, multi, 20)
+        m_bytes = dec_bytes + 2 * w.batch * M * w.q_heads * w.head_dim * 2 - 2 * w.batch * w.q_heads * w.head_dim * 2
+        m_flop = 2048.0 * M * w.batch * w.kv_heads * w.tokens
+        res["multi_query"] = {"queries": M, "ms": m_ms[0], "ms_p10": m_ms[1], "ms_p90": m_ms[2],
+                              "bytes": m_bytes, "gbs": round(m_bytes / (m_ms[0] * 1e-3) / 1e9, 1),
+                              "frac_hbm": round(m_bytes / (m_ms[0] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                              "tflops": round(m_flop / (m_ms[0] * 1e-3) / 1e12, 2),
+                              "frac_fp16_mfma": round(m_flop / (m_ms[0] * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+                              "ctx_tokens_per_s_per_qhead": M * w.batch * w.q_heads * w.tokens / (m_ms[0] * 1e-3)}
     if w.append_steps:
         # generation: each step appends one token per sequence, then decodes
         quantize(0)
@@ -255,6 +279,9 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="time quantize / decode (and append) of every workload; one JSON line each")
     ap.add_argument("--sweep-only", default="", help="with --sweep: just these workloads (comma-separated)")
+    ap.add_argument("--multi-queries", type=int, default=16,
+                    help="with --sweep: also time attention of this many new query tokens per "
+                         "sequence over each tiered cache (0: skip)")
     ap.add_argument("--only", choices=["all", "decode", "quantize", "copy"], default="all",
                     help="profiling aid: run just one kernel family (no JSON line)")
     args = ap.parse_args()

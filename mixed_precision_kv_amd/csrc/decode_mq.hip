@@ -372,8 +372,11 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
 }
 
 // Log-sum-exp merge over every chunk of both pools: workgroup = (unit,
-// query group, row), thread = channel.  Output fp16 [B][M][Hq][D]; lse
-// (natural log, scores scaled) [B][M][Hq] when given.
+// query group, row), thread = channel.  Chunks are read kMqBatch at a time
+// (one memory round trip per batch) into a running maximum, rescaling what
+// has been summed when it grows.  Output fp16 [B][M][Hq][D]; lse (natural
+// log, scores scaled) [B][M][Hq] when given.
+constexpr int kMqBatch = 8;
 __global__ __launch_bounds__(kD) void k_merge_mq(const float* __restrict__ part, uint16_t* __restrict__ out,
                                                 float* __restrict__ lse, int nch, int nqg, int M, int Hkv) {
   const int row = blockIdx.x, r = row % kMqR, ug = row / kMqR;
@@ -383,15 +386,31 @@ __global__ __launch_bounds__(kD) void k_merge_mq(const float* __restrict__ part,
   const int h = r & 3, b = u / Hkv, hk = u % Hkv, d = threadIdx.x;
   const float* base = part + (size_t)ug * nch * kMqR * kPartF + r * kPartF;
   constexpr int kStep = kMqR * kPartF;
-  float mx = -INFINITY;
-  for (int c = 0; c < nch; ++c) mx = fmaxf(mx, base[(size_t)c * kStep]);
-  float l = 0.f, acc = 0.f;
-  for (int c = 0; c < nch; ++c) {
-    const float mc = base[(size_t)c * kStep];
-    if (mc == -INFINITY) continue;
-    const float w = __builtin_amdgcn_exp2f(mc - mx);
-    l = __builtin_fmaf(w, base[(size_t)c * kStep + 1], l);
-    acc = __builtin_fmaf(w, base[(size_t)c * kStep + 4 + d], acc);
+  float mx = -INFINITY, l = 0.f, acc = 0.f;
+  for (int c0 = 0; c0 < nch; c0 += kMqBatch) {
+    float mc[kMqBatch], lc[kMqBatch], ac[kMqBatch];
+#pragma unroll
+    for (int k = 0; k < kMqBatch; ++k) {
+      const bool ok = c0 + k < nch;
+      const float* p = base + (size_t)(ok ? c0 + k : c0) * kStep;
+      mc[k] = ok ? p[0] : -INFINITY;
+      lc[k] = ok ? p[1] : 0.f;
+      ac[k] = ok ? p[4 + d] : 0.f;
+    }
+    float bm = mx;
+#pragma unroll
+    for (int k = 0; k < kMqBatch; ++k) bm = fmaxf(bm, mc[k]);
+    if (bm == -INFINITY) continue;
+    const float f = __builtin_amdgcn_exp2f(mx - bm);      // 0 while nothing has been summed
+    l *= f;
+    acc *= f;
+#pragma unroll
+    for (int k = 0; k < kMqBatch; ++k) {
+      const float w = __builtin_amdgcn_exp2f(mc[k] - bm);  // 0 for empty chunks
+      l = __builtin_fmaf(w, lc[k], l);
+      acc = __builtin_fmaf(w, ac[k], acc);
+    }
+    mx = bm;
   }
   const size_t o = ((size_t)b * M + m) * Hkv * kGqa + hk * kGqa + h;
   out[o * kD + d] = (uint16_t)f2h_rne(acc / l);

@@ -62,6 +62,20 @@ class GpuRun:
         torch.cuda.synchronize()
         return out.cpu().numpy()
 
+    def decode_multi(self, qm, max_len=None):
+        """Attention of a block of query tokens qm [B][M][Hq][D] -> (out, lse)."""
+        import torch
+        M = qm.shape[1]
+        ws = torch.empty(kvq.multi_workspace_bytes(self.lay, M, self.w.capacity), dtype=torch.uint8,
+                         device=dev())
+        q = to_dev(qm)
+        out = torch.empty_like(q)
+        lse = torch.empty((self.w.batch, M, self.w.q_heads), dtype=torch.float32, device=dev())
+        kvq.decode_attn_multi(self.lay, self.cache, q, M, float(self.scale), max_len or self.w.tokens,
+                              out, lse, ws)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), lse.cpu().numpy()
+
     def append(self, step):
         import torch
         kvq.append(self.lay, self.cache, to_dev(step["k_new"]), to_dev(step["v_new"]),

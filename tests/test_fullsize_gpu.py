@@ -44,7 +44,13 @@ def test_tiered_fullsize(idx):
     assert np.array_equal(LV.sorted_scores(buf, run.lay)[:, :w.tokens], np.sort(inp.scores, axis=1))
     out = run.decode(inp.q)
     _bounded(out, inp.v)
-    errs = []
+    # a block of 16 new query tokens, in the bench's launch configuration
+    M = 16
+    qm = synth.make_queries(w, M)
+    outm, lsem = run.decode_multi(qm)
+    _bounded(outm, inp.v)
+    assert np.all(np.isfinite(lsem))
+    errs, merrs, lerrs = [], [], []
     for u in _sample_units(w):
         b, h = divmod(u, w.kv_heads)
         pools = O.quantize_tiered_unit(inp.k[b, :, h], inp.v[b, :, h], inv[b], w.levels_hi,
@@ -54,8 +60,15 @@ def test_tiered_fullsize(idx):
         vh = np.concatenate([pools[0].v_hat(), pools[1].v_hat()])
         ref = oracle_unit_attention(w, inp.q, b, h, kh, vh, run.scale)
         errs.append(O.row_rel_err(out[b, h * 4:(h + 1) * 4], ref))
-    log(f"{w.name}: sampled units {_sample_units(w)} max row rel err {max(errs):.3e}")
+        rows = qm[b, :, h * 4:(h + 1) * 4].reshape(M * 4, -1).astype(np.float64)
+        mref, lref = O.attention_lse_fp64(rows, kh, vh, float(run.scale))
+        merrs.append(O.row_rel_err(outm[b, :, h * 4:(h + 1) * 4].reshape(M * 4, -1), mref))
+        lerrs.append(float(np.abs(lsem[b, :, h * 4:(h + 1) * 4].reshape(-1) - lref).max()))
+    log(f"{w.name}: sampled units {_sample_units(w)} max row rel err {max(errs):.3e}; "
+        f"{M} queries: {max(merrs):.3e}, lse {max(lerrs):.3e}")
     assert max(errs) <= TOL
+    assert max(merrs) <= TOL
+    assert max(lerrs) <= 1e-4
 
 
 def test_append_fullsize():
