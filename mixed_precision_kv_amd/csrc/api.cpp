@@ -39,9 +39,8 @@ QuantWs quant_ws_plan(const kvq_layout* L, int T) {
     const int64_t nblk = ceil_div(T, kSortTile);
     const int64_t ld = (T + 3) & ~3;   // rows of sorted keys stay 16-byte aligned
     for (int i = 0; i < 2; ++i) { p.keys[i] = off; off = align256(off + B * ld * 4); }
-    for (int i = 0; i < 2; ++i) { p.idx[i] = off; off = align256(off + B * ld * 4); }
-    p.hist = off;   off = align256(off + B * 4 * 256 * nblk * 4);   // 4 digit positions
-    p.segcnt = off; off = align256(off + B * nblk * 4);   // high-tier count per block / segment
+    p.idx = off;    off = align256(off + B * ld * 4);
+    p.segcnt = off; off = align256(off + B * nblk * 4);   // high-tier count per 1024 tokens
     p.ranks = off;  off = align256(off + B * T * 4);
     for (int i = 0; i < 2; ++i) { p.inv[i] = off; off = align256(off + B * (int64_t)L->cap[i] * 4); }
   }

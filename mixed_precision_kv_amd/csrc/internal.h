@@ -8,7 +8,6 @@
 namespace kvq {
 
 constexpr int kSortTile = 1024;   // keys per radix-sort block (256 threads x 4)
-constexpr int kSlotSeg = 1024;    // tokens per slot-scan workgroup
 constexpr int kMaxSortLen = 1 << 18;   // longest ranked sequence (tokens)
 constexpr int kMergeMaxT = 32768;      // up to this length: block sort + merge rank (keys in LDS)
 
@@ -28,7 +27,7 @@ inline int kchan_nq(const kvq_layout* L, int T) {
 int decode_chunks(const kvq_layout* L, int max_len, int* nch0, int* nch1);
 
 struct QuantWs {           // byte offsets inside the quantize workspace
-  size_t keys[2], idx[2], hist, segcnt, ranks, inv[2], total;
+  size_t keys[2], idx, segcnt, ranks, inv[2], total;   // keys[1]: partial counts (long sequences)
 };
 QuantWs quant_ws_plan(const kvq_layout* L, int T);
 

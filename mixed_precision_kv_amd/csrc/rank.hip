@@ -4,24 +4,19 @@
 //
 // Rank = position in the stable descending order of the fp32 score, i.e. the
 // ascending order of an order-preserving u32 key with ties in token order.
-// Sequences of up to kMergeMaxT tokens: each block of kSortTile tokens is
-// sorted in LDS (4 stable passes of 8 bits), then each sorted element's rank
-// is its position in its own block plus, for every other block, the number
-// of that block's keys that precede it (binary search over the sequence's
-// sorted keys, all held in one workgroup's LDS): keys that are smaller, and
-// equal keys of earlier blocks.  Longer sequences: a least-significant-digit
-// radix sort over the whole sequence (4 passes of 8 bits, per-(digit, block)
-// counts -> stable scatter, each block deriving its own output offsets from
-// the counts; wave ballots give each element its rank among equal digits of
-// its wave).  Slots (index among same-tier tokens in token order) come from
-// one scan per sequence.
+// Each block of kBlkSort tokens is sorted in LDS (4 stable passes of 8
+// bits); each sorted element's rank is then its position in its own block
+// plus, for every other block, the number of that block's keys that precede
+// it: keys that are smaller, and equal keys of earlier blocks (branch-free
+// binary searches over sorted keys held in LDS).  Up to kMergeMaxT tokens all
+// of a sequence's sorted keys fit one workgroup's LDS; longer sequences take
+// the other blocks kMergeBlocks at a time and add partial counts.  Slots
+// (index among same-tier tokens in token order) come from one scan per
+// sequence.
 #include "common.h"
 #include "internal.h"
 
 namespace kvq {
-
-constexpr int kSortThreads = 256;
-constexpr int kSortItems = kSortTile / kSortThreads;   // 4, striped
 
 // Workgroups are handed to the 8 XCDs round-robin by linear id, and each XCD
 // has its own L2.  The sort kernels run on a 1-D grid of X * ceil(B / X) *
@@ -41,158 +36,6 @@ __device__ inline bool seq_block(int nblk, int B, int& b, int& blk) {
 static inline dim3 seq_grid(int nblk, int B) {
   const int X = seq_group(B);
   return dim3(X * ((B + X - 1) / X) * nblk);
-}
-
-// hist layout: [b][pass][blk][digit].  The first kernel forms the keys and
-// the pass-0 counts, and zeroes the per-segment counts of high-tier tokens
-// (filled by the last scatter).
-__global__ __launch_bounds__(256) void k_rank_keys(const float* __restrict__ scores,
-                                                   uint32_t* __restrict__ keys,
-                                                   uint32_t* __restrict__ hist,
-                                                   uint32_t* __restrict__ segcnt, int T, int nblk,
-                                                   int nseg, int B) {
-  __shared__ uint32_t h[256];
-  const int tid = threadIdx.x;
-  int b, blk;
-  if (!seq_block(nblk, B, b, blk)) return;
-  h[tid] = 0;
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < kSortItems; ++j) {
-    const int i = blk * kSortTile + j * kSortThreads + tid;
-    if (i < T) {
-      const uint32_t key = score_desc_key(scores[(size_t)b * T + i]);
-      keys[(size_t)b * T + i] = key;
-      atomicAdd(&h[key & 255u], 1u);
-    }
-  }
-  __syncthreads();
-  hist[(((size_t)b * 4 + 0) * nblk + blk) * 256 + tid] = h[tid];
-  if (blk == 0)
-    for (int k = tid; k < nseg; k += 256) segcnt[(size_t)b * nseg + k] = 0u;
-}
-
-// Per-block counts of one pass's digit in the current key order.
-__global__ __launch_bounds__(256) void k_rank_count(const uint32_t* __restrict__ keys,
-                                                    uint32_t* __restrict__ hist, int T, int nblk,
-                                                    int pass, int B) {
-  __shared__ uint32_t h[256];
-  const int tid = threadIdx.x;
-  int b, blk;
-  if (!seq_block(nblk, B, b, blk)) return;
-  h[tid] = 0;
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < kSortItems; ++j) {
-    const int i = blk * kSortTile + j * kSortThreads + tid;
-    if (i < T) atomicAdd(&h[(keys[(size_t)b * T + i] >> (8 * pass)) & 255u], 1u);
-  }
-  __syncthreads();
-  hist[(((size_t)b * 4 + pass) * nblk + blk) * 256 + tid] = h[tid];
-}
-
-struct ScatterArgs {
-  const uint32_t* kin;
-  const uint32_t* iin;          // null: the token index itself (first pass)
-  uint32_t* kout;
-  uint32_t* iout;
-  const uint32_t* hist;         // this pass's offsets
-  int T, nblk, pass;
-  // last pass: ranks, the ascending score array, high-tier counts per segment
-  const float* scores;
-  int32_t* ranks;
-  int32_t* ranks_out;
-  float* sorted_asc;
-  uint32_t* segcnt;
-  int cap, n_hi, nseg, B;
-};
-
-// One pass of the stable LSD sort.
-constexpr int kCountBatch = 32;              // block counts per thread per round trip
-__global__ __launch_bounds__(256) void k_rank_scatter(ScatterArgs a) {
-  __shared__ uint32_t goff[256];
-  __shared__ uint32_t cnt[4][256];
-  __shared__ uint32_t run[256];
-  __shared__ uint32_t segl[kMaxSortLen / kSlotSeg];   // last pass: high-tier tokens per segment
-  const int tid = threadIdx.x;
-  int b, blk;
-  if (!seq_block(a.nblk, a.B, b, blk)) return;
-  const int lane = tid & 63, w = tid >> 6;
-  const int shift = 8 * a.pass;
-  const bool last = a.pass == 3;
-  {
-    // output offset of (digit tid, this block) = keys with a smaller digit +
-    // keys with this digit in earlier blocks (counts read kCountBatch blocks per trip)
-    const uint32_t* hp = a.hist + ((size_t)b * 4 + a.pass) * a.nblk * 256;
-    uint32_t before = 0, total = 0;
-    for (int j0 = 0; j0 < a.nblk; j0 += kCountBatch) {
-      uint32_t c[kCountBatch];
-#pragma unroll
-      for (int k = 0; k < kCountBatch; ++k) c[k] = (j0 + k < a.nblk) ? hp[(size_t)(j0 + k) * 256 + tid] : 0u;
-#pragma unroll
-      for (int k = 0; k < kCountBatch; ++k) {
-        total += c[k];
-        before += (j0 + k < blk) ? c[k] : 0u;
-      }
-    }
-    cnt[0][tid] = total;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-      const uint32_t t = tid >= off ? cnt[0][tid - off] : 0u;
-      __syncthreads();
-      cnt[0][tid] += t;
-      __syncthreads();
-    }
-    goff[tid] = cnt[0][tid] - total + before;
-  }
-  run[tid] = 0;
-  if (tid < kMaxSortLen / kSlotSeg) segl[tid] = 0;
-  const size_t sb = (size_t)b * a.T;
-  const int base = blk * kSortTile;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int j = 0; j < kSortItems; ++j) {
-    for (int x = 0; x < 4; ++x) cnt[x][tid] = 0;
-    __syncthreads();
-    const int i = base + j * kSortThreads + tid;
-    const bool valid = i < a.T;
-    const uint32_t key = valid ? a.kin[sb + i] : 0u;
-    const uint32_t idx = valid ? (a.iin ? a.iin[sb + i] : (uint32_t)i) : 0u;
-    const uint32_t d = (key >> shift) & 255u;
-    uint64_t peers = __ballot(valid);
-#pragma unroll
-    for (int bit = 0; bit < 8; ++bit) {
-      const bool on = (d >> bit) & 1u;
-      const uint64_t bb = __ballot(on);
-      peers &= on ? bb : ~bb;
-    }
-    const uint32_t rank_w = (uint32_t)__popcll(peers & lt_mask);
-    if (valid && rank_w == 0) cnt[w][d] = (uint32_t)__popcll(peers);
-    __syncthreads();
-    {
-      const uint32_t r0 = run[tid];
-      const uint32_t c0 = cnt[0][tid], c1 = cnt[1][tid], c2 = cnt[2][tid], c3 = cnt[3][tid];
-      cnt[0][tid] = r0;
-      cnt[1][tid] = r0 + c0;
-      cnt[2][tid] = r0 + c0 + c1;
-      cnt[3][tid] = r0 + c0 + c1 + c2;
-      run[tid] = r0 + c0 + c1 + c2 + c3;
-    }
-    __syncthreads();
-    if (valid) {
-      const uint32_t pos = goff[d] + cnt[w][d] + rank_w;
-      if (!last) {
-        a.kout[sb + pos] = key;
-        a.iout[sb + pos] = idx;
-      } else {
-        a.ranks[sb + idx] = (int32_t)pos;
-        if (a.ranks_out) a.ranks_out[sb + idx] = (int32_t)pos;
-        a.sorted_asc[(size_t)b * a.cap + (a.T - 1 - pos)] = a.scores[sb + idx];
-        if ((int)pos < a.n_hi) atomicAdd(&segl[idx / kSlotSeg], 1u);
-      }
-    }
-    __syncthreads();
-  }
-  if (last && tid < a.nseg && segl[tid]) atomicAdd(&a.segcnt[(size_t)b * a.nseg + tid], segl[tid]);
 }
 
 // Slot = index among same-tier tokens in token order.  Workgroup (seg, b)
@@ -273,11 +116,13 @@ constexpr int kBlkThreads = 1024;            // 16 waves x 4 chunks of 64
 // an element goes to (keys with a smaller digit) + (same digit in earlier
 // waves) + (same digit earlier in its own wave, from the wave's running
 // counts).  Out of range elements carry the largest key and the largest
-// indices, so they sort last.  Also clears the block's high-tier counts.
+// indices, so they sort last.  Also clears the block's high-tier counts and,
+// for long sequences, the partial counts of its elements.
 __global__ __launch_bounds__(kBlkThreads) void k_rank_block_sort(const float* __restrict__ scores,
                                                                  uint32_t* __restrict__ skeys,
                                                                  uint32_t* __restrict__ sidx,
-                                                                 uint32_t* __restrict__ hicnt, int T,
+                                                                 uint32_t* __restrict__ hicnt,
+                                                                 uint32_t* __restrict__ cnt, int T,
                                                                  int ld, int nblk, int B) {
   constexpr int NW = kBlkThreads / 64;
   __shared__ uint32_t kb[kBlkSort];
@@ -363,6 +208,7 @@ __global__ __launch_bounds__(kBlkThreads) void k_rank_block_sort(const float* __
     if (e < nb) {
       skeys[(size_t)b * ld + base + e] = key[c];
       sidx[(size_t)b * ld + base + e] = (uint32_t)base + ix[c];
+      if (cnt) cnt[(size_t)b * ld + base + e] = 0u;
     }
   }
 }
@@ -375,7 +221,9 @@ struct MergeArgs {
   int32_t* ranks_out;
   float* sorted_asc;
   uint32_t* hicnt;              // high-tier tokens per kSortTile tokens, [b][ceil(T / kSortTile)]
+  uint32_t* cnt;                // long sequences: entries of other blocks before each element, [b][ld]
   int T, ld, nblk, n_hi, cap, B;
+  int ngrp;                     // long sequences: groups of kMergeBlocks blocks
 };
 
 // LDS word of sorted key i: one pad word per 32 and per 1024 keys, so that
@@ -397,6 +245,26 @@ __device__ inline int count_before(const uint32_t* sk, int first, uint32_t xe) {
     pos += y < xe ? step : 0;
   }
   return pos + (blk[sk_slot(pos)] < xe ? 1 : 0);
+}
+
+// Rank r of sorted element p of block blk (when valid): ranks, the ascending
+// score array, and the high-tier counts per kSortTile-token range.
+__device__ inline void write_rank(const MergeArgs& a, int b, int blk, int p, bool valid, int r,
+                                  uint32_t* whi) {
+  const int tid = threadIdx.x, base = blk * kBlkSort;
+  if (tid < kBlkSort / kSortTile) whi[tid] = 0u;
+  __syncthreads();
+  if (valid) {
+    const uint32_t tok = a.sidx[(size_t)b * a.ld + base + p];
+    a.ranks[(size_t)b * a.T + tok] = r;
+    if (a.ranks_out) a.ranks_out[(size_t)b * a.T + tok] = r;
+    a.sorted_asc[(size_t)b * a.cap + (a.T - 1 - r)] = a.scores[(size_t)b * a.T + tok];
+    if (r < a.n_hi) atomicAdd(&whi[(tok - base) / kSortTile], 1u);
+  }
+  __syncthreads();
+  const int nseg = (a.T + kSortTile - 1) / kSortTile, seg = base / kSortTile + tid;
+  if (tid < kBlkSort / kSortTile && seg < nseg && whi[tid])
+    atomicAdd(&a.hicnt[(size_t)b * nseg + seg], whi[tid]);
 }
 
 // Rank of 1024 sorted elements of one block (quarter q): the element's
@@ -448,20 +316,72 @@ __global__ __launch_bounds__(1024) void k_rank_merge(MergeArgs a) {
   }
 #pragma unroll
   for (int i = 0; i < NI; ++i) r += c[i];
-  if (tid < kBlkSort / kSortTile) whi[tid] = 0u;
-  __syncthreads();
-  if (valid) {
-    const uint32_t tok = a.sidx[(size_t)b * a.ld + base + p];
-    a.ranks[(size_t)b * a.T + tok] = r;
-    if (a.ranks_out) a.ranks_out[(size_t)b * a.T + tok] = r;
-    a.sorted_asc[(size_t)b * a.cap + (a.T - 1 - r)] = a.scores[(size_t)b * a.T + tok];
-    if (r < a.n_hi) atomicAdd(&whi[(tok - base) / kSortTile], 1u);
+  write_rank(a, b, blk, p, valid, r, whi);
+}
+
+// Groups of kMergeBlocks sorted blocks (kMergeMaxT keys) fit one workgroup's
+// LDS; longer sequences count, per (element quarter, group), the entries of
+// the group's blocks that precede each element and add them to its partial
+// count; k_rank_finish then writes the ranks.
+constexpr int kMergeBlocks = kMergeMaxT / kBlkSort;
+__global__ __launch_bounds__(1024) void k_rank_merge_part(MergeArgs a) {
+  __shared__ uint32_t sk[kSkWords];
+  const int tid = threadIdx.x;
+  int b, bg;
+  if (!seq_block(a.nblk * 4 * a.ngrp, a.B, b, bg)) return;
+  const int bq = bg % (a.nblk * 4), gi = bg / (a.nblk * 4);
+  const int blk = bq >> 2, p = (bq & 3) * 1024 + tid;
+  const int g0 = gi * kMergeMaxT, gn = min(kMergeMaxT, a.T - g0);
+  {
+    const uint32_t* src = a.skeys + (size_t)b * a.ld + g0;
+    const int n4 = gn >> 2;
+    const uint4* src4 = reinterpret_cast<const uint4*>(src);
+    uint4 v[kMergeMaxT / 4 / 1024];
+#pragma unroll
+    for (int k = 0; k < kMergeMaxT / 4 / 1024; ++k) {
+      const int i = tid + 1024 * k;
+      if (i < n4) v[k] = src4[i];
+    }
+#pragma unroll
+    for (int k = 0; k < kMergeMaxT / 4 / 1024; ++k) {
+      const int i = tid + 1024 * k;
+      if (i < n4) {
+        const int o = sk_slot(4 * i);
+        sk[o] = v[k].x; sk[o + 1] = v[k].y; sk[o + 2] = v[k].z; sk[o + 3] = v[k].w;
+      }
+    }
+    if (tid < (gn & 3)) sk[sk_slot(4 * n4 + tid)] = src[4 * n4 + tid];
+    for (int i = gn + tid; i < kMergeMaxT; i += 1024) sk[sk_slot(i)] = 0xFFFFFFFFu;
   }
   __syncthreads();
-  // high-tier tokens per kSortTile-token range of the block
-  const int nseg = (a.T + kSortTile - 1) / kSortTile, seg = base / kSortTile + tid;
-  if (tid < kBlkSort / kSortTile && seg < nseg && whi[tid])
-    atomicAdd(&a.hicnt[(size_t)b * nseg + seg], whi[tid]);
+  const int base = blk * kBlkSort, nb = min(kBlkSort, a.T - base);
+  if (p >= nb) return;
+  const uint32_t x = a.skeys[(size_t)b * a.ld + base + p];
+  int r = 0;
+  int c[kMergeBlocks];
+#pragma unroll
+  for (int i = 0; i < kMergeBlocks; ++i) {
+    const int gb = gi * kMergeBlocks + i;
+    const bool use = gb < a.nblk && gb != blk;
+    const int n = use ? min(kBlkSort, a.T - gb * kBlkSort) : 0;
+    if (gb < blk && x == 0xFFFFFFFFu) c[i] = use ? n : 0;
+    else c[i] = use ? count_before(sk, i * kBlkSort, gb < blk ? x + 1u : x) : 0;
+  }
+#pragma unroll
+  for (int i = 0; i < kMergeBlocks; ++i) r += c[i];
+  if (r) atomicAdd(&a.cnt[(size_t)b * a.ld + base + p], (uint32_t)r);
+}
+
+__global__ __launch_bounds__(1024) void k_rank_finish(MergeArgs a) {
+  __shared__ uint32_t whi[kBlkSort / kSortTile];
+  const int tid = threadIdx.x;
+  int b, bq;
+  if (!seq_block(a.nblk * 4, a.B, b, bq)) return;
+  const int blk = bq >> 2, p = (bq & 3) * 1024 + tid;
+  const int base = blk * kBlkSort, nb = min(kBlkSort, a.T - base);
+  const bool valid = p < nb;
+  const int r = valid ? p + (int)a.cnt[(size_t)b * a.ld + base + p] : 0;
+  write_rank(a, b, blk, p, valid, r, whi);
 }
 
 bool launch_rank_tiers(const kvq_layout* L, uint8_t* cache, const float* scores, int T, int n_hi,
@@ -469,10 +389,8 @@ bool launch_rank_tiers(const kvq_layout* L, uint8_t* cache, const float* scores,
   hipStream_t s = (hipStream_t)stream;
   const int B = L->cfg.batch;
   const int nblk = ceil_div(T, kSortTile);
-  const int nseg = ceil_div(T, kSlotSeg);
   uint32_t* keys[2] = {(uint32_t*)(ws + plan.keys[0]), (uint32_t*)(ws + plan.keys[1])};
-  uint32_t* idx[2] = {(uint32_t*)(ws + plan.idx[0]), (uint32_t*)(ws + plan.idx[1])};
-  uint32_t* hist = (uint32_t*)(ws + plan.hist);
+  uint32_t* sidx = (uint32_t*)(ws + plan.idx);
   uint32_t* segcnt = (uint32_t*)(ws + plan.segcnt);
   int32_t* ranks = (int32_t*)(ws + plan.ranks);
   int32_t* inv_hi = (int32_t*)(ws + plan.inv[0]);
@@ -480,48 +398,30 @@ bool launch_rank_tiers(const kvq_layout* L, uint8_t* cache, const float* scores,
   const dim3 gblk = seq_grid(nblk, B);
   uint32_t* tokmap = (uint32_t*)(cache + L->tokmap);
   int32_t* counters = (int32_t*)(cache + L->counters);
-  if (T <= kMergeMaxT) {
-    const int nb4 = ceil_div(T, kBlkSort);
-    const int ld = (T + 3) & ~3;             // 16-byte aligned rows of sorted keys
-    k_rank_block_sort<<<seq_grid(nb4, B), kBlkThreads, 0, s>>>(scores, keys[0], idx[0], segcnt, T, ld, nb4,
-                                                               B);
-    MergeArgs m;
-    m.skeys = keys[0];
-    m.sidx = idx[0];
-    m.scores = scores;
-    m.ranks = ranks;
-    m.ranks_out = ranks_out;
-    m.sorted_asc = (float*)(cache + L->sorted);
-    m.hicnt = segcnt;
-    m.T = T; m.ld = ld; m.nblk = nb4; m.n_hi = n_hi; m.cap = L->cfg.capacity; m.B = B;
+  const int nb4 = ceil_div(T, kBlkSort);
+  const int ld = (T + 3) & ~3;               // 16-byte aligned rows of sorted keys
+  const bool grouped = T > kMergeMaxT;       // sorted keys exceed one workgroup's LDS
+  MergeArgs m;
+  m.skeys = keys[0];
+  m.sidx = sidx;
+  m.scores = scores;
+  m.ranks = ranks;
+  m.ranks_out = ranks_out;
+  m.sorted_asc = (float*)(cache + L->sorted);
+  m.hicnt = segcnt;
+  m.cnt = grouped ? keys[1] : nullptr;
+  m.T = T; m.ld = ld; m.nblk = nb4; m.n_hi = n_hi; m.cap = L->cfg.capacity; m.B = B;
+  m.ngrp = ceil_div(nb4, kMergeBlocks);
+  k_rank_block_sort<<<seq_grid(nb4, B), kBlkThreads, 0, s>>>(scores, keys[0], sidx, segcnt, m.cnt, T,
+                                                             ld, nb4, B);
+  if (!grouped) {
     k_rank_merge<<<seq_grid(4 * nb4, B), 1024, 0, s>>>(m);
-    k_rank_slots<kSortTile><<<gblk, 256, 0, s>>>(ranks, segcnt, tokmap, inv_hi, inv_lo, counters, T, n_hi,
-                                                 L->cfg.capacity, L->cap[0], L->cap[1], nblk, B);
-    return hipGetLastError() == hipSuccess;
+  } else {
+    k_rank_merge_part<<<seq_grid(4 * nb4 * m.ngrp, B), 1024, 0, s>>>(m);
+    k_rank_finish<<<seq_grid(4 * nb4, B), 1024, 0, s>>>(m);
   }
-  k_rank_keys<<<gblk, kSortThreads, 0, s>>>(scores, keys[0], hist, segcnt, T, nblk, nseg, B);
-  int cur = 0;
-  for (int pass = 0; pass < 4; ++pass) {
-    if (pass > 0) k_rank_count<<<gblk, kSortThreads, 0, s>>>(keys[cur], hist, T, nblk, pass, B);
-    ScatterArgs a;
-    a.kin = keys[cur];
-    a.iin = pass == 0 ? nullptr : idx[cur];
-    a.kout = keys[cur ^ 1];
-    a.iout = idx[cur ^ 1];
-    a.hist = hist;
-    a.T = T; a.nblk = nblk; a.pass = pass;
-    a.scores = scores;
-    a.ranks = ranks;
-    a.ranks_out = ranks_out;
-    a.sorted_asc = (float*)(cache + L->sorted);
-    a.segcnt = segcnt;
-    a.cap = L->cfg.capacity; a.n_hi = n_hi; a.nseg = nseg; a.B = B;
-    k_rank_scatter<<<gblk, kSortThreads, 0, s>>>(a);
-    cur ^= 1;
-  }
-  k_rank_slots<kSlotSeg><<<seq_grid(nseg, B), 256, 0, s>>>(ranks, segcnt, tokmap, inv_hi, inv_lo, counters,
-                                                          T, n_hi, L->cfg.capacity, L->cap[0], L->cap[1],
-                                                          nseg, B);
+  k_rank_slots<kSortTile><<<gblk, 256, 0, s>>>(ranks, segcnt, tokmap, inv_hi, inv_lo, counters, T, n_hi,
+                                               L->cfg.capacity, L->cap[0], L->cap[1], nblk, B);
   return hipGetLastError() == hipSuccess;
 }
 

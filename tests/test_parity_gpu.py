@@ -85,6 +85,21 @@ def test_tiered_edge_sizes(T, n_hi):
     _check_tiered(w, inp, run)
 
 
+@pytest.mark.parametrize("T", [32769, 70001])
+def test_tiered_long_sequences_with_ties(T):
+    """Sequences longer than one workgroup's LDS of sorted keys (the ranks
+    add partial counts over groups of blocks, the last group partial), with
+    runs of equal scores across block and group boundaries."""
+    w = C[2].shrink(name=f"long_T{T}", batch=2, kv_heads=1, q_heads=4, tokens=T)
+    log(f"case {w.name}")
+    inp = synth.make_inputs(w)
+    inp.scores[0] = np.round(inp.scores[0] * 4) / 4            # few distinct values: long tie runs
+    inp.scores[1, 30000:36000] = np.float32(1.0)                # one run over the group boundary
+    run = GpuRun(w, inp)
+    run.quantize()
+    _check_tiered(w, inp, run)
+
+
 def test_tiered_ties_zeros_and_constant_groups():
     """Equal scores (stable order decides), -0/+0 scores, constant groups
     (scale 0), signed zeros in the data."""
