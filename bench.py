@@ -154,6 +154,20 @@ def _timed(torch, stream, fn, iters):
     return float(np.median(t)), float(np.percentile(t, 10)), float(np.percentile(t, 90))
 
 
+def stream_read_gbs(torch, kvq, dev, stream, nbytes=1 << 30, iters=10):
+    """Achievable HBM read rate: the library's read-stream probe over a buffer
+    four times the 256 MB infinity cache, median of `iters` launches."""
+    import numpy as np
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    nwg = 4096
+    sink = torch.zeros(nwg, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        kvq.stream_read(buf, sink, nwg, stream=stream)
+    ms = _timed(torch, stream, lambda i: kvq.stream_read(buf, sink, nwg, stream=stream), iters)[0]
+    del buf
+    return nbytes / (ms * 1e-3) / 1e9
+
+
 def sweep_one(w, args, torch, np, kvq, synth, dev):
     """Quantize and decode (and, for the append workload, append + decode per
     generation step) of one workload, inputs resident in HBM."""
@@ -296,6 +310,9 @@ def main():
 
     dev = torch.device("cuda:0")
     if args.sweep:
+        rg = stream_read_gbs(torch, kvq, dev, torch.cuda.current_stream())
+        print(json.dumps({"probe": "stream_read", "bytes": 1 << 30, "gbs": round(rg, 1),
+                          "frac_hbm": round(rg / HBM_PEAK_GBS, 4)}), flush=True)
         for cw in synth.CONFIGS:
             if args.sweep_only and cw.name not in args.sweep_only.split(","):
                 continue
@@ -410,6 +427,11 @@ def main():
         roof = dict(bound="hbm", achieved=round(q_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(q_gbs / HBM_PEAK_GBS, 4),
                     traffic=measured_traffic("quantize", khash), kernel="kvq_quantize (rank + quantize)")
+
+    # achievable HBM read bandwidth of this device (read-stream probe, 1 GiB)
+    read_gbs = stream_read_gbs(torch, kvq, dev, stream)
+    roof["achievable_read_gbs"] = round(read_gbs, 1)
+    roof["frac_of_achievable"] = round(roof["achieved"] / read_gbs, 4)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -231,6 +231,17 @@ kvq_status kvq_decode_attn_multi(const kvq_layout* lay, const void* cache,
                                  int32_t max_len, void* out, float* lse,
                                  void* ws, size_t ws_bytes, void* stream);
 
+/* Measurement aid, not part of the method: reads every byte of a device
+ * buffer once (16-byte loads, coalesced) to measure the achievable HBM read
+ * bandwidth, the reference beside the published peak for the rates of the
+ * entry points above.
+ *   buf:   device pointer, 16-byte aligned; bytes: a multiple of 16, > 0.
+ *   sink:  device uint32 [n_workgroups], written (the xor of what was read).
+ *   n_workgroups: 1 .. 65536 (256 threads each).
+ * KVQ_ERR_ARG on a null or misaligned pointer or a bad size. */
+kvq_status kvq_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t n_workgroups,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -10,7 +10,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libkvq.so")
 BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["api.cpp", "rank.hip", "quantize.hip", "decode.hip", "decode_mfma.hip", "decode_mq.hip"]
+SOURCES = ["api.cpp", "rank.hip", "quantize.hip", "decode.hip", "decode_mfma.hip", "decode_mq.hip", "probe.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -231,3 +231,11 @@ extern "C" kvq_status kvq_decode_attn_multi(const kvq_layout* lay, const void* c
     return KVQ_ERR_LAUNCH;
   return KVQ_OK;
 }
+
+extern "C" kvq_status kvq_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t n_workgroups,
+                                      void* stream) {
+  if (!buf || !sink || !aligned16(buf) || ((uintptr_t)sink & 3u)) return KVQ_ERR_ARG;
+  if (bytes == 0 || (bytes & 15) || n_workgroups < 1 || n_workgroups > 65536) return KVQ_ERR_ARG;
+  if (!launch_stream_read(buf, bytes, sink, n_workgroups, stream)) return KVQ_ERR_LAUNCH;
+  return KVQ_OK;
+}

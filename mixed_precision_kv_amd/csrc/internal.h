@@ -79,6 +79,8 @@ struct PoolMqArgs {
 bool launch_decode_mq(const kvq_layout* L, const uint8_t* cache, const void* q, int M, float scale,
                       int max_len, void* out, float* lse, uint8_t* ws, void* stream);
 size_t decode_mq_ws_bytes(const kvq_layout* L, int M, int max_len);
+// Read-stream probe (every byte once, 16-byte loads) over nwg workgroups.
+bool launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int nwg, void* stream);
 // Matrix-core decode of a per-channel-key cache: nch0 quantized chunks and
 // nwch fp16-window chunks per unit in one launch; false when the
 // configuration is not the one it is built for.

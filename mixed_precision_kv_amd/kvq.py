@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_decode_attn_multi.argtypes = [cp(KvqLayout), vp, vp, _i32, ctypes.c_float, _i32, vp, vp,
                                             vp, ctypes.c_size_t, vp]
         L.kvq_decode_attn_multi.restype = ctypes.c_int
+        L.kvq_stream_read.argtypes = [vp, ctypes.c_size_t, vp, _i32, vp]
+        L.kvq_stream_read.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -169,3 +171,10 @@ def decode_attn_multi(lay, cache, q, n_queries, scale, max_len, out, lse, ws, ws
                                      max_len, _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
                                      _stream(stream))
     _check(st, "kvq_decode_attn_multi")
+
+
+def stream_read(buf, sink, n_workgroups, stream=None):
+    """Measurement aid: read every byte of `buf` once on the device."""
+    st = lib().kvq_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), n_workgroups,
+                               _stream(stream))
+    _check(st, "kvq_stream_read")

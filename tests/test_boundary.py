@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol():
     names = declared_symbols()
     assert {"kvq_layout_init", "kvq_workspace_bytes", "kvq_status_str", "kvq_quantize",
             "kvq_append", "kvq_decode_attn", "kvq_multi_workspace_bytes",
-            "kvq_decode_attn_multi"} <= set(names)
+            "kvq_decode_attn_multi", "kvq_stream_read"} <= set(names)
     L = kvq.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -188,6 +188,15 @@ def test_decode_multi_workspace_and_mode():
         kvq.decode_attn_multi(lay5, FAKE, FAKE, 4, 0.088, 1024, FAKE, None, FAKE, ws_bytes=1 << 40,
                               stream=0)
     assert e.value.status == 2
+
+
+@pytest.mark.parametrize("buf,nbytes,sink,nwg", [
+    (0, 1024, FAKE, 8), (FAKE + 8, 1024, FAKE, 8), (FAKE, 1000, FAKE, 8), (FAKE, 0, FAKE, 8),
+    (FAKE, 1024, 0, 8), (FAKE, 1024, FAKE + 2, 8), (FAKE, 1024, FAKE, 0), (FAKE, 1024, FAKE, 65537),
+])
+def test_stream_read_validation(buf, nbytes, sink, nwg):
+    st = kvq.lib().kvq_stream_read(buf, nbytes, sink, nwg, None)
+    assert st == 1
 
 
 def test_status_strings():

@@ -249,3 +249,19 @@ def test_append_pool_full_flag():
     after = LV.counters(run.buf(), run.lay)
     assert after[:, 3].tolist() == [1, 1]
     assert np.array_equal(after[:, :3], before[:, :3])
+
+
+def test_stream_read_probe_reads_every_word_once():
+    """The bandwidth probe's sink: the xor of the per-workgroup words equals
+    the xor of every word of the buffer (each word read exactly once)."""
+    import torch
+    from mixed_precision_kv_amd import kvq
+    rng = np.random.default_rng(5)
+    words = rng.integers(0, 2**32, size=(1 << 20) + 4, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(words.view(np.int32)).to("cuda:0")
+    for nwg in (1, 7, 300):
+        sink = torch.zeros(nwg, dtype=torch.int32, device="cuda:0")
+        kvq.stream_read(buf, sink, nwg)
+        torch.cuda.synchronize()
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        assert got == np.bitwise_xor.reduce(words), nwg
