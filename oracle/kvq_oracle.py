@@ -289,6 +289,23 @@ def attention_lse_fp64(q: np.ndarray, k_hat: np.ndarray, v_hat: np.ndarray, scal
     return (p @ v_hat.astype(F64)) / l, (m + np.log(l))[:, 0]
 
 
+def token_attention_mass(q_seq: np.ndarray, k_hat_heads, scale: float) -> np.ndarray:
+    """Per-token importance from one decode step: the attention weight each
+    cached token receives, summed over every query head of the sequence, fp64
+    ([SemKV] Abstract: tokens are ranked by a model-internal score; this is
+    the score decode itself can report).  q_seq [Hq][D]; k_hat_heads: list of
+    Hkv arrays [N][D] in token order; query head hq reads KV head
+    hq // (Hq / Hkv).  Returns [N]; it sums to Hq."""
+    Hq = q_seq.shape[0]
+    g = Hq // len(k_hat_heads)
+    mass = np.zeros(k_hat_heads[0].shape[0], dtype=F64)
+    for hq in range(Hq):
+        s = (k_hat_heads[hq // g].astype(F64) @ q_seq[hq].astype(F64)) * F64(scale)
+        p = np.exp(s - s.max())
+        mass += p / p.sum()
+    return mass
+
+
 def row_rel_err(o: np.ndarray, r: np.ndarray) -> float:
     """Error measure for attention outputs: max over rows of
     max|o - r| / max|r| (rows are the last-but-one axis)."""

@@ -328,6 +328,34 @@ def test_attention_lse_brute_force_and_closed_forms():
     assert np.allclose(lm, lse, atol=1e-13) and np.allclose(om, o, atol=1e-13)
 
 
+def test_token_attention_mass_pins():
+    rng = np.random.default_rng(23)
+    Hq, Hkv, N, D = 8, 2, 13, 16
+    q = rng.standard_normal((Hq, D))
+    ks = [rng.standard_normal((N, D)) for _ in range(Hkv)]
+    m = O.token_attention_mass(q, ks, 0.3)
+    # every head's weights sum to one
+    assert abs(m.sum() - Hq) < 1e-12 and np.all(m >= 0)
+    # brute force: pure-Python softmax of every head
+    for t in (0, 5, 12):
+        tot = 0.0
+        for hq in range(Hq):
+            sc = [0.3 * math.fsum(float(q[hq, d]) * float(ks[hq // 4][u, d]) for d in range(D)) for u in range(N)]
+            den = math.fsum(math.exp(x) for x in sc)
+            tot += math.exp(sc[t]) / den
+        assert abs(m[t] - tot) < 1e-12
+    # identical keys: every token gets Hq / N; one token gets Hq
+    same = [np.repeat(k[:1], N, 0) for k in ks]
+    assert np.allclose(O.token_attention_mass(q, same, 0.3), Hq / N, atol=1e-14)
+    assert np.allclose(O.token_attention_mass(q, [k[:1] for k in ks], 0.3), [Hq], atol=1e-14)
+    # it agrees with the weights behind attention_lse_fp64 (exp(s - lse))
+    _, lse = O.attention_lse_fp64(q[:4], ks[0], ks[0], 0.3)
+    w = np.exp(0.3 * (q[:4] @ ks[0].T) - lse[:, None]).sum(0)
+    _, lse2 = O.attention_lse_fp64(q[4:], ks[1], ks[1], 0.3)
+    w += np.exp(0.3 * (q[4:] @ ks[1].T) - lse2[:, None]).sum(0)
+    assert np.allclose(w, m, atol=1e-13)
+
+
 def test_row_rel_err_definition():
     r = np.array([[1.0, -2.0, 0.5]])
     o = np.array([[1.0, -2.002, 0.5]])
