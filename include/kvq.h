@@ -87,7 +87,7 @@ typedef enum kvq_status {
 } kvq_status;
 
 enum { KVQ_MODE_TIERED = 0, KVQ_MODE_KCHAN = 1 };
-enum { KVQ_OP_QUANTIZE = 0, KVQ_OP_DECODE = 1 };
+enum { KVQ_OP_QUANTIZE = 0, KVQ_OP_DECODE = 1, KVQ_OP_DECODE_MASS = 2 };
 
 /* Caller-filled description of one cache (host memory, plain data). */
 typedef struct kvq_config {
@@ -208,6 +208,22 @@ kvq_status kvq_append(const kvq_layout* lay, void* cache,
 kvq_status kvq_decode_attn(const kvq_layout* lay, const void* cache,
                            const void* q, float softmax_scale, int32_t max_len,
                            void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Decode attention as kvq_decode_attn, plus the attention mass of every
+ * cached token: the softmax weight it receives, summed over the sequence's
+ * query heads (SemKV, Abstract: tokens are ranked by a model-internal score;
+ * this is a score the decode step itself can hand back for re-ranking).  The
+ * masses of a sequence sum to Hq.  Tiered mode only.
+ *   mass:  device fp32 [B][max_len]; entry (b, t) for token index t of
+ *          sequence b (insertion order, appended tokens included), 0 past
+ *          the sequence's length.
+ *   ws:    device workspace >= kvq_workspace_bytes(lay, KVQ_OP_DECODE_MASS,
+ *          max_len) (the partials, each pool's raw scores, per-head sums).
+ * Returns KVQ_ERR_UNSUPPORTED for the per-channel-key mode. */
+kvq_status kvq_decode_attn_mass(const kvq_layout* lay, const void* cache,
+                                const void* q, float softmax_scale, int32_t max_len,
+                                void* out, float* mass, void* ws, size_t ws_bytes,
+                                void* stream);
 
 /* Workspace bytes of kvq_decode_attn_multi for n_queries query tokens per
  * sequence and sequences of at most max_len tokens; 0 on bad arguments. */

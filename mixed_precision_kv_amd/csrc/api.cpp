@@ -137,12 +137,9 @@ extern "C" kvq_status kvq_layout_init(const kvq_config* cfg, kvq_layout* out) {
 extern "C" size_t kvq_workspace_bytes(const kvq_layout* lay, int32_t op, int32_t max_len) {
   if (!lay || max_len < 1 || max_len > lay->cfg.capacity) return 0;
   if (op == KVQ_OP_QUANTIZE) return quant_ws_plan(lay, max_len).total;
-  if (op == KVQ_OP_DECODE) {
-    int a, b;
-    int n = decode_chunks(lay, max_len, &a, &b);
-    const int64_t U = (int64_t)lay->cfg.batch * lay->cfg.kv_heads;
-    return (size_t)(U * n * kGqa * (4 + kD) * 4);
-  }
+  if (op == KVQ_OP_DECODE) return decode_ws_bytes(lay, max_len, false);
+  if (op == KVQ_OP_DECODE_MASS)
+    return lay->cfg.mode == KVQ_MODE_TIERED ? decode_ws_bytes(lay, max_len, true) : 0;
   return 0;
 }
 
@@ -237,5 +234,22 @@ extern "C" kvq_status kvq_stream_read(const void* buf, size_t bytes, uint32_t* s
   if (!buf || !sink || !aligned16(buf) || ((uintptr_t)sink & 3u)) return KVQ_ERR_ARG;
   if (bytes == 0 || (bytes & 15) || n_workgroups < 1 || n_workgroups > 65536) return KVQ_ERR_ARG;
   if (!launch_stream_read(buf, bytes, sink, n_workgroups, stream)) return KVQ_ERR_LAUNCH;
+  return KVQ_OK;
+}
+
+extern "C" kvq_status kvq_decode_attn_mass(const kvq_layout* lay, const void* cache, const void* q,
+                                           float softmax_scale, int32_t max_len, void* out, float* mass,
+                                           void* ws, size_t ws_bytes, void* stream) {
+  if (!lay || !cache || !q || !out || !mass) return KVQ_ERR_ARG;
+  if (!aligned16(cache) || !aligned16(q) || !aligned16(out) || ((uintptr_t)mass & 3u)) return KVQ_ERR_ARG;
+  if (!(softmax_scale > 0.0f) || softmax_scale > 1e30f) return KVQ_ERR_ARG;
+  if (max_len < 1) return KVQ_ERR_ARG;
+  if (max_len > lay->cfg.capacity) return KVQ_ERR_CAPACITY;
+  if (lay->cfg.mode != KVQ_MODE_TIERED) return KVQ_ERR_UNSUPPORTED;
+  size_t need = kvq_workspace_bytes(lay, KVQ_OP_DECODE_MASS, max_len);
+  if (!ws || !aligned16(ws) || ws_bytes < need) return KVQ_ERR_WORKSPACE;
+  if (!launch_decode(lay, (const uint8_t*)cache, q, softmax_scale, max_len, out, (uint8_t*)ws, stream,
+                     mass))
+    return KVQ_ERR_LAUNCH;
   return KVQ_OK;
 }

@@ -279,7 +279,7 @@ constexpr int kMergeBatch = 8;                // chunks per thread per round tri
 template <int THREADS>
 __global__ __launch_bounds__(THREADS) void k_merge(const float* __restrict__ part,
                                                    uint16_t* __restrict__ out, int nch_total,
-                                                   int Hkv) {
+                                                   int Hkv, float2* __restrict__ stats) {
   constexpr int S = THREADS / 32;             // slices
   __shared__ float smax[S];
   __shared__ float4 racc[S][32];
@@ -339,6 +339,7 @@ __global__ __launch_bounds__(THREADS) void k_merge(const float* __restrict__ par
       l += rl[k];
     }
     uint16_t* po = out + ((size_t)b * Hkv * kGqa + hk * kGqa + hh) * kD + 4 * t;
+    if (stats && t == 0) stats[u * kGqa + hh] = make_float2(Mg, l);   // (max, sum) of the head
     po[0] = f2h_rne(r.x / l);
     po[1] = f2h_rne(r.y / l);
     po[2] = f2h_rne(r.z / l);
@@ -347,13 +348,56 @@ __global__ __launch_bounds__(THREADS) void k_merge(const float* __restrict__ par
 }
 
 // 8 slices for few chunks per unit, 32 for many (long contexts over few units)
-static void launch_merge(const float* part, uint16_t* out, int U, int nch, int Hkv, hipStream_t s) {
-  if (nch <= 8 * kMergeBatch) k_merge<256><<<dim3(U, kGqa), 256, 0, s>>>(part, out, nch, Hkv);
-  else k_merge<1024><<<dim3(U, kGqa), 1024, 0, s>>>(part, out, nch, Hkv);
+static void launch_merge(const float* part, uint16_t* out, int U, int nch, int Hkv, hipStream_t s,
+                         float2* stats = nullptr) {
+  if (nch <= 8 * kMergeBatch) k_merge<256><<<dim3(U, kGqa), 256, 0, s>>>(part, out, nch, Hkv, stats);
+  else k_merge<1024><<<dim3(U, kGqa), 1024, 0, s>>>(part, out, nch, Hkv, stats);
+}
+
+// Attention mass of every cached token of sequence b: the softmax weight it
+// receives summed over the sequence's query heads, from the pools' raw
+// (log2-domain) scores and each head's (max, sum) after the merge; the token
+// map gives each token's pool and slot.  Tokens past the sequence's length
+// get 0.
+__global__ __launch_bounds__(256) void k_token_mass(const int32_t* __restrict__ counters,
+                                                   const uint32_t* __restrict__ tokmap,
+                                                   const float* __restrict__ raw0,
+                                                   const float* __restrict__ raw1,
+                                                   const float2* __restrict__ stats,
+                                                   float* __restrict__ mass, int cap, int cap0,
+                                                   int cap1, int Hkv, int max_len) {
+  const int b = blockIdx.y, t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= max_len) return;
+  float sum = 0.f;
+  if (t < counters[b * 4 + 0]) {
+    const uint32_t mp = tokmap[(size_t)b * cap + t];
+    const bool lo = (mp >> 31) != 0u;
+    const uint32_t slot = mp & 0x7FFFFFFFu;
+    const float* raw = lo ? raw1 : raw0;
+    const int capp = lo ? cap1 : cap0;
+    for (int hk = 0; hk < Hkv; ++hk) {
+      const int u = b * Hkv + hk;
+#pragma unroll
+      for (int h = 0; h < kGqa; ++h) {
+        const float2 st = stats[u * kGqa + h];
+        sum += __builtin_amdgcn_exp2f(raw[((size_t)u * kGqa + h) * capp + slot] - st.x) / st.y;
+      }
+    }
+  }
+  mass[(size_t)b * max_len + t] = sum;
+}
+
+size_t decode_ws_bytes(const kvq_layout* L, int max_len, bool mass) {
+  int a, b;
+  const int n = decode_chunks(L, max_len, &a, &b);
+  const size_t U = (size_t)L->cfg.batch * L->cfg.kv_heads;
+  size_t bytes = U * n * kGqa * kPartStride * 4;
+  if (mass) bytes += U * kGqa * ((size_t)L->cap[0] + L->cap[1]) * 4 + U * kGqa * 8;
+  return bytes;
 }
 
 bool launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, float scale,
-                   int max_len, void* out, uint8_t* ws, void* stream) {
+                   int max_len, void* out, uint8_t* ws, void* stream, float* mass) {
   hipStream_t s = (hipStream_t)stream;
   const kvq_config& c = L->cfg;
   const int U = c.batch * c.kv_heads;
@@ -378,6 +422,11 @@ bool launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, flo
     }
     const int nch_used = nchp[0] + nchp[1];
     if (nch_used > nch) return false;          // workspace is sized for the finest split
+    // with the token mass: raw scores of both pools, then per-head (max, sum)
+    float* raw[2];
+    raw[0] = (float*)(ws + (size_t)U * nch * kGqa * kPartStride * 4);
+    raw[1] = raw[0] + (size_t)U * kGqa * L->cap[0];
+    float2* stats = (float2*)(raw[1] + (size_t)U * kGqa * L->cap[1]);
     for (int p = 0; p < 2; ++p) {
       PoolArgs pa;
       pa.counters = a.counters;
@@ -395,9 +444,15 @@ bool launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, flo
       pa.part_off = p ? nchp[0] : 0;
       pa.chunk = chunk[p];
       pa.c = a.scale_log2;
+      pa.raw = mass ? raw[p] : nullptr;
+      pa.cap_p = L->cap[p];
       if (nchp[p] > 0 && !launch_decode_pool(lv[p], pa, c.group, nchp[p], U, stream)) return false;
     }
-    launch_merge((const float*)ws, (uint16_t*)out, U, nch_used, c.kv_heads, s);
+    launch_merge((const float*)ws, (uint16_t*)out, U, nch_used, c.kv_heads, s, mass ? stats : nullptr);
+    if (mass)
+      k_token_mass<<<dim3(ceil_div(max_len, 256), c.batch), 256, 0, s>>>(
+          a.counters, (const uint32_t*)(cache + L->tokmap), raw[0], raw[1], stats, mass, c.capacity,
+          L->cap[0], L->cap[1], c.kv_heads, max_len);
     return hipGetLastError() == hipSuccess;
   } else {
     a.kwords[0] = (const uint32_t*)(cache + L->k_words[0]);

@@ -172,6 +172,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
           for (int h = 0; h < 4; ++h) x[h] = __builtin_fmaf(ssc, pr[h], zz * qc[h]);
           float sc = reduce_scatter4(x);
           scs[t] = (s0 + 16 * t + n < s_end) ? sc : -INFINITY;
+          if (a.raw && s0 + 16 * t + n < s_end)     // lane (n, j): head j of slot n
+            a.raw[((size_t)u * kGqa + j) * a.cap_p + s0 + 16 * t + n] = sc;
           mx = fmaxf(mx, scs[t]);
         }
         // online softmax (lane (n, h): head h).  Weights go to the value wave

@@ -42,7 +42,10 @@ bool launch_quantize_kchan(const kvq_layout* L, uint8_t* cache, const void* k, c
 bool launch_append(const kvq_layout* L, uint8_t* cache, const void* k_new, const void* v_new,
                    const float* score_new, void* stream);
 bool launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, float scale,
-                   int max_len, void* out, uint8_t* ws, void* stream);
+                   int max_len, void* out, uint8_t* ws, void* stream, float* mass = nullptr);
+// Workspace of a decode (partials), plus, with the token mass, the pools'
+// raw scores and the per-head (max, sum) after the merge.
+size_t decode_ws_bytes(const kvq_layout* L, int max_len, bool mass);
 
 // One tier pool of the matrix-core decode kernel.
 struct PoolArgs {
@@ -56,6 +59,8 @@ struct PoolArgs {
   int pool, Hkv, tiles, vrows, nch_total, part_off;
   int chunk;          // slots per workgroup (a whole number of macro tiles)
   float c;            // softmax scale * log2(e)
+  float* raw;         // or null: log2-domain scores out, [unit][head][cap_p]
+  int cap_p;          // slots of this pool
 };
 // Slots per workgroup for one pool so that the grid fills the chip about once
 // (uses the kernel's occupancy; falls back to 8 macro tiles).

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvq.so")
 
 MODE_TIERED, MODE_KCHAN = 0, 1
-OP_QUANTIZE, OP_DECODE = 0, 1
+OP_QUANTIZE, OP_DECODE, OP_DECODE_MASS = 0, 1, 2
 STATUS = {0: "KVQ_OK", 1: "KVQ_ERR_ARG", 2: "KVQ_ERR_UNSUPPORTED", 3: "KVQ_ERR_CAPACITY",
           4: "KVQ_ERR_WORKSPACE", 5: "KVQ_ERR_LAUNCH"}
 
@@ -77,6 +77,9 @@ def lib() -> ctypes.CDLL:
         L.kvq_decode_attn_multi.argtypes = [cp(KvqLayout), vp, vp, _i32, ctypes.c_float, _i32, vp, vp,
                                             vp, ctypes.c_size_t, vp]
         L.kvq_decode_attn_multi.restype = ctypes.c_int
+        L.kvq_decode_attn_mass.argtypes = [cp(KvqLayout), vp, vp, ctypes.c_float, _i32, vp, vp, vp,
+                                           ctypes.c_size_t, vp]
+        L.kvq_decode_attn_mass.restype = ctypes.c_int
         L.kvq_stream_read.argtypes = [vp, ctypes.c_size_t, vp, _i32, vp]
         L.kvq_stream_read.restype = ctypes.c_int
         _lib = L
@@ -178,3 +181,11 @@ def stream_read(buf, sink, n_workgroups, stream=None):
     st = lib().kvq_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), n_workgroups,
                                _stream(stream))
     _check(st, "kvq_stream_read")
+
+
+def decode_attn_mass(lay, cache, q, scale, max_len, out, mass, ws, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = lib().kvq_decode_attn_mass(ctypes.byref(lay), _ptr(cache), _ptr(q), float(scale), max_len,
+                                    _ptr(out), _ptr(mass), _ptr(ws), ws_bytes, _stream(stream))
+    _check(st, "kvq_decode_attn_mass")

@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol():
     names = declared_symbols()
     assert {"kvq_layout_init", "kvq_workspace_bytes", "kvq_status_str", "kvq_quantize",
             "kvq_append", "kvq_decode_attn", "kvq_multi_workspace_bytes",
-            "kvq_decode_attn_multi", "kvq_stream_read"} <= set(names)
+            "kvq_decode_attn_multi", "kvq_stream_read", "kvq_decode_attn_mass"} <= set(names)
     L = kvq.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -187,6 +187,34 @@ def test_decode_multi_workspace_and_mode():
     with pytest.raises(kvq.KvqError) as e:
         kvq.decode_attn_multi(lay5, FAKE, FAKE, 4, 0.088, 1024, FAKE, None, FAKE, ws_bytes=1 << 40,
                               stream=0)
+    assert e.value.status == 2
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(cache=0), 1), (dict(q=FAKE + 2), 1), (dict(out=0), 1), (dict(mass=0), 1),
+    (dict(mass=FAKE + 2), 1), (dict(scale=0.0), 1), (dict(max_len=0), 1), (dict(max_len=4097), 3),
+    (dict(ws=0), 4), (dict(ws_bytes=64), 4),
+])
+def test_decode_mass_validation(over, status):
+    lay = kvq.layout_init(_cfg())
+    a = dict(cache=FAKE, q=FAKE, scale=0.088, max_len=4096, out=FAKE, mass=FAKE, ws=FAKE, ws_bytes=1 << 40)
+    a.update(over)
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.decode_attn_mass(lay, a["cache"], a["q"], a["scale"], a["max_len"], a["out"], a["mass"],
+                             a["ws"], ws_bytes=a["ws_bytes"], stream=0)
+    assert e.value.status == status
+
+
+def test_decode_mass_workspace_and_mode():
+    lay = kvq.layout_init(_cfg())
+    plain = kvq.workspace_bytes(lay, kvq.OP_DECODE, 4096)
+    extra = kvq.workspace_bytes(lay, kvq.OP_DECODE_MASS, 4096) - plain
+    U = lay.cfg.batch * lay.cfg.kv_heads
+    assert extra == U * 4 * (lay.cap[0] + lay.cap[1]) * 4 + U * 4 * 8
+    lay5 = kvq.layout_init(kvq.config_for(synth.CONFIGS[4]))
+    assert kvq.workspace_bytes(lay5, kvq.OP_DECODE_MASS, 1024) == 0
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.decode_attn_mass(lay5, FAKE, FAKE, 0.088, 1024, FAKE, FAKE, FAKE, ws_bytes=1 << 40, stream=0)
     assert e.value.status == 2
 
 
