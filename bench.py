@@ -222,6 +222,19 @@ def sweep_one(w, args, torch, np, kvq, synth, dev):
                       "frac_hbm": round(dec_bytes / (d_ms[0] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                       "ctx_tokens_per_s_per_qhead": w.batch * w.q_heads * w.tokens / (d_ms[0] * 1e-3),
                       "replicas": R}}
+    if tiered:
+        # decode that also reports every token's attention mass
+        mass = torch.empty((w.batch, max_len), dtype=torch.float32, device=dev)
+        wsm = torch.empty(kvq.workspace_bytes(lay, kvq.OP_DECODE_MASS, max_len), dtype=torch.uint8, device=dev)
+
+        def decode_mass(i):
+            kvq.decode_attn_mass(lay, caches[i % R], q, scale, max_len, out, mass, wsm, stream=stream)
+
+        for i in range(3):
+            decode_mass(i)
+        dm_ms = _timed(torch, stream, decode_mass, 30)
+        res["decode_mass"] = {"ms": dm_ms[0], "ms_p10": dm_ms[1], "ms_p90": dm_ms[2],
+                              "overhead_vs_decode": round(dm_ms[0] / d_ms[0] - 1.0, 4)}
     if tiered and args.multi_queries > 0:
         # a block of M new query tokens per sequence over the same caches
         M = args.multi_queries

@@ -62,6 +62,19 @@ class GpuRun:
         torch.cuda.synchronize()
         return out.cpu().numpy()
 
+    def decode_mass(self, q_np, max_len=None):
+        """Decode with the per-token attention mass -> mass [B][capacity]."""
+        import torch
+        ml = max_len or self.w.capacity
+        ws = torch.empty(kvq.workspace_bytes(self.lay, kvq.OP_DECODE_MASS, ml), dtype=torch.uint8,
+                         device=dev())
+        q = to_dev(q_np)
+        out = torch.empty_like(q)
+        mass = torch.empty((self.w.batch, ml), dtype=torch.float32, device=dev())
+        kvq.decode_attn_mass(self.lay, self.cache, q, float(self.scale), ml, out, mass, ws)
+        torch.cuda.synchronize()
+        return mass.cpu().numpy()
+
     def decode_multi(self, qm, max_len=None):
         """Attention of a block of query tokens qm [B][M][Hq][D] -> (out, lse)."""
         import torch

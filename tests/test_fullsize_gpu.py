@@ -44,6 +44,11 @@ def test_tiered_fullsize(idx):
     assert np.array_equal(LV.sorted_scores(buf, run.lay)[:, :w.tokens], np.sort(inp.scores, axis=1))
     out = run.decode(inp.q)
     _bounded(out, inp.v)
+    # per-token attention mass: properties at full size (sums to Hq per sequence)
+    mass = run.decode_mass(inp.q)
+    assert np.all(np.isfinite(mass)) and np.all(mass >= 0)
+    assert np.allclose(mass[:, :w.tokens].astype(np.float64).sum(1), w.q_heads, rtol=1e-4)
+    assert np.all(mass[:, w.tokens:] == 0)
     # a block of 16 new query tokens, in the bench's launch configuration
     M = 16
     qm = synth.make_queries(w, M)
