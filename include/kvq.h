@@ -48,6 +48,9 @@
  *   sequence (mean of the two middle values for an even count, in fp64).
  * Attention: out = softmax(softmax_scale * q . k^) v^ over every cached token
  *   of the sequence, query head hq reads KV head hq / (q_heads / kv_heads).
+ *   kvq_decode_attn_multi does the same for a block of new query tokens (with
+ *   each row's log-sum-exp); kvq_decode_attn_mass also returns, per cached
+ *   token, its softmax weight summed over the query heads.
  *
  * Conventions for every entry point:
  *   - Device pointers are HIP device pointers, 16-byte aligned.  `stream` is
@@ -55,7 +58,8 @@
  *     that stream; the library never allocates, frees or synchronizes.
  *   - The caller owns every buffer.  Inputs are read-only.  The cache is one
  *     device buffer of kvq_layout.total_bytes, written by kvq_quantize and
- *     kvq_append, read by kvq_decode_attn.
+ *     kvq_append, read by kvq_decode_attn, kvq_decode_attn_multi and
+ *     kvq_decode_attn_mass.
  *   - Arguments are validated on the host before any launch; on error the
  *     call returns a nonzero kvq_status and launches nothing.  A failed
  *     launch returns KVQ_ERR_LAUNCH.  Faults inside kernels surface at the
