@@ -137,8 +137,10 @@ __device__ inline void load_q(const uint16_t* q, int b, int hk, int Hkv, float (
   }
 }
 
-// kchan: blockIdx.z == 0 -> quantized tokens (per-channel keys + sparse),
-// blockIdx.z == 1 -> the fp16 window (a single chunk).
+// Per-channel-key cache on the VALU, for the shapes the matrix-core kernel
+// does not cover: blockIdx.z == 0 -> chunk blockIdx.x of the quantized tokens
+// (per-channel keys + sparse), blockIdx.z == 1 -> chunk blockIdx.x of the
+// fp16 window (kWinChunk tokens).
 __global__ __launch_bounds__(kDecThreads) void k_decode_kchan(DecodeArgs a) {
   __shared__ float qf[kGqa][kD];
   __shared__ float qs[kGqa][kD];            // q * per-channel scale of the current key block

@@ -7,7 +7,7 @@
 
 namespace kvq {
 
-constexpr int kSortTile = 1024;   // keys per radix-sort block (256 threads x 4)
+constexpr int kSortTile = 1024;   // tokens per high-tier count segment and slot-scan workgroup
 constexpr int kMaxSortLen = 1 << 18;   // longest ranked sequence (tokens)
 constexpr int kMergeMaxT = 32768;      // up to this length: block sort + merge rank (keys in LDS)
 
