@@ -167,6 +167,25 @@ def test_kchan_quantize_and_decode(T):
     _check_kchan(w, inp, run)
 
 
+@pytest.mark.parametrize("kl,vl,vg,spv,win,T", [
+    (3, 4, 64, 1, 64, 1000),      # VALU decode, one sparse entry, short window
+    (8, 6, 128, 0, 0, 777),       # no sparse entries, no window beyond the ragged block tail
+    (16, 8, 32, 5, 200, 1500),    # 16-level keys (generic key kernel), five sparse entries
+    (4, 3, 32, 2, 17, 300),       # the matrix-core shape with an odd window
+])
+def test_kchan_other_shapes(kl, vl, vg, spv, win, T):
+    """Per-channel-key caches outside the matrix-core kernel's shape: the
+    generic key quantizer and the VALU decode (quantized chunks and fp16
+    window chunks)."""
+    w = C[4].shrink(name=f"kchan_k{kl}_v{vl}_g{vg}_s{spv}_w{win}_T{T}", batch=2, kv_heads=2, q_heads=8,
+                    tokens=T, k_levels=kl, v_levels=vl, v_group=vg, sparse_per_vec=spv, window=win)
+    log(f"case {w.name}")
+    inp = synth.make_inputs(w)
+    run = GpuRun(w, inp)
+    run.quantize()
+    _check_kchan(w, inp, run)
+
+
 def test_kchan_outlier_ties_and_degenerate_blocks():
     """Sparse outliers under magnitude ties (lower channel wins, +x and -x
     tie), all-zero and -0 key rows (channels 0 and 1 are taken), constant
