@@ -172,6 +172,7 @@ def test_kchan_quantize_and_decode(T):
     (8, 6, 128, 0, 0, 777),       # no sparse entries, no window beyond the ragged block tail
     (16, 8, 32, 5, 200, 1500),    # 16-level keys (generic key kernel), five sparse entries
     (4, 3, 32, 2, 17, 300),       # the matrix-core shape with an odd window
+    (9, 16, 64, 3, 128, 900),     # values past 8 levels (generic pool quantizer)
 ])
 def test_kchan_other_shapes(kl, vl, vg, spv, win, T):
     """Per-channel-key caches outside the matrix-core kernel's shape: the
