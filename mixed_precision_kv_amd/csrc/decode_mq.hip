@@ -159,6 +159,14 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
     int spos[KT];
 #pragma unroll
     for (int t = 0; t < KT; ++t) spos[t] = ppos_lds[16 * t + n];
+    // the A operands stay in registers when they fit beside the rest
+    constexpr bool kAqRegs = KM <= 5;
+    h8 aqr[kAqRegs ? NS : 1][kAqRegs ? KM : 1];
+    if (kAqRegs)
+#pragma unroll
+      for (int sg = 0; sg < NS; ++sg)
+#pragma unroll
+        for (int mo = 0; mo < KM; ++mo) aqr[kAqRegs ? sg : 0][kAqRegs ? mo : 0] = aq_lds[sg][mo][lane];
     float m_run[kGqa], l_run[kGqa];
 #pragma unroll
     for (int h = 0; h < kGqa; ++h) { m_run[h] = -INFINITY; l_run[h] = 0.f; }
@@ -187,7 +195,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
             f4 pr = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int mo = 0; mo < KM; ++mo)
-              pr = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq_lds[sg][mo][lane], bk[mo], pr, 0, 0, 0);
+              pr = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                  kAqRegs ? aqr[kAqRegs ? sg : 0][kAqRegs ? mo : 0] : aq_lds[sg][mo][lane], bk[mo], pr, 0, 0, 0);
             const uint32_t meta = km_lds[(t * NG + sg / SUB) * 16 + n];
             const float sgf = h2f(meta & 0xFFFFu) * MUL;
             const float ssc = sgf * a.c, zz = AFF ? h2f(meta >> 16) - sgf : h2f(meta >> 16);
