@@ -10,8 +10,9 @@
 // matrix instruction: four query tokens x four heads, r = 4 m + h, instead of
 // four 32-channel sub-groups x four heads.  The digits of a key tile are
 // expanded once and multiplied by four A operands (one per sub-group, zero
-// outside it); the value digits of a channel tile once, against A = p * s of
-// that tile's sub-group.  So the expansion work, the part that bounds one
+// outside it; held in registers where they fit, else read from LDS); the
+// value digits of a channel tile once, against A = p * s of that tile's
+// sub-group.  So the expansion work, the part that bounds one
 // query, is shared by four query tokens.
 //   keys wave:   lane (n, j) gets rows (j, 0..3) of column n: query j, four
 //                heads, slot n; per sub-group it adds s_g * P + z_g * Q_g
