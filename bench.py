@@ -313,8 +313,9 @@ def main():
                     help="profiling aid: run just one kernel family (no JSON line)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (see the sharding "
-              "notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (independent "
+              "(sequence, KV head) units would shard across GPUs with no exchange); run with --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

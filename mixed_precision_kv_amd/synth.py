@@ -94,6 +94,11 @@ CONFIGS = [
              v_group=32, window=128, sparse_per_vec=2),
 ]
 BY_NAME = {w.name: w for w in CONFIGS}
+W_SINGLE = BY_NAME["c1_single_head_t4096"]     # 1 x 4096 tokens, one KV head
+W_LLAMA = BY_NAME["c2_llama8b_b8_t32k"]        # 8 x 32768 tokens, Llama-3.1-8B-shaped layer
+W_LONG = BY_NAME["c3_long_b1_t128k"]           # 1 x 131072 tokens, 8/6 levels, G 64
+W_APPEND = BY_NAME["c4_append_b64_t16k"]       # 64 x 16384 prefix + 256 appends
+W_KCHAN = BY_NAME["c5_kchan_b4_t64k"]          # 4 x 65536, per-channel keys
 
 
 CHUNK = 1 << 22

@@ -69,7 +69,7 @@ def test_layout_of_every_workload(w):
 
 
 def _cfg(**kw):
-    c = kvq.config_for(synth.CONFIGS[0])
+    c = kvq.config_for(synth.W_SINGLE)
     for k, v in kw.items():
         setattr(c, k, v)
     return c
@@ -87,7 +87,7 @@ def test_layout_rejects(kw, status):
 
 
 def test_kchan_rejects_unsupported():
-    w = synth.CONFIGS[4]
+    w = synth.W_KCHAN
     for kw in (dict(k_block=64), dict(v_levels=5), dict(window=600), dict(sparse_per_vec=9)):
         c = kvq.config_for(w)
         for k, v in kw.items():
@@ -139,7 +139,7 @@ def test_append_validation():
         with pytest.raises(kvq.KvqError) as e:
             kvq.append(lay, *args, stream=0)
         assert e.value.status == 1
-    lay5 = kvq.layout_init(kvq.config_for(synth.CONFIGS[4]))
+    lay5 = kvq.layout_init(kvq.config_for(synth.W_KCHAN))
     with pytest.raises(kvq.KvqError) as e:
         kvq.append(lay5, FAKE, FAKE, FAKE, FAKE, stream=0)
     assert e.value.status == 2
@@ -182,7 +182,7 @@ def test_decode_multi_workspace_and_mode():
     assert one > 0 and kvq.multi_workspace_bytes(lay, 5, 4096) == 2 * one   # four queries a group
     assert kvq.multi_workspace_bytes(lay, 0, 4096) == 0
     assert kvq.multi_workspace_bytes(lay, 4, 4097) == 0
-    lay5 = kvq.layout_init(kvq.config_for(synth.CONFIGS[4]))
+    lay5 = kvq.layout_init(kvq.config_for(synth.W_KCHAN))
     assert kvq.multi_workspace_bytes(lay5, 4, 1024) == 0
     with pytest.raises(kvq.KvqError) as e:
         kvq.decode_attn_multi(lay5, FAKE, FAKE, 4, 0.088, 1024, FAKE, None, FAKE, ws_bytes=1 << 40,
@@ -211,7 +211,7 @@ def test_decode_mass_workspace_and_mode():
     extra = kvq.workspace_bytes(lay, kvq.OP_DECODE_MASS, 4096) - plain
     U = lay.cfg.batch * lay.cfg.kv_heads
     assert extra == U * 4 * (lay.cap[0] + lay.cap[1]) * 4 + U * 4 * 8
-    lay5 = kvq.layout_init(kvq.config_for(synth.CONFIGS[4]))
+    lay5 = kvq.layout_init(kvq.config_for(synth.W_KCHAN))
     assert kvq.workspace_bytes(lay5, kvq.OP_DECODE_MASS, 1024) == 0
     with pytest.raises(kvq.KvqError) as e:
         kvq.decode_attn_mass(lay5, FAKE, FAKE, 0.088, 1024, FAKE, FAKE, FAKE, ws_bytes=1 << 40, stream=0)

@@ -13,7 +13,6 @@ from gpu_harness import (GpuRun, TOL, compare_tiered_unit, log, oracle_tiers,
                          oracle_unit_attention)
 
 pytestmark = pytest.mark.gpu
-C = synth.CONFIGS
 
 
 def _sample_units(w):
@@ -29,9 +28,8 @@ def _bounded(out, v):
     assert np.abs(o).max() <= vmax * 1.01 + 1e-2
 
 
-@pytest.mark.parametrize("idx", [0, 1, 2], ids=lambda i: C[i].name)
-def test_tiered_fullsize(idx):
-    w = C[idx]
+@pytest.mark.parametrize("w", [synth.W_SINGLE, synth.W_LLAMA, synth.W_LONG], ids=lambda w: w.name)
+def test_tiered_fullsize(w):
     log(f"case {w.name} full size")
     inp = synth.make_inputs(w, steps=0)
     run = GpuRun(w, inp)
@@ -81,7 +79,7 @@ def test_append_fullsize():
     decode.  Tier decisions of every sequence at every step (token map),
     counters and sorted scores at the end; words of sampled units at the end;
     attention of sampled units at sampled steps."""
-    w = C[3]
+    w = synth.W_APPEND
     log(f"case {w.name} full size, {w.append_steps} steps")
     inp = synth.make_inputs(w)
     run = GpuRun(w, inp, want_ranks=False)
@@ -132,7 +130,7 @@ def test_append_fullsize():
 
 
 def test_kchan_fullsize():
-    w = C[4]
+    w = synth.W_KCHAN
     log(f"case {w.name} full size")
     inp = synth.make_inputs(w)
     run = GpuRun(w, inp)

@@ -17,7 +17,6 @@ from gpu_harness import GpuRun, TOL, log, oracle_tiers, to_dev
 
 pytestmark = pytest.mark.gpu
 
-C = synth.CONFIGS
 LSE_TOL = 1e-4
 
 
@@ -64,7 +63,7 @@ def _check_multi(w, inp, run, qm, units=None):
 
 @pytest.mark.parametrize("M", [1, 3, 4, 9])
 def test_multi_query_c2_shape(M):
-    w = C[1].shrink(name="c2_small_mq", batch=2, kv_heads=2, q_heads=8, tokens=1999)
+    w = synth.W_LLAMA.shrink(name="c2_small_mq", batch=2, kv_heads=2, q_heads=8, tokens=1999)
     log(f"case {w.name} M{M}")
     inp = synth.make_inputs(w)
     run = GpuRun(w, inp, want_ranks=False)
@@ -76,7 +75,7 @@ def test_multi_query_c2_shape(M):
                                        (7, 5, 64, 1500)])
 def test_multi_query_level_pairs(lh, ll, g, T):
     """Every grid 3..8 (table and power-of-two digit paths) and group size."""
-    w = C[1].shrink(name=f"mq_levels_{lh}_{ll}_g{g}", batch=1, kv_heads=2, q_heads=8, tokens=T,
+    w = synth.W_LLAMA.shrink(name=f"mq_levels_{lh}_{ll}_g{g}", batch=1, kv_heads=2, q_heads=8, tokens=T,
                     levels_hi=lh, levels_lo=ll, group=g)
     log(f"case {w.name}")
     inp = synth.make_inputs(w)
@@ -88,7 +87,7 @@ def test_multi_query_level_pairs(lh, ll, g, T):
 @pytest.mark.parametrize("T,n_hi", [(1, 0), (17, 17), (193, 96)])
 def test_multi_query_edge_sizes(T, n_hi):
     """One token, an empty pool, ragged tails."""
-    w = C[1].shrink(name=f"mq_edge_T{T}_n{n_hi}", batch=2, kv_heads=1, q_heads=4, tokens=T,
+    w = synth.W_LLAMA.shrink(name=f"mq_edge_T{T}_n{n_hi}", batch=2, kv_heads=1, q_heads=4, tokens=T,
                     frac_hi=n_hi / T)
     log(f"case {w.name}")
     inp = synth.make_inputs(w)
@@ -100,7 +99,7 @@ def test_multi_query_edge_sizes(T, n_hi):
 def test_multi_query_matches_single_query_and_no_lse():
     """Query 0 of a block equals kvq_decode_attn on that query (both within the
     oracle bound), and a null lse pointer is accepted."""
-    w = C[1].shrink(name="mq_vs_one", batch=2, kv_heads=2, q_heads=8, tokens=1500)
+    w = synth.W_LLAMA.shrink(name="mq_vs_one", batch=2, kv_heads=2, q_heads=8, tokens=1500)
     log(f"case {w.name}")
     inp = synth.make_inputs(w)
     run = GpuRun(w, inp, want_ranks=False)

@@ -364,7 +364,7 @@ def test_row_rel_err_definition():
 
 # ------------------------------------------------------------ tiered unit ---
 def test_tiered_unit_roundtrip_small():
-    w = synth.CONFIGS[0].shrink(tokens=300, name="tiny")
+    w = synth.W_SINGLE.shrink(tokens=300, name="tiny")
     inp = synth.make_inputs(w)
     rank = O.rank_desc(inp.scores)
     tokmap, counts, inv = O.tiers_and_slots(rank, w.n_hi)
@@ -384,7 +384,7 @@ def test_tiered_unit_roundtrip_small():
 
 # ----------------------------------------------------------------- kchan ---
 def test_kchan_unit_structure():
-    w = synth.CONFIGS[4].shrink(tokens=128 * 3 + 50, batch=1, kv_heads=1, q_heads=4, name="tiny5")
+    w = synth.W_KCHAN.shrink(tokens=128 * 3 + 50, batch=1, kv_heads=1, q_heads=4, name="tiny5")
     inp = synth.make_inputs(w)
     k, v = inp.k[0, :, 0], inp.v[0, :, 0]
     u = O.KChanUnit(k, v, w)
@@ -416,7 +416,7 @@ def test_storage_ratio_closed_forms():
     assert O.tiered_unit_bytes(16384, 16384, 6, 5, 32, D) == hi + lo
     fp16 = 32768 * 128 * 2 * 2
     assert abs(O.storage_ratio(fp16, hi + lo) - 16777216 / 3769856) < 1e-12
-    w = synth.CONFIGS[4]
+    w = synth.W_KCHAN
     nq = 65408
     b = nq * 32 + 511 * 512 + nq * 8 + (-(-nq // 20)) * 512 + nq * 16 + 128 * 512
     assert O.kchan_unit_bytes(65536, w, D) == b

@@ -11,7 +11,6 @@ from gpu_harness import GpuRun, TOL, compare_tiered_unit, log, oracle_tiers, ora
 
 pytestmark = pytest.mark.gpu
 
-C = synth.CONFIGS
 
 
 def _check_tiered(w, inp, run, decode=True):
@@ -44,10 +43,10 @@ def _check_tiered(w, inp, run, decode=True):
 
 
 SMALL = [
-    C[0],                                                            # config 1 at full size
-    C[1].shrink(name="c2_small", batch=2, kv_heads=2, q_heads=8, tokens=1999),
-    C[2].shrink(name="c3_small", batch=1, kv_heads=2, q_heads=8, tokens=3001),
-    C[3].shrink(name="c4_prefix_small", batch=3, kv_heads=2, q_heads=8, tokens=777, append_steps=0),
+    synth.W_SINGLE,                                                            # config 1 at full size
+    synth.W_LLAMA.shrink(name="c2_small", batch=2, kv_heads=2, q_heads=8, tokens=1999),
+    synth.W_LONG.shrink(name="c3_small", batch=1, kv_heads=2, q_heads=8, tokens=3001),
+    synth.W_APPEND.shrink(name="c4_prefix_small", batch=3, kv_heads=2, q_heads=8, tokens=777, append_steps=0),
 ]
 
 
@@ -64,7 +63,7 @@ def test_tiered_quantize_and_decode(w):
 def test_tiered_level_pairs(lh, ll, g):
     """Every grid size 3..8 and group size of the tiered path (codes per
     word 20, 16, 13, 12, 11, 10), with decode over the result."""
-    w = C[1].shrink(name=f"levels_{lh}_{ll}_g{g}", batch=2, kv_heads=2, q_heads=8, tokens=1201,
+    w = synth.W_LLAMA.shrink(name=f"levels_{lh}_{ll}_g{g}", batch=2, kv_heads=2, q_heads=8, tokens=1201,
                     levels_hi=lh, levels_lo=ll, group=g)
     log(f"case {w.name}")
     inp = synth.make_inputs(w)
@@ -75,7 +74,7 @@ def test_tiered_level_pairs(lh, ll, g):
 
 @pytest.mark.parametrize("T,n_hi", [(1, 0), (1, 1), (17, 0), (17, 17), (193, 96), (640, 320)])
 def test_tiered_edge_sizes(T, n_hi):
-    w = C[1].shrink(name=f"edge_T{T}_n{n_hi}", batch=2, kv_heads=1, q_heads=4, tokens=T,
+    w = synth.W_LLAMA.shrink(name=f"edge_T{T}_n{n_hi}", batch=2, kv_heads=1, q_heads=4, tokens=T,
                     frac_hi=n_hi / T)
     assert w.n_hi == n_hi
     log(f"case {w.name}")
@@ -90,7 +89,7 @@ def test_tiered_long_sequences_with_ties(T):
     """Sequences longer than one workgroup's LDS of sorted keys (the ranks
     add partial counts over groups of blocks, the last group partial), with
     runs of equal scores across block and group boundaries."""
-    w = C[2].shrink(name=f"long_T{T}", batch=2, kv_heads=1, q_heads=4, tokens=T)
+    w = synth.W_LONG.shrink(name=f"long_T{T}", batch=2, kv_heads=1, q_heads=4, tokens=T)
     log(f"case {w.name}")
     inp = synth.make_inputs(w)
     inp.scores[0] = np.round(inp.scores[0] * 4) / 4            # few distinct values: long tie runs
@@ -103,7 +102,7 @@ def test_tiered_long_sequences_with_ties(T):
 def test_tiered_ties_zeros_and_constant_groups():
     """Equal scores (stable order decides), -0/+0 scores, constant groups
     (scale 0), signed zeros in the data."""
-    w = C[1].shrink(name="degenerate", batch=2, kv_heads=2, q_heads=8, tokens=500)
+    w = synth.W_LLAMA.shrink(name="degenerate", batch=2, kv_heads=2, q_heads=8, tokens=500)
     log(f"case {w.name}")
     inp = synth.make_inputs(w)
     inp.scores[0, :] = np.float32(1.5)                       # all equal
@@ -159,7 +158,7 @@ def _check_kchan(w, inp, run, units=None):
 
 @pytest.mark.parametrize("T", [100, 255, 256, 434, 1408, 2000])
 def test_kchan_quantize_and_decode(T):
-    w = C[4].shrink(name=f"c5_T{T}", batch=2, kv_heads=2, q_heads=8, tokens=T)
+    w = synth.W_KCHAN.shrink(name=f"c5_T{T}", batch=2, kv_heads=2, q_heads=8, tokens=T)
     log(f"case {w.name}")
     inp = synth.make_inputs(w)
     run = GpuRun(w, inp)
@@ -178,7 +177,7 @@ def test_kchan_other_shapes(kl, vl, vg, spv, win, T):
     """Per-channel-key caches outside the matrix-core kernel's shape: the
     generic key quantizer and the VALU decode (quantized chunks and fp16
     window chunks)."""
-    w = C[4].shrink(name=f"kchan_k{kl}_v{vl}_g{vg}_s{spv}_w{win}_T{T}", batch=2, kv_heads=2, q_heads=8,
+    w = synth.W_KCHAN.shrink(name=f"kchan_k{kl}_v{vl}_g{vg}_s{spv}_w{win}_T{T}", batch=2, kv_heads=2, q_heads=8,
                     tokens=T, k_levels=kl, v_levels=vl, v_group=vg, sparse_per_vec=spv, window=win)
     log(f"case {w.name}")
     inp = synth.make_inputs(w)
@@ -191,7 +190,7 @@ def test_kchan_outlier_ties_and_degenerate_blocks():
     """Sparse outliers under magnitude ties (lower channel wins, +x and -x
     tie), all-zero and -0 key rows (channels 0 and 1 are taken), constant
     channels (scale 0) and tiny channel ranges (subnormal scales)."""
-    w = C[4].shrink(name="c5_edges", batch=1, kv_heads=2, q_heads=8, tokens=640)
+    w = synth.W_KCHAN.shrink(name="c5_edges", batch=1, kv_heads=2, q_heads=8, tokens=640)
     log(f"case {w.name}")
     inp = synth.make_inputs(w)
     k = inp.k
@@ -212,7 +211,7 @@ def test_kchan_outlier_ties_and_degenerate_blocks():
 def test_append_then_decode_small():
     """Generation-time quantization: every step's tier decision, slot, words
     and the attention after it, against the running-median oracle."""
-    w = C[3].shrink(name="c4_small", batch=3, kv_heads=2, q_heads=8, tokens=300, append_steps=40)
+    w = synth.W_APPEND.shrink(name="c4_small", batch=3, kv_heads=2, q_heads=8, tokens=300, append_steps=40)
     log(f"case {w.name}")
     inp = synth.make_inputs(w)
     run = GpuRun(w, inp)
@@ -255,7 +254,7 @@ def test_append_then_decode_small():
 
 def test_append_pool_full_flag():
     """A sequence whose tier pool is full is left unchanged and flagged."""
-    w = C[3].shrink(name="c4_full", batch=2, kv_heads=1, q_heads=4, tokens=64, append_steps=2)
+    w = synth.W_APPEND.shrink(name="c4_full", batch=2, kv_heads=1, q_heads=4, tokens=64, append_steps=2)
     inp = synth.make_inputs(w)
     run = GpuRun(w, inp)
     run.quantize()

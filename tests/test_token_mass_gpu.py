@@ -15,7 +15,6 @@ from oracle import kvq_oracle as O
 from gpu_harness import GpuRun, TOL, log, oracle_tiers, oracle_unit_attention, to_dev
 
 pytestmark = pytest.mark.gpu
-C = synth.CONFIGS
 
 
 def _decode_mass(run, q_np, max_len):
@@ -75,7 +74,7 @@ def _setup(w):
 
 @pytest.mark.parametrize("lh,ll,g,T", [(6, 5, 32, 1999), (8, 6, 64, 3001), (4, 3, 128, 1201), (8, 7, 32, 1)])
 def test_token_mass_after_quantize(lh, ll, g, T):
-    w = C[1].shrink(name=f"mass_{lh}_{ll}_g{g}_T{T}", batch=2, kv_heads=2, q_heads=8, tokens=T,
+    w = synth.W_LLAMA.shrink(name=f"mass_{lh}_{ll}_g{g}_T{T}", batch=2, kv_heads=2, q_heads=8, tokens=T,
                     levels_hi=lh, levels_lo=ll, group=g)
     log(f"case {w.name}")
     inp, run, pools, inv = _setup(w)
@@ -85,7 +84,7 @@ def test_token_mass_after_quantize(lh, ll, g, T):
 
 def test_token_mass_after_appends():
     """Appended tokens get their mass at their token index."""
-    w = C[3].shrink(name="mass_append", batch=2, kv_heads=2, q_heads=8, tokens=300, append_steps=5)
+    w = synth.W_APPEND.shrink(name="mass_append", batch=2, kv_heads=2, q_heads=8, tokens=300, append_steps=5)
     log(f"case {w.name}")
     inp, run, pools, inv = _setup(w)
     med = [O.RunningMedian(inp.scores[b]) for b in range(w.batch)]
