@@ -62,6 +62,10 @@ class Workload:
     # input distribution
     outlier_channels: int = 4
     outlier_scale: float = 10.0
+    outlier_stride: int = 1           # outlier key channels at 0, stride, 2*stride, ...
+    # channel rearrangement and clipped group ranges (tiered mode)
+    reorder: bool = False             # store the channel orders of channel_orders()
+    clip: float = 0.0                 # group min/max scale factor; 0: no clipping
     seed: int = 0
 
     @property
@@ -99,6 +103,11 @@ W_LLAMA = BY_NAME["c2_llama8b_b8_t32k"]        # 8 x 32768 tokens, Llama-3.1-8B-
 W_LONG = BY_NAME["c3_long_b1_t128k"]           # 1 x 131072 tokens, 8/6 levels, G 64
 W_APPEND = BY_NAME["c4_append_b64_t16k"]       # 64 x 16384 prefix + 256 appends
 W_KCHAN = BY_NAME["c5_kchan_b4_t64k"]          # 4 x 65536, per-channel keys
+# The Llama-shaped layer with rearranged channels and clipped group ranges
+# (SKVQ abstract): one outlier key channel in every group of 32 in the input,
+# brought into one group by the stored order; clip factor 0.9.
+W_SKVQ = W_LLAMA.shrink(name="skvq_llama8b_b8_t32k", outlier_stride=32, reorder=True, clip=0.9)
+BY_NAME[W_SKVQ.name] = W_SKVQ
 
 
 CHUNK = 1 << 22
@@ -158,7 +167,7 @@ def make_inputs(w: Workload, steps: Optional[int] = None) -> Inputs:
     n_steps = w.append_steps if steps is None else min(steps, w.append_steps)
     kids = np.random.SeedSequence(w.seed).spawn(4 + 4 * w.append_steps)
     col = np.ones(D, dtype=np.float32)
-    col[:w.outlier_channels] = np.float32(w.outlier_scale)
+    col[:w.outlier_channels * w.outlier_stride:w.outlier_stride] = np.float32(w.outlier_scale)
     k = _draw_f16(kids[0], (B, T, H, D), col)
     v = _draw_f16(kids[1], (B, T, H, D))
     scores = _draw_scores(kids[2], (B, T), w.score_sigma) if w.mode == TIERED else None
@@ -177,3 +186,20 @@ def make_queries(w: Workload, n_queries: int, seed: int = 1) -> np.ndarray:
     cache inputs of the workload are unchanged."""
     ss = np.random.SeedSequence([w.seed, 1000 + seed])
     return _draw_f16(ss, (w.batch, n_queries, w.q_heads, w.head_dim))
+
+
+def channel_orders(w: Workload) -> np.ndarray:
+    """Stored channel orders int32 [2][Hkv][D] (keys, values) standing in for
+    an order calibrated offline: keys put the input's outlier channels first
+    (ascending), then the others ascending; values take a seeded random order
+    per KV head (their channels are alike, so it only exercises the layout).
+    Entry p is the input channel stored at position p."""
+    D, H = w.head_dim, w.kv_heads
+    out = np.empty((2, H, D), dtype=np.int32)
+    outl = np.arange(w.outlier_channels) * w.outlier_stride
+    rest = np.setdiff1d(np.arange(D), outl)
+    out[0] = np.concatenate([outl, rest])[None, :]
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, 2000])))
+    for h in range(H):
+        out[1, h] = g.permutation(D)
+    return out

@@ -48,6 +48,12 @@ supports; all are listed in the design notes):
   values per token in groups of v_group.  k^ = deq(dense) + sparse.
 * Attention: o = softmax(scale * q . k^) v^ in fp64 over every cached token,
   query head hq reads KV head hq // (Hq / Hkv).
+* [SKVQ] Abstract, channel rearrangement and clipped group ranges (tiered
+  mode, optional): a fixed channel order per KV head for keys and for values
+  (stored position p holds channel order[p]; groups are runs of G positions);
+  the group minimum and maximum are each scaled by a clip factor in (0, 1]
+  (fp32 product, fp16 RNE) before the grid is formed, values outside take the
+  end codes.
 """
 from __future__ import annotations
 
@@ -88,9 +94,15 @@ def _f16_total_order_key(x16: np.ndarray) -> np.ndarray:
     return np.where(b & 0x8000, -(b & 0x7FFF) - 1, b)
 
 
-def quantize_groups(x16: np.ndarray, L: int):
+def quantize_groups(x16: np.ndarray, L: int, clip=None):
     """[SemKV] Abstract (uniform affine quantizer on an L-level grid), applied
     to every group along the last axis.
+
+    clip (0 < clip <= 1, or None): [SKVQ] Abstract, clipped dynamic
+    quantization at the group level.  Reading: the group's minimum and maximum
+    are each multiplied by clip in fp32 and rounded to fp16 (RNE) before the
+    grid is formed from them; values outside the clipped range take the end
+    codes 0 and L - 1.  clip = 1 leaves both unchanged.
 
     x16: fp16 [..., G].  Returns (codes uint8 [..., G], scale fp16 [...],
     zero fp16 [...]).
@@ -102,6 +114,10 @@ def quantize_groups(x16: np.ndarray, L: int):
     i_mx = np.argmax(key, axis=-1)[..., None]
     mn = np.take_along_axis(x16, i_mn, axis=-1)[..., 0]
     mx = np.take_along_axis(x16, i_mx, axis=-1)[..., 0]
+    if clip is not None:
+        assert 0.0 < clip <= 1.0
+        mn = (mn.astype(F32) * F32(clip)).astype(np.float16)   # fp32 product, then fp16 RNE
+        mx = (mx.astype(F32) * F32(clip)).astype(np.float16)
     rng32 = mx.astype(F32) - mn.astype(F32)            # fp32, round to nearest even
     s32 = rng32 / F32(L - 1)                            # IEEE fp32 division
     s16 = s32.astype(np.float16)                        # RNE, subnormals kept
@@ -200,10 +216,23 @@ def tiers_and_slots(rank: np.ndarray, n_hi: int):
 
 # ------------------------------------------------------ tiered cache unit ---
 class Pool:
-    """Canonical contents of one tier pool of one (sequence, KV head)."""
+    """Canonical contents of one tier pool of one (sequence, KV head).
 
-    def __init__(self, L: int, G: int, D: int):
+    order_k / order_v (int [D] or None): [SKVQ] Abstract, the channels of
+    the KV cache rearranged so that the channels sharing a quantization group
+    are alike.  Reading: a fixed order per KV head for keys and one for values;
+    position p of a stored row holds channel order[p], so groups are runs of G
+    positions in that order and the codes are stored in it.  ``k_hat`` and
+    ``v_hat`` return rows in the original channel order.  clip: see
+    ``quantize_groups``."""
+
+    def __init__(self, L: int, G: int, D: int, order_k=None, order_v=None, clip=None):
         self.L, self.G, self.D = L, G, D
+        self.order_k = None if order_k is None else np.asarray(order_k, dtype=np.int64)
+        self.order_v = None if order_v is None else np.asarray(order_v, dtype=np.int64)
+        for o in (self.order_k, self.order_v):
+            assert o is None or np.array_equal(np.sort(o), np.arange(D)), "not a permutation"
+        self.clip = clip
         self.k_codes = np.zeros((0, D), np.uint8)
         self.k_scale = np.zeros((0, D // G), np.float16)
         self.k_zero = np.zeros((0, D // G), np.float16)
@@ -221,8 +250,12 @@ class Pool:
         if N == 0:
             return
         ng = self.D // self.G
-        kc, ks, kz = quantize_groups(k16.reshape(N, ng, self.G), self.L)
-        vc, vs, vz = quantize_groups(v16.reshape(N, ng, self.G), self.L)
+        if self.order_k is not None:
+            k16 = k16[:, self.order_k]                  # stored position p <- channel order[p]
+        if self.order_v is not None:
+            v16 = v16[:, self.order_v]
+        kc, ks, kz = quantize_groups(k16.reshape(N, ng, self.G), self.L, self.clip)
+        vc, vs, vz = quantize_groups(v16.reshape(N, ng, self.G), self.L, self.clip)
         self.k_codes = np.concatenate([self.k_codes, kc.reshape(N, self.D)])
         self.k_scale = np.concatenate([self.k_scale, ks])
         self.k_zero = np.concatenate([self.k_zero, kz])
@@ -236,24 +269,35 @@ class Pool:
     def v_words(self):
         return pack_cols(self.v_codes, self.L)
 
+    @staticmethod
+    def _original_order(rows, order):
+        if order is None:
+            return rows
+        out = np.empty_like(rows)
+        out[:, order] = rows                            # channel order[p] <- stored position p
+        return out
+
     def k_hat(self):
         N, ng = self.n, self.D // self.G
-        return dequantize_groups(self.k_codes.reshape(N, ng, self.G), self.k_scale,
-                                 self.k_zero).reshape(N, self.D)
+        deq = dequantize_groups(self.k_codes.reshape(N, ng, self.G), self.k_scale,
+                                self.k_zero).reshape(N, self.D)
+        return self._original_order(deq, self.order_k)
 
     def v_hat(self):
         N, ng = self.n, self.D // self.G
-        return dequantize_groups(self.v_codes.reshape(N, ng, self.G), self.v_scale,
-                                 self.v_zero).reshape(N, self.D)
+        deq = dequantize_groups(self.v_codes.reshape(N, ng, self.G), self.v_scale,
+                                self.v_zero).reshape(N, self.D)
+        return self._original_order(deq, self.order_v)
 
 
 def quantize_tiered_unit(k_unit: np.ndarray, v_unit: np.ndarray, inv_b, L_hi: int, L_lo: int,
-                         G: int):
+                         G: int, order_k=None, order_v=None, clip=None):
     """[SemKV] Abstract: every token of one (sequence, KV head) is quantized on
     its tier's grid and stored, none dropped.  k_unit, v_unit fp16 [T][D];
-    inv_b = (tokens_hi, tokens_lo) in slot order.  Returns (Pool hi, Pool lo)."""
+    inv_b = (tokens_hi, tokens_lo) in slot order.  Channel orders and clip as
+    in ``Pool`` (None: the plain quantizer).  Returns (Pool hi, Pool lo)."""
     D = k_unit.shape[1]
-    pools = (Pool(L_hi, G, D), Pool(L_lo, G, D))
+    pools = (Pool(L_hi, G, D, order_k, order_v, clip), Pool(L_lo, G, D, order_k, order_v, clip))
     for p, toks in enumerate(inv_b):
         pools[p].add_rows(k_unit[toks], v_unit[toks])
     return pools

@@ -421,3 +421,125 @@ def test_storage_ratio_closed_forms():
     b = nq * 32 + 511 * 512 + nq * 8 + (-(-nq // 20)) * 512 + nq * 16 + 128 * 512
     assert O.kchan_unit_bytes(65536, w, D) == b
     assert 5.5 < O.storage_ratio(65536 * 512, b) < 6.0
+
+
+# ------------------------------------------- channel order and clipping ---
+def test_clip_worked_examples():
+    """Hand-worked clipped groups (fixture cites SKVQ, Abstract)."""
+    rows = _golden("skvq_clip_examples.txt")
+    assert len(rows) == 4
+    for r in rows:
+        clip, L, scale, zero, n = float(r[0]), int(r[1]), float(r[2]), float(r[3]), int(r[4])
+        x = np.array([float(t) for t in r[5:5 + n]], dtype=np.float16)
+        want = [int(t) for t in r[5 + n:5 + 2 * n]]
+        c, s, z = O.quantize_groups(x[None, :], L, clip)
+        assert c[0].tolist() == want, (r, c)
+        assert float(s[0]) == scale and float(z[0]) == zero
+
+
+def test_clip_one_is_the_plain_quantizer():
+    rng = np.random.default_rng(11)
+    x = _f16_groups(rng, (400, 4, 32), 3.0)
+    for L in (3, 5, 6, 8):
+        a = O.quantize_groups(x, L)
+        b = O.quantize_groups(x, L, 1.0)
+        for u, v in zip(a, b):
+            assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
+
+
+@pytest.mark.parametrize("clip", [0.5, 0.8, 0.95])
+def test_clip_codes_are_the_nearest_clipped_grid_point(clip):
+    """Brute force: every code is the grid point z + c s (c in 0..L-1) nearest
+    to x, with z and s formed from the clipped min and max worked out here in
+    exact arithmetic; values beyond the clipped range take the end codes."""
+    rng = np.random.default_rng(int(clip * 100))
+    x = _f16_groups(rng, (300, 32), 2.0)
+    x[::7, 3] = np.float16(25.0)                       # a heavy tail in some groups
+    for L in (3, 5, 8):
+        c, s, z = O.quantize_groups(x, L, clip)
+        for g in range(x.shape[0]):
+            xs = [Fraction(float(t)) for t in x[g]]
+            lo = Fraction(float(np.float16(np.float32(min(xs)) * np.float32(clip))))
+            hi = Fraction(float(np.float16(np.float32(max(xs)) * np.float32(clip))))
+            assert Fraction(float(z[g])) == lo
+            sf = Fraction(float(s[g]))
+            assert abs(sf - (hi - lo) / (L - 1)) <= sf * Fraction(1, 1024) + Fraction(1, 2 ** 24)
+            if sf == 0:
+                assert not c[g].any()
+                continue
+            for xi, ci in zip(xs, c[g].tolist()):
+                errs = [abs(xi - (lo + k * sf)) for k in range(L)]
+                assert errs[ci] <= min(errs) + sf * Fraction(1, 10 ** 5), (g, xi, ci)
+
+
+def _lossless_pattern(D=128):
+    """Rows whose channel d holds a value that depends only on d % 4 (keys)
+    or (d // 2) % 4 (values): grouped by that key every group of 32 is
+    constant, so a stored order that sorts by it quantizes without loss.
+    Neither order is its own inverse, so applying one backwards is caught."""
+    kd, vd = np.arange(D) % 4, (np.arange(D) // 2) % 4
+    k = np.stack([(kd * (r + 1) - 3).astype(np.float16) for r in range(5)])
+    v = np.stack([(vd * 0.5 * (r + 1) + 1).astype(np.float16) for r in range(5)])
+    order_k = np.argsort(kd, kind="stable")
+    order_v = np.argsort(vd, kind="stable")
+    return k, v, order_k, order_v
+
+
+def test_channel_order_that_makes_groups_constant_is_lossless():
+    """SKVQ, Abstract: rearranging channels makes each quantization group's
+    channels alike.  In the extreme case every group is constant, the scale
+    is 0 and the reconstruction is exact, in the original channel order."""
+    k, v, ok, ov = _lossless_pattern()
+    p = O.Pool(3, 32, 128, ok, ov)
+    p.add_rows(k, v)
+    assert np.array_equal(p.k_hat(), k.astype(np.float64))
+    assert np.array_equal(p.v_hat(), v.astype(np.float64))
+    assert not p.k_scale.astype(np.float64).any() and not p.v_scale.astype(np.float64).any()
+    # the stored codes follow the order: position p holds channel order[p]
+    assert np.array_equal(p.k_zero[:, 1].astype(np.float64), k[:, ok[32]].astype(np.float64))
+    # the natural order and the inverse order both lose information
+    for a, b in ((None, None), (np.argsort(ok), np.argsort(ov))):
+        q = O.Pool(3, 32, 128, a, b)
+        q.add_rows(k, v)
+        assert not np.array_equal(q.k_hat(), k.astype(np.float64))
+        assert not np.array_equal(q.v_hat(), v.astype(np.float64))
+
+
+def test_lossless_order_gives_plain_attention():
+    """With a lossless order the oracle's attention over the pool equals plain
+    attention over the raw rows (original channel order throughout)."""
+    k, v, ok, ov = _lossless_pattern()
+    p = O.Pool(3, 32, 128, ok, ov)
+    p.add_rows(k, v)
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((4, 128))
+    scale = 1 / math.sqrt(128)
+    got = O.attention_fp64(q, p.k_hat(), p.v_hat(), scale)
+    ref = _naive_attention(q, k.astype(np.float64), v.astype(np.float64), scale)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_channel_order_and_clip_lower_key_error_on_spread_outliers():
+    """The workload with one outlier key channel per group: its stored order
+    gathers the four outliers into the first stored group, so the 96 channels
+    stored in the other three groups no longer share a range with an outlier
+    and their key reconstruction error falls by more than half (the group
+    range shrinks from about one outlier to about two standard deviations
+    either side); clipping at 0.9 on these Gaussian groups lowers it further."""
+    w = synth.W_SKVQ.shrink(tokens=256, batch=1, kv_heads=1, q_heads=4, name="tiny_skvq")
+    inp = synth.make_inputs(w)
+    orders = synth.channel_orders(w)
+    k, v = inp.k[0, :, 0], inp.v[0, :, 0]
+    plain = O.Pool(6, 32, 128)
+    plain.add_rows(k, v)
+    skvq = O.Pool(6, 32, 128, orders[0, 0], orders[1, 0], w.clip)
+    skvq.add_rows(k, v)
+    normal = orders[0, 0, 32:]                         # channels stored outside the first group
+    assert not np.isin(normal, np.arange(4) * 32).any()
+    e_plain = np.abs(plain.k_hat() - k.astype(np.float64))[:, normal].mean()
+    e_skvq = np.abs(skvq.k_hat() - k.astype(np.float64))[:, normal].mean()
+    assert e_skvq < e_plain / 2, (e_plain, e_skvq)
+    unclipped = O.Pool(6, 32, 128, orders[0, 0], orders[1, 0])
+    unclipped.add_rows(k, v)
+    e_unclipped = np.abs(unclipped.k_hat() - k.astype(np.float64))[:, normal].mean()
+    assert e_skvq < e_unclipped, (e_unclipped, e_skvq)
