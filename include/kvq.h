@@ -32,6 +32,7 @@
  *
  * Quantizer (both modes, one group of values x_i, fp16):
  *   z = min x_i (IEEE total order, -0 < +0), m = max x_i,
+ *   (with clip: z = fp16_rne(fp32(z) * clip), m = fp16_rne(fp32(m) * clip)),
  *   s = fp16_rne( fp32(m - z) / fp32(L - 1) ),
  *   c_i = clamp( rint_even( fp32(x_i - z) / fp32(s) ), 0, L - 1 ),  s == 0 -> c_i = 0,
  *   dequantized value z + c_i * s.
@@ -114,6 +115,10 @@ typedef struct kvq_config {
   int32_t v_group;        /* values per value group: 32, 64 or 128 */
   int32_t window;         /* fp16 recent window, >= 0 */
   int32_t sparse_per_vec; /* fp16 outliers per key vector, 0..8 */
+  /* tiered mode, optional (SKVQ, Abstract: channels rearranged so that each
+   * quantization group holds alike channels; clipped group ranges) */
+  int32_t reorder;        /* 1: stored channel orders (kvq_set_channel_order); 0: none */
+  float clip;             /* 0: none; else in (0, 1]: group min and max scaled by clip */
 } kvq_config;
 
 /* Filled by kvq_layout_init.  All offsets are bytes from the cache base;
@@ -131,6 +136,10 @@ typedef struct kvq_config {
  *       k_meta[p] / v_meta[p] + (((u * tiles[p] + s/16) * (D/group) + g) * 16 + s%16)
  *   value words (uint32), slot s at digit s % nv[p] of row r = s / nv[p]:
  *       v_words[p] + ((u * vrows[p] + r) * D + d)
+ *   with reorder = 1, channel orders uint8 [2][kv_heads][D] (keys, values):
+ *       chan_order + (kv * kv_heads + h) * D + p = the channel whose code,
+ *       like every index d above, sits at position p (groups are runs of
+ *       `group` positions)
  *
  * kchan mode (slots are token indices t < n_q, n_q = k_block *
  * floor((T - window) / k_block)):
@@ -156,6 +165,7 @@ typedef struct kvq_layout {
   int64_t counters, tokmap, sorted;
   int64_t k_words[2], k_meta[2], v_words[2], v_meta[2];
   int64_t sparse, k_win, v_win;
+  int64_t chan_order;     /* tiered with reorder = 1; else 0 */
   int64_t total_bytes;
 } kvq_layout;
 
@@ -170,6 +180,23 @@ size_t kvq_workspace_bytes(const kvq_layout* lay, int32_t op, int32_t max_len);
 
 /* Static string for a status code. */
 const char* kvq_status_str(kvq_status s);
+
+/* Stores the channel orders of a cache laid out with reorder = 1 (SKVQ,
+ * Abstract: the channels of the KV cache are rearranged so that the channels
+ * of each quantization group are alike; the order itself is calibrated
+ * offline by the caller).  Call it before kvq_quantize / kvq_append; the
+ * order is then used by every call on the cache: quantize and append read
+ * channel order[p] into position p, decode reads q through the key order and
+ * writes output channel order[p] from position p of the value sums.
+ *   order:  HOST int32 [2][kv_heads][D]: [0] keys, [1] values; every row a
+ *           permutation of 0..D-1 (else KVQ_ERR_ARG, nothing launched).
+ *   One small launch per KV head on `stream` carries the bytes as kernel
+ *   arguments; `order` may be reused as soon as the call returns.
+ * KVQ_ERR_UNSUPPORTED if the cache was laid out with reorder = 0.  Without
+ * this call such a cache gives undefined results (every access still stays
+ * inside the cache and the caller's buffers). */
+kvq_status kvq_set_channel_order(const kvq_layout* lay, void* cache, const int32_t* order,
+                                 void* stream);
 
 /* Quantize-on-write of a whole prefix (SemKV Abstract: rank, two adjacent
  * grids, every token kept; KVQuant / SKVQ for kchan mode).

@@ -79,6 +79,8 @@ extern "C" kvq_status kvq_layout_init(const kvq_config* cfg, kvq_layout* out) {
   if (c.mode == KVQ_MODE_TIERED) {
     if (!decode_levels_ok(c.levels_hi) || !decode_levels_ok(c.levels_lo) || !group_ok(c.group))
       return KVQ_ERR_UNSUPPORTED;
+    if (c.reorder != 0 && c.reorder != 1) return KVQ_ERR_ARG;
+    if (!(c.clip == 0.0f || (c.clip > 0.0f && c.clip <= 1.0f))) return KVQ_ERR_ARG;
     if (c.cap_hi < 0 || c.cap_lo < 0) return KVQ_ERR_ARG;
     L.cap[0] = c.cap_hi ? c.cap_hi : c.capacity;
     L.cap[1] = c.cap_lo ? c.cap_lo : c.capacity;
@@ -99,7 +101,9 @@ extern "C" kvq_status kvq_layout_init(const kvq_config* cfg, kvq_layout* out) {
       L.v_words[p] = off; off = align256(off + U * L.vrows[p] * D * 4);
       L.v_meta[p] = off;  off = align256(off + U * L.tiles[p] * ng * kTile * 4);
     }
+    if (c.reorder) { L.chan_order = off; off = align256(off + 2 * (int64_t)c.kv_heads * D); }
   } else if (c.mode == KVQ_MODE_KCHAN) {
+    if (c.reorder != 0 || c.clip != 0.0f) return KVQ_ERR_UNSUPPORTED;
     if (!levels_ok(c.k_levels) || !levels_ok(c.v_levels) || !group_ok(c.v_group))
       return KVQ_ERR_UNSUPPORTED;
     if (c.k_block != 128 || c.window < 0 || c.sparse_per_vec < 0 || c.sparse_per_vec > 8)
@@ -144,6 +148,32 @@ extern "C" size_t kvq_workspace_bytes(const kvq_layout* lay, int32_t op, int32_t
 }
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+extern "C" kvq_status kvq_set_channel_order(const kvq_layout* lay, void* cache, const int32_t* order,
+                                            void* stream) {
+  if (!lay || !cache || !order || !aligned16(cache)) return KVQ_ERR_ARG;
+  const kvq_config& c = lay->cfg;
+  if (c.mode != KVQ_MODE_TIERED || !c.reorder) return KVQ_ERR_UNSUPPORTED;
+  for (int r = 0; r < 2 * c.kv_heads; ++r) {
+    bool seen[kD] = {};
+    for (int p = 0; p < kD; ++p) {
+      const int32_t ch = order[(size_t)r * kD + p];
+      if (ch < 0 || ch >= kD || seen[ch]) return KVQ_ERR_ARG;
+      seen[ch] = true;
+    }
+  }
+  uint8_t* base = (uint8_t*)cache + lay->chan_order;
+  for (int h = 0; h < c.kv_heads; ++h) {
+    uint8_t kb[kD], vb[kD];
+    for (int p = 0; p < kD; ++p) {
+      kb[p] = (uint8_t)order[(size_t)h * kD + p];
+      vb[p] = (uint8_t)order[((size_t)c.kv_heads + h) * kD + p];
+    }
+    if (!launch_write_order(base + (size_t)h * kD, base + ((size_t)c.kv_heads + h) * kD, kb, vb, stream))
+      return KVQ_ERR_LAUNCH;
+  }
+  return KVQ_OK;
+}
 
 extern "C" kvq_status kvq_quantize(const kvq_layout* lay, void* cache, const void* k, const void* v,
                                    int64_t stride_b, int64_t stride_t, int64_t stride_h,

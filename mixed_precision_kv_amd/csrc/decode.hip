@@ -281,7 +281,8 @@ constexpr int kMergeBatch = 8;                // chunks per thread per round tri
 template <int THREADS>
 __global__ __launch_bounds__(THREADS) void k_merge(const float* __restrict__ part,
                                                    uint16_t* __restrict__ out, int nch_total,
-                                                   int Hkv, float2* __restrict__ stats) {
+                                                   int Hkv, float2* __restrict__ stats,
+                                                   const uint8_t* __restrict__ vorder) {
   constexpr int S = THREADS / 32;             // slices
   __shared__ float smax[S];
   __shared__ float4 racc[S][32];
@@ -340,20 +341,41 @@ __global__ __launch_bounds__(THREADS) void k_merge(const float* __restrict__ par
       r.x += x.x; r.y += x.y; r.z += x.z; r.w += x.w;
       l += rl[k];
     }
-    uint16_t* po = out + ((size_t)b * Hkv * kGqa + hk * kGqa + hh) * kD + 4 * t;
+    uint16_t* po = out + ((size_t)b * Hkv * kGqa + hk * kGqa + hh) * kD;
     if (stats && t == 0) stats[u * kGqa + hh] = make_float2(Mg, l);   // (max, sum) of the head
-    po[0] = f2h_rne(r.x / l);
-    po[1] = f2h_rne(r.y / l);
-    po[2] = f2h_rne(r.z / l);
-    po[3] = f2h_rne(r.w / l);
+    // position p of the sums is channel vorder[p] of the output (stored order)
+    const uint32_t ch = vorder ? *reinterpret_cast<const uint32_t*>(vorder + (size_t)hk * kD + 4 * t) & 0x7F7F7F7Fu
+                               : 0x03020100u + 0x04040404u * (uint32_t)t;
+    po[ch & 0xFF] = f2h_rne(r.x / l);
+    po[(ch >> 8) & 0xFF] = f2h_rne(r.y / l);
+    po[(ch >> 16) & 0xFF] = f2h_rne(r.z / l);
+    po[ch >> 24] = f2h_rne(r.w / l);
   }
+}
+
+// Query rows gathered into the stored key channel order of their KV head, so
+// that q . k^ over stored positions equals the product in channel order.
+__global__ __launch_bounds__(kD) void k_gather_q(const uint16_t* __restrict__ src,
+                                                 const uint8_t* __restrict__ korder,
+                                                 uint16_t* __restrict__ dst, int Hq) {
+  const int r = blockIdx.x, p = threadIdx.x;
+  const int hk = (r % Hq) / kGqa;
+  dst[(size_t)r * kD + p] = src[(size_t)r * kD + (korder[(size_t)hk * kD + p] & 0x7F)];
+}
+
+bool launch_gather_q(const uint16_t* src, const uint8_t* korder, uint16_t* dst, int rows, int Hq,
+                     void* stream) {
+  k_gather_q<<<rows, kD, 0, (hipStream_t)stream>>>(src, korder, dst, Hq);
+  return hipGetLastError() == hipSuccess;
 }
 
 // 8 slices for few chunks per unit, 32 for many (long contexts over few units)
 static void launch_merge(const float* part, uint16_t* out, int U, int nch, int Hkv, hipStream_t s,
-                         float2* stats = nullptr) {
-  if (nch <= 8 * kMergeBatch) k_merge<256><<<dim3(U, kGqa), 256, 0, s>>>(part, out, nch, Hkv, stats);
-  else k_merge<1024><<<dim3(U, kGqa), 1024, 0, s>>>(part, out, nch, Hkv, stats);
+                         float2* stats = nullptr, const uint8_t* vorder = nullptr) {
+  if (nch <= 8 * kMergeBatch)
+    k_merge<256><<<dim3(U, kGqa), 256, 0, s>>>(part, out, nch, Hkv, stats, vorder);
+  else
+    k_merge<1024><<<dim3(U, kGqa), 1024, 0, s>>>(part, out, nch, Hkv, stats, vorder);
 }
 
 // Attention mass of every cached token of sequence b: the softmax weight it
@@ -389,13 +411,21 @@ __global__ __launch_bounds__(256) void k_token_mass(const int32_t* __restrict__ 
   mass[(size_t)b * max_len + t] = sum;
 }
 
-size_t decode_ws_bytes(const kvq_layout* L, int max_len, bool mass) {
+// partials (+ raw scores and per-head sums with the mass), then, with stored
+// channel orders, the gathered query rows at the next 256-byte boundary
+static size_t decode_ws_base(const kvq_layout* L, int max_len, bool mass) {
   int a, b;
   const int n = decode_chunks(L, max_len, &a, &b);
   const size_t U = (size_t)L->cfg.batch * L->cfg.kv_heads;
   size_t bytes = U * n * kGqa * kPartStride * 4;
   if (mass) bytes += U * kGqa * ((size_t)L->cap[0] + L->cap[1]) * 4 + U * kGqa * 8;
   return bytes;
+}
+
+size_t decode_ws_bytes(const kvq_layout* L, int max_len, bool mass) {
+  const size_t base = decode_ws_base(L, max_len, mass);
+  const size_t qb = qperm_bytes(L, L->cfg.batch * L->cfg.q_heads);
+  return qb ? align256z(base) + qb : base;
 }
 
 bool launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, float scale,
@@ -429,6 +459,13 @@ bool launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, flo
     raw[0] = (float*)(ws + (size_t)U * nch * kGqa * kPartStride * 4);
     raw[1] = raw[0] + (size_t)U * kGqa * L->cap[0];
     float2* stats = (float2*)(raw[1] + (size_t)U * kGqa * L->cap[1]);
+    const uint8_t* korder = c.reorder ? cache + L->chan_order : nullptr;
+    const uint8_t* vorder = c.reorder ? korder + (size_t)c.kv_heads * kD : nullptr;
+    if (korder) {
+      uint16_t* qp = (uint16_t*)(ws + align256z(decode_ws_base(L, max_len, mass != nullptr)));
+      if (!launch_gather_q(a.q, korder, qp, c.batch * c.q_heads, c.q_heads, stream)) return false;
+      a.q = qp;
+    }
     for (int p = 0; p < 2; ++p) {
       PoolArgs pa;
       pa.counters = a.counters;
@@ -450,7 +487,8 @@ bool launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, flo
       pa.cap_p = L->cap[p];
       if (nchp[p] > 0 && !launch_decode_pool(lv[p], pa, c.group, nchp[p], U, stream)) return false;
     }
-    launch_merge((const float*)ws, (uint16_t*)out, U, nch_used, c.kv_heads, s, mass ? stats : nullptr);
+    launch_merge((const float*)ws, (uint16_t*)out, U, nch_used, c.kv_heads, s, mass ? stats : nullptr,
+                 vorder);
     if (mass)
       k_token_mass<<<dim3(ceil_div(max_len, 256), c.batch), 256, 0, s>>>(
           a.counters, (const uint32_t*)(cache + L->tokmap), raw[0], raw[1], stats, mass, c.capacity,

@@ -388,7 +388,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
 // log, scores scaled) [B][M][Hq] when given.
 constexpr int kMqBatch = 8;
 __global__ __launch_bounds__(kD) void k_merge_mq(const float* __restrict__ part, uint16_t* __restrict__ out,
-                                                float* __restrict__ lse, int nch, int nqg, int M, int Hkv) {
+                                                float* __restrict__ lse, int nch, int nqg, int M, int Hkv,
+                                                const uint8_t* __restrict__ vorder) {
   const int row = blockIdx.x, r = row % kMqR, ug = row / kMqR;
   const int qg = ug % nqg, u = ug / nqg;
   const int m = qg * kMqQ + (r >> 2);
@@ -423,7 +424,8 @@ __global__ __launch_bounds__(kD) void k_merge_mq(const float* __restrict__ part,
     mx = bm;
   }
   const size_t o = ((size_t)b * M + m) * Hkv * kGqa + hk * kGqa + h;
-  out[o * kD + d] = (uint16_t)f2h_rne(acc / l);
+  // position d of the sums is channel vorder[d] of the output (stored order)
+  out[o * kD + (vorder ? (int)(vorder[(size_t)hk * kD + d] & 0x7F) : d)] = (uint16_t)f2h_rne(acc / l);
   if (lse && d == 0) lse[o] = (mx + __log2f(l)) * 0.69314718055994530942f;
 }
 
@@ -454,6 +456,8 @@ static bool launch_mq_pool(int L, const PoolMqArgs& a, int G, int nch, int U, hi
   return false;
 }
 
+static size_t decode_mq_part_bytes(const kvq_layout* L, int M, int max_len);
+
 bool launch_decode_mq(const kvq_layout* L, const uint8_t* cache, const void* q, int M, float scale,
                       int max_len, void* out, float* lse, uint8_t* ws, void* stream) {
   hipStream_t s = (hipStream_t)stream;
@@ -471,10 +475,18 @@ bool launch_decode_mq(const kvq_layout* L, const uint8_t* cache, const void* q, 
   }
   const int nch_used = nchp[0] + nchp[1];
   if (nch_used > nch) return false;          // workspace is sized for the finest split
+  const uint8_t* korder = c.reorder ? cache + L->chan_order : nullptr;
+  const uint8_t* vorder = c.reorder ? korder + (size_t)c.kv_heads * kD : nullptr;
+  const uint16_t* qs = (const uint16_t*)q;
+  if (korder) {
+    uint16_t* qp = (uint16_t*)(ws + align256z(decode_mq_part_bytes(L, M, max_len)));
+    if (!launch_gather_q(qs, korder, qp, c.batch * M * c.q_heads, c.q_heads, stream)) return false;
+    qs = qp;
+  }
   for (int p = 0; p < 2; ++p) {
     PoolMqArgs pa;
     pa.counters = (const int32_t*)(cache + L->counters);
-    pa.q = (const uint16_t*)q;
+    pa.q = qs;
     pa.part = (float*)ws;
     pa.kwords = (const uint32_t*)(cache + L->k_words[p]);
     pa.kmeta = (const uint32_t*)(cache + L->k_meta[p]);
@@ -493,15 +505,23 @@ bool launch_decode_mq(const kvq_layout* L, const uint8_t* cache, const void* q, 
     if (nchp[p] > 0 && !launch_mq_pool(lv[p], pa, c.group, nchp[p], U, s)) return false;
   }
   k_merge_mq<<<U * nqg * kMqR, kD, 0, s>>>((const float*)ws, (uint16_t*)out, lse, nch_used, nqg, M,
-                                           c.kv_heads);
+                                           c.kv_heads, vorder);
   return hipGetLastError() == hipSuccess;
 }
 
-size_t decode_mq_ws_bytes(const kvq_layout* L, int M, int max_len) {
+// partials, then, with stored channel orders, the gathered query rows at the
+// next 256-byte boundary
+static size_t decode_mq_part_bytes(const kvq_layout* L, int M, int max_len) {
   int a, b;
   const int n = decode_chunks(L, max_len, &a, &b);
   const size_t U = (size_t)L->cfg.batch * L->cfg.kv_heads, nqg = (M + kMqQ - 1) / kMqQ;
   return U * nqg * (size_t)n * kMqR * kPartF * 4;
+}
+
+size_t decode_mq_ws_bytes(const kvq_layout* L, int M, int max_len) {
+  const size_t base = decode_mq_part_bytes(L, M, max_len);
+  const size_t qb = qperm_bytes(L, L->cfg.batch * M * L->cfg.q_heads);
+  return qb ? align256z(base) + qb : base;
 }
 
 }  // namespace kvq

@@ -8,6 +8,8 @@
 // writes is complete.  Codes are staged in LDS as bytes,
 // then packed twice: along head_dim for keys (row words) and along slots for
 // values (column words).
+#include <string.h>
+
 #include "common.h"
 #include "internal.h"
 #include "digits.h"
@@ -30,6 +32,9 @@ struct QuantArgs {
   uint32_t* kmeta;
   uint32_t* vwords;
   uint32_t* vmeta;
+  const uint8_t* korder = nullptr;   // [Hkv][128] stored key channel order, or null
+  const uint8_t* vorder = nullptr;   // [Hkv][128] stored value channel order, or null
+  float clip = 1.0f;                 // group min/max scale factor (1: none)
 };
 
 // Quantize one group of G fp16 values at src (16-byte aligned); codes to LDS.
@@ -242,8 +247,9 @@ __device__ inline uint32_t chunk_extremes(const uint4* x) {
 
 // codes of the 8 values of one chunk (fp16 bits in x) into two byte words;
 // CLAMP bounds the quotient by the top level (needed only for subnormal
-// scales, where s can be far below range / (L - 1))
-template <int L, bool CLAMP>
+// scales, where s can be far below range / (L - 1)); LOW bounds it below by 0
+// (clipped ranges, where values can lie below the zero point)
+template <int L, bool CLAMP, bool LOW = false>
 __device__ inline void chunk_codes(uint4 x, uint32_t meta, float r, float one, uint32_t& c0, uint32_t& c1) {
   const h2v zs = hb(meta);                    // (s, z)
   const uint32_t w[4] = {x.x, x.y, x.z, x.w};
@@ -251,6 +257,7 @@ __device__ inline void chunk_codes(uint4 x, uint32_t meta, float r, float one, u
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     float q = quotient_of(hb(w[e / 2])[e & 1], zs[1], zs[0], r, one);
+    if (LOW) q = fmaxf(q, 0.0f);
     if (CLAMP) q = fminf(q, (float)(L - 1));
     c[e / 4] = __builtin_amdgcn_cvt_pk_u8_f32(q, e & 3, c[e / 4]);
   }
@@ -258,7 +265,20 @@ __device__ inline void chunk_codes(uint4 x, uint32_t meta, float r, float one, u
   c1 = c[1];
 }
 
-template <int L, int G>
+// Clipped group range: min and max each scaled by clip in fp32, then rounded
+// to fp16 (two roundings, kept apart from any fused form).
+__device__ inline void clip_range(uint32_t& mn, uint32_t& mx, float clip) {
+  float lo = h2f(mn) * clip, hi = h2f(mx) * clip;
+  asm volatile("" : "+v"(lo), "+v"(hi));
+  mn = f2h_rne(lo);
+  mx = f2h_rne(hi);
+}
+
+// SKVQ selects the variant with stored channel orders and clipped group
+// ranges: each wave's rows go through LDS (natural order in, 16-byte chunks)
+// and come back gathered in the stored order, so the rest of the kernel sees
+// stored positions; codes are then bounded at both ends.
+template <int L, int G, bool SKVQ>
 __global__ __launch_bounds__(kQThreads) void k_quant_rows(QuantArgs a) {
   using P = RowPack<L>;
   constexpr int NV = P::NV, KW = P::KW, NG = kD / G, SL = P::SL, ROWS = P::ROWS;
@@ -269,6 +289,8 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows(QuantArgs a) {
   static_assert(NG >= 1 && NG <= 4, "group of 32, 64 or 128 channels");
   __shared__ uint32_t codes[SL][CW];               // byte codes, [slot][channel]
   __shared__ int tok[256];
+  constexpr int SW = kD / 2 + 2;                   // dwords per staged fp16 row (+2: bank spread)
+  __shared__ uint32_t stage[SKVQ ? 64 : 1][SW];    // one pass of rows, natural channel order
   const int tid = threadIdx.x, u = blockIdx.y;
   const int b = u / a.Hkv, h = u % a.Hkv;
   const int s0 = blockIdx.x * SL;
@@ -293,6 +315,41 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows(QuantArgs a) {
         x[p][i] = t >= 0 ? *reinterpret_cast<const uint4*>(base + (int64_t)t * a.st + 32 * i)
                          : make_uint4(0u, 0u, 0u, 0u);
     }
+    if constexpr (SKVQ) {
+      const uint8_t* ord = kv ? a.vorder : a.korder;
+      if (ord) {
+        // bytes of the channels stored at positions 32 i + 8 q .. 32 i + 8 q + 7
+        uint32_t ow[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            ow[2 * i + j] = *reinterpret_cast<const uint32_t*>(ord + (size_t)h * kD + 32 * i + 8 * q + 4 * j);
+        uint32_t* srow = stage[rp];
+        const uint16_t* hrow = reinterpret_cast<const uint16_t*>(srow);
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          __syncthreads();                           // the previous pass has been gathered
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            *reinterpret_cast<uint2*>(srow + 16 * i + 4 * q) = make_uint2(x[p][i].x, x[p][i].y);
+            *reinterpret_cast<uint2*>(srow + 16 * i + 4 * q + 2) = make_uint2(x[p][i].z, x[p][i].w);
+          }
+          __syncthreads();
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+              const uint32_t ob = ow[2 * i + e / 4];
+              const uint32_t c0 = (ob >> (8 * (e % 4))) & 0x7Fu, c1 = (ob >> (8 * (e % 4) + 8)) & 0x7Fu;
+              w[e / 2] = (uint32_t)hrow[c0] | ((uint32_t)hrow[c1] << 16);
+            }
+            x[p][i] = make_uint4(w[0], w[1], w[2], w[3]);
+          }
+        }
+      }
+    }
     uint32_t* mp = kv ? a.vmeta : a.kmeta;
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
@@ -308,7 +365,8 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows(QuantArgs a) {
       uint32_t eo = e[0];
 #pragma unroll
       for (int g = 1; g < NG; ++g) eo = gown == g ? e[g] : eo;
-      const uint32_t mn = eo & 0xFFFFu, mx = (eo >> 16) ^ 0x8000u;
+      uint32_t mn = eo & 0xFFFFu, mx = (eo >> 16) ^ 0x8000u;
+      if constexpr (SKVQ) clip_range(mn, mx, a.clip);
       GroupQ gq = group_setup(mn, mx, L);
       if (gq.s == 0.0f) gq.r = 0.0f;               // all codes 0
       const uint32_t meta = gq.s_bits | (mn << 16);
@@ -328,7 +386,12 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows(QuantArgs a) {
         else { gm[g] = quad_bcast<3>(meta); gr[g] = quad_bcast<3>(__float_as_uint(gq.r)); }
       }
       uint32_t c[4][2];
-      if (__builtin_expect(__ballot(sub && gq.s != 0.0f) != 0ull, 0)) {
+      if constexpr (SKVQ) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          chunk_codes<L, true, true>(x[p][i], gm[i / CPG], __uint_as_float(gr[i / CPG]), one, c[i][0],
+                                     c[i][1]);
+      } else if (__builtin_expect(__ballot(sub && gq.s != 0.0f) != 0ull, 0)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           chunk_codes<L, true>(x[p][i], gm[i / CPG], __uint_as_float(gr[i / CPG]), one, c[i][0], c[i][1]);
@@ -374,14 +437,20 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows(QuantArgs a) {
   }
 }
 
-template <int L>
-static bool launch_rows_L(const QuantArgs& a, int G, dim3 grid, hipStream_t s) {
+template <int L, bool SKVQ>
+static bool launch_rows_LS(const QuantArgs& a, int G, dim3 grid, hipStream_t s) {
   switch (G) {
-    case 32: k_quant_rows<L, 32><<<grid, kQThreads, 0, s>>>(a); return true;
-    case 64: k_quant_rows<L, 64><<<grid, kQThreads, 0, s>>>(a); return true;
-    case 128: k_quant_rows<L, 128><<<grid, kQThreads, 0, s>>>(a); return true;
+    case 32: k_quant_rows<L, 32, SKVQ><<<grid, kQThreads, 0, s>>>(a); return true;
+    case 64: k_quant_rows<L, 64, SKVQ><<<grid, kQThreads, 0, s>>>(a); return true;
+    case 128: k_quant_rows<L, 128, SKVQ><<<grid, kQThreads, 0, s>>>(a); return true;
   }
   return false;
+}
+
+template <int L>
+static bool launch_rows_L(const QuantArgs& a, int G, dim3 grid, hipStream_t s) {
+  const bool skvq = a.korder || a.vorder || a.clip != 1.0f;
+  return skvq ? launch_rows_LS<L, true>(a, G, grid, s) : launch_rows_LS<L, false>(a, G, grid, s);
 }
 
 static bool launch_pool(const QuantArgs& a, int G, int U, hipStream_t s) {
@@ -396,6 +465,7 @@ static bool launch_pool(const QuantArgs& a, int G, int U, hipStream_t s) {
     case 7: return launch_rows_L<7>(a, G, grid, s);
     case 8: return launch_rows_L<8>(a, G, grid, s);
   }
+  if (a.korder || a.vorder || a.clip != 1.0f) return false;   // the row kernel covers L <= 8 only
   size_t lds = (size_t)2 * SL * kD;
   switch (G) {
     case 32: k_quant_pool<32><<<grid, kQThreads, lds, s>>>(a); break;
@@ -427,6 +497,9 @@ bool launch_quantize_tiered(const kvq_layout* L, uint8_t* cache, const void* k, 
     a.kmeta = (uint32_t*)(cache + L->k_meta[p]);
     a.vwords = (uint32_t*)(cache + L->v_words[p]);
     a.vmeta = (uint32_t*)(cache + L->v_meta[p]);
+    a.korder = L->cfg.reorder ? cache + L->chan_order : nullptr;
+    a.vorder = L->cfg.reorder ? cache + L->chan_order + (size_t)L->cfg.kv_heads * kD : nullptr;
+    a.clip = L->cfg.clip > 0.0f ? L->cfg.clip : 1.0f;
     if (!launch_pool(a, L->cfg.group, U, s)) return false;
   }
   return hipGetLastError() == hipSuccess;
@@ -779,7 +852,35 @@ struct AppendArgs {
   const float* score_new;
   int L[2], nv[2], kw[2], tiles[2], vrows[2], cap[2];
   int capacity, Hkv, G;
+  const uint8_t* korder = nullptr;   // [Hkv][128] stored channel orders, or null
+  const uint8_t* vorder = nullptr;
+  float clip = 1.0f;                 // group min/max scale factor (1: none)
+  int skvq = 0;                      // orders or clipping in use
 };
+
+// One group of a new token's row with a stored channel order (ord: the
+// group's G order bytes, or null for natural order) and a clipped range;
+// codes in stored order to LDS, (scale, zero) returned.
+template <int G>
+__device__ inline uint32_t quant_group_skvq(const uint16_t* __restrict__ row, const uint8_t* ord, int g,
+                                            float clip, int L, uint8_t* codes) {
+  uint16_t x[G];
+#pragma unroll
+  for (int i = 0; i < G; ++i) x[i] = row[ord ? (int)(ord[i] & 0x7F) : g * G + i];
+  int kmn = f16_order_key(x[0]), kmx = kmn;
+#pragma unroll
+  for (int i = 1; i < G; ++i) {
+    const int kk = f16_order_key(x[i]);
+    kmn = min(kmn, kk);
+    kmx = max(kmx, kk);
+  }
+  uint32_t mn = f16_from_order_key(kmn), mx = f16_from_order_key(kmx);
+  clip_range(mn, mx, clip);
+  const GroupQ gq = group_setup(mn, mx, L);
+#pragma unroll
+  for (int i = 0; i < G; ++i) codes[i] = (uint8_t)quant_value(h2f(x[i]), gq);
+  return gq.s_bits | (mn << 16);
+}
 
 constexpr int kAppendBatch = 16;              // sorted-score elements per thread per round trip
 
@@ -834,8 +935,15 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
   // quantize every (head, k/v, group)
   for (int task = tid; task < a.Hkv * 2 * NG; task += 256) {
     const int h = task / (2 * NG), kv = (task / NG) % 2, g = task % NG;
-    const uint16_t* src = (kv ? a.v_new : a.k_new) + ((size_t)b * a.Hkv + h) * kD + g * G;
-    const uint32_t meta = quant_group<G>(src, L, &codes[kv][h][g * G]);
+    const uint16_t* row = (kv ? a.v_new : a.k_new) + ((size_t)b * a.Hkv + h) * kD;
+    uint32_t meta;
+    if (a.skvq) {
+      const uint8_t* ord = kv ? a.vorder : a.korder;
+      meta = quant_group_skvq<G>(row, ord ? ord + (size_t)h * kD + g * G : nullptr, g, a.clip, L,
+                                 &codes[kv][h][g * G]);
+    } else {
+      meta = quant_group<G>(row + g * G, L, &codes[kv][h][g * G]);
+    }
     const int u = b * a.Hkv + h;
     uint32_t* mp = kv ? a.vmeta[tier] : a.kmeta[tier];
     mp[(((size_t)u * tiles + slot / kTile) * NG + g) * kTile + (slot % kTile)] = meta;
@@ -909,12 +1017,36 @@ bool launch_append(const kvq_layout* L, uint8_t* cache, const void* k_new, const
   a.capacity = c.capacity;
   a.Hkv = c.kv_heads;
   a.G = c.group;
+  a.korder = c.reorder ? cache + L->chan_order : nullptr;
+  a.vorder = c.reorder ? cache + L->chan_order + (size_t)c.kv_heads * kD : nullptr;
+  a.clip = c.clip > 0.0f ? c.clip : 1.0f;
+  a.skvq = (c.reorder || a.clip != 1.0f) ? 1 : 0;
   switch (c.group) {
     case 32: k_append<32><<<c.batch, 256, 0, s>>>(a); break;
     case 64: k_append<64><<<c.batch, 256, 0, s>>>(a); break;
     case 128: k_append<128><<<c.batch, 256, 0, s>>>(a); break;
     default: return false;
   }
+  return hipGetLastError() == hipSuccess;
+}
+
+// ------------------------------------------------------- channel orders ----
+struct OrderBytes {
+  uint32_t k[kD / 4], v[kD / 4];
+};
+
+__global__ __launch_bounds__(64) void k_write_order(uint32_t* dk, uint32_t* dv, OrderBytes o) {
+  const int t = threadIdx.x;
+  if (t < kD / 4) dk[t] = o.k[t];
+  else if (t < kD / 2) dv[t - kD / 4] = o.v[t - kD / 4];
+}
+
+bool launch_write_order(uint8_t* dk, uint8_t* dv, const uint8_t* kbytes, const uint8_t* vbytes,
+                        void* stream) {
+  OrderBytes o;
+  memcpy(o.k, kbytes, kD);
+  memcpy(o.v, vbytes, kD);
+  k_write_order<<<1, 64, 0, (hipStream_t)stream>>>((uint32_t*)dk, (uint32_t*)dv, o);
   return hipGetLastError() == hipSuccess;
 }
 

@@ -26,7 +26,8 @@ class KvqConfig(ctypes.Structure):
     _fields_ = [(n, _i32) for n in (
         "mode", "batch", "kv_heads", "q_heads", "head_dim", "capacity",
         "levels_hi", "levels_lo", "group", "cap_hi", "cap_lo",
-        "k_levels", "k_block", "v_levels", "v_group", "window", "sparse_per_vec")]
+        "k_levels", "k_block", "v_levels", "v_group", "window", "sparse_per_vec",
+        "reorder")] + [("clip", ctypes.c_float)]
 
 
 class KvqLayout(ctypes.Structure):
@@ -38,6 +39,7 @@ class KvqLayout(ctypes.Structure):
         ("counters", _i64), ("tokmap", _i64), ("sorted", _i64),
         ("k_words", _i64 * 2), ("k_meta", _i64 * 2), ("v_words", _i64 * 2), ("v_meta", _i64 * 2),
         ("sparse", _i64), ("k_win", _i64), ("v_win", _i64),
+        ("chan_order", _i64),
         ("total_bytes", _i64),
     ]
 
@@ -80,6 +82,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_decode_attn_mass.argtypes = [cp(KvqLayout), vp, vp, ctypes.c_float, _i32, vp, vp, vp,
                                            ctypes.c_size_t, vp]
         L.kvq_decode_attn_mass.restype = ctypes.c_int
+        L.kvq_set_channel_order.argtypes = [cp(KvqLayout), vp, vp, vp]
+        L.kvq_set_channel_order.restype = ctypes.c_int
         L.kvq_stream_read.argtypes = [vp, ctypes.c_size_t, vp, _i32, vp]
         L.kvq_stream_read.restype = ctypes.c_int
         _lib = L
@@ -118,6 +122,8 @@ def config_for(w) -> KvqConfig:
         c.levels_hi, c.levels_lo, c.group = w.levels_hi, w.levels_lo, w.group
         c.cap_hi = min(w.capacity, w.n_hi + w.append_steps)
         c.cap_lo = min(w.capacity, w.tokens - w.n_hi + w.append_steps)
+        c.reorder = 1 if w.reorder else 0
+        c.clip = w.clip
     else:
         c.k_levels, c.k_block, c.v_levels, c.v_group = w.k_levels, w.k_block, w.v_levels, w.v_group
         c.window, c.sparse_per_vec = w.window, w.sparse_per_vec
@@ -132,6 +138,15 @@ def layout_init(cfg: KvqConfig) -> KvqLayout:
 
 def workspace_bytes(lay: KvqLayout, op: int, max_len: int) -> int:
     return int(lib().kvq_workspace_bytes(ctypes.byref(lay), op, max_len))
+
+
+def set_channel_order(lay, cache, order, stream=None):
+    """order: host int32 array [2][Hkv][D] (keys, values); entry p of a row is
+    the channel stored at position p."""
+    import numpy as np
+    o = np.ascontiguousarray(order, dtype=np.int32)
+    st = lib().kvq_set_channel_order(ctypes.byref(lay), _ptr(cache), o.ctypes.data, _stream(stream))
+    _check(st, "kvq_set_channel_order")
 
 
 def quantize(lay, cache, k, v, scores, T, n_hi, ranks_out=None, ws=None, ws_bytes=None,

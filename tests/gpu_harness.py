@@ -46,6 +46,8 @@ class GpuRun:
         wsd = kvq.workspace_bytes(self.lay, kvq.OP_DECODE, w.capacity)
         self.wsd = torch.empty(wsd, dtype=torch.uint8, device=dev())
         self.scale = np.float32(1.0 / math.sqrt(w.head_dim))
+        if getattr(w, "reorder", False):
+            kvq.set_channel_order(self.lay, self.cache, synth.channel_orders(w))
 
     def quantize(self):
         import torch
@@ -97,6 +99,19 @@ class GpuRun:
 
     def buf(self):
         return self.cache.cpu().numpy().tobytes()
+
+
+def oracle_unit(w, inp, inv, b, h):
+    """Oracle pools of unit (b, h), with the workload's stored channel orders
+    and clip factor when it has them."""
+    kw = {}
+    if w.reorder:
+        o = synth.channel_orders(w)
+        kw.update(order_k=o[0, h], order_v=o[1, h])
+    if w.clip:
+        kw.update(clip=w.clip)
+    return O.quantize_tiered_unit(inp.k[b, :, h], inp.v[b, :, h], inv[b], w.levels_hi, w.levels_lo,
+                                  w.group, **kw)
 
 
 def oracle_tiers(w, inp):

@@ -26,7 +26,8 @@ def test_exports_every_declared_symbol():
     names = declared_symbols()
     assert {"kvq_layout_init", "kvq_workspace_bytes", "kvq_status_str", "kvq_quantize",
             "kvq_append", "kvq_decode_attn", "kvq_multi_workspace_bytes",
-            "kvq_decode_attn_multi", "kvq_stream_read", "kvq_decode_attn_mass"} <= set(names)
+            "kvq_decode_attn_multi", "kvq_stream_read", "kvq_decode_attn_mass",
+            "kvq_set_channel_order"} <= set(names)
     L = kvq.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -52,7 +53,7 @@ def test_structs_match_header(tmp_path):
             assert int(got[f"{struct}.{name}"]) == getattr(cls, name).offset, name
 
 
-@pytest.mark.parametrize("w", synth.CONFIGS, ids=lambda w: w.name)
+@pytest.mark.parametrize("w", synth.CONFIGS + [synth.W_SKVQ], ids=lambda w: w.name)
 def test_layout_of_every_workload(w):
     lay = kvq.layout_init(kvq.config_for(w))
     assert lay.total_bytes > 0
@@ -79,6 +80,7 @@ def _cfg(**kw):
     (dict(head_dim=64), 2), (dict(q_heads=8), 2), (dict(levels_hi=2), 2), (dict(levels_lo=17), 2),
     (dict(group=48), 2), (dict(capacity=0), 1), (dict(batch=0), 1), (dict(mode=7), 1),
     (dict(cap_hi=100, cap_lo=100), 1), (dict(cap_hi=5000), 1),
+    (dict(reorder=2), 1), (dict(clip=-0.5), 1), (dict(clip=1.5), 1), (dict(clip=float("nan")), 1),
 ])
 def test_layout_rejects(kw, status):
     with pytest.raises(kvq.KvqError) as e:
@@ -88,7 +90,8 @@ def test_layout_rejects(kw, status):
 
 def test_kchan_rejects_unsupported():
     w = synth.W_KCHAN
-    for kw in (dict(k_block=64), dict(v_levels=5), dict(window=600), dict(sparse_per_vec=9)):
+    for kw in (dict(k_block=64), dict(v_levels=5), dict(window=600), dict(sparse_per_vec=9),
+               dict(reorder=1), dict(clip=0.9)):
         c = kvq.config_for(w)
         for k, v in kw.items():
             setattr(c, k, v)
@@ -232,3 +235,44 @@ def test_status_strings():
     for s in range(6):
         assert L.kvq_status_str(s)
     assert L.kvq_status_str(99) == b"unknown status"
+
+
+def test_channel_order_layout_and_workspace():
+    """reorder = 1 adds the [2][Hkv][D] byte orders to the cache and the
+    gathered query rows to the decode workspaces; clipping alone adds
+    nothing."""
+    plain = kvq.layout_init(_cfg())
+    lay = kvq.layout_init(_cfg(reorder=1, clip=0.9))
+    assert plain.chan_order == 0
+    assert lay.chan_order % 256 == 0 and lay.chan_order + 2 * 128 <= lay.total_bytes
+    assert lay.total_bytes == plain.total_bytes + 256
+    clipped = kvq.layout_init(_cfg(clip=0.5))
+    assert clipped.total_bytes == plain.total_bytes and clipped.chan_order == 0
+    for op, extra in ((kvq.OP_DECODE, 4 * 128 * 2), (kvq.OP_DECODE_MASS, 4 * 128 * 2)):
+        a, b = kvq.workspace_bytes(plain, op, 4096), kvq.workspace_bytes(lay, op, 4096)
+        assert b == -(-a // 256) * 256 + extra
+    a, b = kvq.multi_workspace_bytes(plain, 6, 4096), kvq.multi_workspace_bytes(lay, 6, 4096)
+    assert b == -(-a // 256) * 256 + 6 * 4 * 128 * 2
+    assert kvq.workspace_bytes(lay, kvq.OP_QUANTIZE, 4096) == kvq.workspace_bytes(plain, kvq.OP_QUANTIZE, 4096)
+
+
+def test_set_channel_order_validation():
+    import numpy as np
+    lay = kvq.layout_init(_cfg(reorder=1))
+    ident = np.tile(np.arange(128, dtype=np.int32), (2, 1, 1))
+    bad_dup = ident.copy()
+    bad_dup[1, 0, 5] = 6
+    bad_range = ident.copy()
+    bad_range[0, 0, 0] = 128
+    bad_neg = ident.copy()
+    bad_neg[0, 0, 7] = -1
+    for o in (bad_dup, bad_range, bad_neg):
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.set_channel_order(lay, FAKE, o, stream=0)
+        assert e.value.status == 1
+    with pytest.raises(kvq.KvqError) as e:                 # cache laid out without orders
+        kvq.set_channel_order(kvq.layout_init(_cfg()), FAKE, ident, stream=0)
+    assert e.value.status == 2
+    with pytest.raises(kvq.KvqError) as e:                 # misaligned cache
+        kvq.set_channel_order(lay, FAKE + 8, ident, stream=0)
+    assert e.value.status == 1

@@ -9,7 +9,7 @@ import pytest
 from mixed_precision_kv_amd import synth
 from oracle import kvq_oracle as O
 import layout_view as LV
-from gpu_harness import (GpuRun, TOL, compare_tiered_unit, log, oracle_tiers,
+from gpu_harness import (GpuRun, TOL, compare_tiered_unit, log, oracle_tiers, oracle_unit,
                          oracle_unit_attention)
 
 pytestmark = pytest.mark.gpu
@@ -28,7 +28,7 @@ def _bounded(out, v):
     assert np.abs(o).max() <= vmax * 1.01 + 1e-2
 
 
-@pytest.mark.parametrize("w", [synth.W_SINGLE, synth.W_LLAMA, synth.W_LONG], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [synth.W_SINGLE, synth.W_LLAMA, synth.W_LONG, synth.W_SKVQ], ids=lambda w: w.name)
 def test_tiered_fullsize(w):
     log(f"case {w.name} full size")
     inp = synth.make_inputs(w, steps=0)
@@ -56,8 +56,7 @@ def test_tiered_fullsize(w):
     errs, merrs, lerrs = [], [], []
     for u in _sample_units(w):
         b, h = divmod(u, w.kv_heads)
-        pools = O.quantize_tiered_unit(inp.k[b, :, h], inp.v[b, :, h], inv[b], w.levels_hi,
-                                       w.levels_lo, w.group)
+        pools = oracle_unit(w, inp, inv, b, h)
         compare_tiered_unit(buf, run.lay, pools, u, f"{w.name} u{u}")
         kh = np.concatenate([pools[0].k_hat(), pools[1].k_hat()])
         vh = np.concatenate([pools[0].v_hat(), pools[1].v_hat()])
@@ -90,8 +89,7 @@ def test_append_fullsize():
     pools = {}
     for u in units:
         b, h = divmod(u, w.kv_heads)
-        pools[u] = O.quantize_tiered_unit(inp.k[b, :, h], inp.v[b, :, h], inv[b], w.levels_hi,
-                                          w.levels_lo, w.group)
+        pools[u] = oracle_unit(w, inp, inv, b, h)
     tok = [list(tokmap[b]) for b in range(w.batch)]
     n_pool = counts.astype(np.int64).copy()
     check_steps = {0, 1, 127, w.append_steps - 1}

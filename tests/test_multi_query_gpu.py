@@ -13,7 +13,7 @@ import pytest
 
 from mixed_precision_kv_amd import kvq, synth
 from oracle import kvq_oracle as O
-from gpu_harness import GpuRun, TOL, log, oracle_tiers, to_dev
+from gpu_harness import GpuRun, TOL, log, oracle_tiers, oracle_unit, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -47,8 +47,7 @@ def _check_multi(w, inp, run, qm, units=None):
             u = b * w.kv_heads + h
             if units is not None and u not in units:
                 continue
-            pools = O.quantize_tiered_unit(inp.k[b, :, h], inp.v[b, :, h], inv[b], w.levels_hi,
-                                           w.levels_lo, w.group)
+            pools = oracle_unit(w, inp, inv, b, h)
             kh = np.concatenate([pools[0].k_hat(), pools[1].k_hat()])
             vh = np.concatenate([pools[0].v_hat(), pools[1].v_hat()])
             rows = qm[b, :, h * g:(h + 1) * g].reshape(M * g, -1).astype(np.float64)
@@ -64,6 +63,18 @@ def _check_multi(w, inp, run, qm, units=None):
 @pytest.mark.parametrize("M", [1, 3, 4, 9])
 def test_multi_query_c2_shape(M):
     w = synth.W_LLAMA.shrink(name="c2_small_mq", batch=2, kv_heads=2, q_heads=8, tokens=1999)
+    log(f"case {w.name} M{M}")
+    inp = synth.make_inputs(w)
+    run = GpuRun(w, inp, want_ranks=False)
+    run.quantize()
+    _check_multi(w, inp, run, synth.make_queries(w, M))
+
+
+@pytest.mark.parametrize("M", [1, 6])
+def test_multi_query_skvq(M):
+    """Queries gathered through the stored key order, outputs written back
+    through the value order."""
+    w = synth.W_SKVQ.shrink(name="skvq_small_mq", batch=2, kv_heads=2, q_heads=8, tokens=1999)
     log(f"case {w.name} M{M}")
     inp = synth.make_inputs(w)
     run = GpuRun(w, inp, want_ranks=False)

@@ -7,7 +7,7 @@ import pytest
 from mixed_precision_kv_amd import synth
 from oracle import kvq_oracle as O
 import layout_view as LV
-from gpu_harness import GpuRun, TOL, compare_tiered_unit, log, oracle_tiers, oracle_unit_attention
+from gpu_harness import GpuRun, TOL, compare_tiered_unit, log, oracle_tiers, oracle_unit, oracle_unit_attention
 
 pytestmark = pytest.mark.gpu
 
@@ -28,8 +28,7 @@ def _check_tiered(w, inp, run, decode=True):
     for b in range(w.batch):
         for h in range(w.kv_heads):
             u = b * w.kv_heads + h
-            pools = O.quantize_tiered_unit(inp.k[b, :, h], inp.v[b, :, h], inv[b], w.levels_hi,
-                                           w.levels_lo, w.group)
+            pools = oracle_unit(w, inp, inv, b, h)
             compare_tiered_unit(buf, lay, pools, u, f"{w.name} b{b} h{h}")
             if decode:
                 kh = np.concatenate([pools[0].k_hat(), pools[1].k_hat()])
@@ -47,6 +46,7 @@ SMALL = [
     synth.W_LLAMA.shrink(name="c2_small", batch=2, kv_heads=2, q_heads=8, tokens=1999),
     synth.W_LONG.shrink(name="c3_small", batch=1, kv_heads=2, q_heads=8, tokens=3001),
     synth.W_APPEND.shrink(name="c4_prefix_small", batch=3, kv_heads=2, q_heads=8, tokens=777, append_steps=0),
+    synth.W_SKVQ.shrink(name="skvq_small", batch=2, kv_heads=2, q_heads=8, tokens=1999),
 ]
 
 
@@ -67,6 +67,49 @@ def test_tiered_level_pairs(lh, ll, g):
                     levels_hi=lh, levels_lo=ll, group=g)
     log(f"case {w.name}")
     inp = synth.make_inputs(w)
+    run = GpuRun(w, inp)
+    run.quantize()
+    _check_tiered(w, inp, run)
+
+
+@pytest.mark.parametrize("lh,ll,g,clip,reorder,T", [
+    (6, 5, 32, 0.9, True, 1201),
+    (8, 6, 64, 0.5, True, 3001),
+    (4, 3, 128, 0.75, True, 777),
+    (7, 6, 32, 0.8, False, 1201),      # clipping alone (natural channel order)
+    (5, 4, 64, 0.0, True, 1201),       # stored orders alone
+    (8, 7, 32, 1.0, True, 17),         # clip factor 1 with orders, one ragged tile
+    (3, 3, 32, 0.3, True, 640),
+])
+def test_skvq_variants(lh, ll, g, clip, reorder, T):
+    """Stored channel orders and clipped group ranges (SKVQ, Abstract) over
+    grid sizes 3..8 and groups of 32, 64 and 128: codes, words and fp16
+    (scale, zero) bit-exact in stored order, decode in channel order."""
+    w = synth.W_SKVQ.shrink(name=f"skvq_{lh}_{ll}_g{g}_c{clip}_r{int(reorder)}_T{T}", batch=2, kv_heads=2,
+                            q_heads=8, tokens=T, levels_hi=lh, levels_lo=ll, group=g, clip=clip,
+                            reorder=reorder)
+    log(f"case {w.name}")
+    inp = synth.make_inputs(w)
+    run = GpuRun(w, inp)
+    run.quantize()
+    _check_tiered(w, inp, run)
+
+
+def test_skvq_degenerate_groups():
+    """Clipping and stored orders on constant groups (scale 0), signed
+    zeros, ranges that clip to one fp16 value, and tiny ranges whose
+    clipped fp16 scale is subnormal."""
+    w = synth.W_SKVQ.shrink(name="skvq_degenerate", batch=2, kv_heads=2, q_heads=8, tokens=500, clip=0.5)
+    log(f"case {w.name}")
+    inp = synth.make_inputs(w)
+    inp.k[0, 10:20, 0, :] = np.float16(0.75)                 # constant rows
+    inp.v[1, 5:9, 1, :] = np.float16(-2.0)
+    inp.k[1, 30, 1, :] = np.float16(-0.0)
+    inp.v[0, 40, 0, ::2] = np.float16(-0.0)
+    inp.v[0, 40, 0, 1::2] = np.float16(0.0)
+    tiny = np.float16(2.0 ** -24)
+    inp.k[0, 50:60, 1, :] = (np.arange(128) % 8).astype(np.float16) * tiny
+    inp.v[1, 61:70, 0, :] = (np.arange(128) % 3).astype(np.float16) * tiny   # clipped range: one value
     run = GpuRun(w, inp)
     run.quantize()
     _check_tiered(w, inp, run)
@@ -208,18 +251,21 @@ def test_kchan_outlier_ties_and_degenerate_blocks():
     _check_kchan(w, inp, run)
 
 
-def test_append_then_decode_small():
+@pytest.mark.parametrize("w", [
+    synth.W_APPEND.shrink(name="c4_small", batch=3, kv_heads=2, q_heads=8, tokens=300, append_steps=40),
+    synth.W_SKVQ.shrink(name="skvq_append_small", batch=3, kv_heads=2, q_heads=8, tokens=300, append_steps=40),
+], ids=lambda w: w.name)
+def test_append_then_decode_small(w):
     """Generation-time quantization: every step's tier decision, slot, words
-    and the attention after it, against the running-median oracle."""
-    w = synth.W_APPEND.shrink(name="c4_small", batch=3, kv_heads=2, q_heads=8, tokens=300, append_steps=40)
+    and the attention after it, against the running-median oracle (also with
+    stored channel orders and clipped ranges)."""
     log(f"case {w.name}")
     inp = synth.make_inputs(w)
     run = GpuRun(w, inp)
     run.quantize()
     rank, tokmap, counts, inv = oracle_tiers(w, inp)
     med = [O.RunningMedian(inp.scores[b]) for b in range(w.batch)]
-    pools = {(b, h): O.quantize_tiered_unit(inp.k[b, :, h], inp.v[b, :, h], inv[b], w.levels_hi,
-                                            w.levels_lo, w.group)
+    pools = {(b, h): oracle_unit(w, inp, inv, b, h)
              for b in range(w.batch) for h in range(w.kv_heads)}
     tok = [list(tokmap[b]) for b in range(w.batch)]
     for i, st in enumerate(inp.steps):

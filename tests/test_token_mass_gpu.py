@@ -12,7 +12,7 @@ import pytest
 
 from mixed_precision_kv_amd import kvq, synth
 from oracle import kvq_oracle as O
-from gpu_harness import GpuRun, TOL, log, oracle_tiers, oracle_unit_attention, to_dev
+from gpu_harness import GpuRun, TOL, log, oracle_tiers, oracle_unit, oracle_unit_attention, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -65,8 +65,7 @@ def _setup(w):
     run = GpuRun(w, inp, want_ranks=False)
     run.quantize()
     _, _, _, inv = oracle_tiers(w, inp)
-    pools = {(b, h): O.quantize_tiered_unit(inp.k[b, :, h], inp.v[b, :, h], inv[b], w.levels_hi,
-                                            w.levels_lo, w.group)
+    pools = {(b, h): oracle_unit(w, inp, inv, b, h)
              for b in range(w.batch) for h in range(w.kv_heads)}
     inv = [[list(inv[b][0]), list(inv[b][1])] for b in range(w.batch)]
     return inp, run, pools, inv
@@ -80,6 +79,15 @@ def test_token_mass_after_quantize(lh, ll, g, T):
     inp, run, pools, inv = _setup(w)
     mass = _check(w, inp, run, inp.q, w.tokens, pools, inv, w.capacity)
     log(f"{w.name}: mass sums {mass.sum(1)}")
+
+
+def test_token_mass_skvq():
+    """The mass does not depend on the channel order; checked with stored
+    orders and clipped ranges."""
+    w = synth.W_SKVQ.shrink(name="mass_skvq", batch=2, kv_heads=2, q_heads=8, tokens=1999)
+    log(f"case {w.name}")
+    inp, run, pools, inv = _setup(w)
+    _check(w, inp, run, inp.q, w.tokens, pools, inv, w.capacity)
 
 
 def test_token_mass_after_appends():
