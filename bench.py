@@ -103,8 +103,8 @@ def _oracle_unit(args):
     import numpy as np
     from oracle import kvq_oracle as O
     k_unit, v_unit, inv_b, q_group, w_fields, scale = args
-    L_hi, L_lo, G = w_fields
-    pools = O.quantize_tiered_unit(k_unit, v_unit, inv_b, L_hi, L_lo, G)
+    L_hi, L_lo, G, skvq = w_fields
+    pools = O.quantize_tiered_unit(k_unit, v_unit, inv_b, L_hi, L_lo, G, **skvq)
     pools[0].k_words(), pools[0].v_words(), pools[1].k_words(), pools[1].v_words()
     kh = np.concatenate([pools[0].k_hat(), pools[1].k_hat()])
     vh = np.concatenate([pools[0].v_hat(), pools[1].v_hat()])
@@ -116,6 +116,7 @@ def cpu_baseline(w, inp, scale, max_units, workers):
     pack and fp64 attention of a sample of (sequence, KV head) units) on the
     host, units spread over `workers` processes."""
     import numpy as np
+    from mixed_precision_kv_amd import synth
     from oracle import kvq_oracle as O
     os.environ.setdefault("OMP_NUM_THREADS", "1")
     t0 = time.perf_counter()
@@ -124,8 +125,14 @@ def cpu_baseline(w, inp, scale, max_units, workers):
     t_rank = time.perf_counter() - t0
     g = w.q_heads // w.kv_heads
     units = [(b, h) for b in range(w.batch) for h in range(w.kv_heads)][:max_units]
+    orders = synth.channel_orders(w) if w.reorder else None
+
+    def skvq(h):
+        kw = dict(order_k=orders[0, h], order_v=orders[1, h]) if w.reorder else {}
+        return dict(kw, clip=w.clip) if w.clip else kw
+
     jobs = [(np.ascontiguousarray(inp.k[b, :, h]), np.ascontiguousarray(inp.v[b, :, h]), inv[b],
-             inp.q[b, h * g:(h + 1) * g].astype(np.float64), (w.levels_hi, w.levels_lo, w.group),
+             inp.q[b, h * g:(h + 1) * g].astype(np.float64), (w.levels_hi, w.levels_lo, w.group, skvq(h)),
              scale) for b, h in units]
     t0 = time.perf_counter()
     with mp.get_context("fork").Pool(workers) as pool:
@@ -185,6 +192,9 @@ def sweep_one(w, args, torch, np, kvq, synth, dev):
     wsd = torch.empty(max(1, kvq.workspace_bytes(lay, kvq.OP_DECODE, max_len)), dtype=torch.uint8, device=dev)
     R = 1 if w.append_steps else max(1, math.ceil(1.0e9 / lay.total_bytes))
     caches = [torch.zeros(lay.total_bytes, dtype=torch.uint8, device=dev) for _ in range(R)]
+    if w.reorder:
+        for c in caches:
+            kvq.set_channel_order(lay, c, synth.channel_orders(w), stream=stream)
     scale = 1.0 / math.sqrt(w.head_dim)
     tiered = w.mode == synth.TIERED
 
@@ -327,7 +337,7 @@ def main():
         rg = stream_read_gbs(torch, kvq, dev, torch.cuda.current_stream())
         print(json.dumps({"probe": "stream_read", "bytes": 1 << 30, "gbs": round(rg, 1),
                           "frac_hbm": round(rg / HBM_PEAK_GBS, 4)}), flush=True)
-        for cw in synth.CONFIGS:
+        for cw in synth.CONFIGS + [synth.W_SKVQ]:
             if args.sweep_only and cw.name not in args.sweep_only.split(","):
                 continue
             print(json.dumps(sweep_one(cw, args, torch, np, kvq, synth, dev)), flush=True)
@@ -360,6 +370,9 @@ def main():
     wsd = torch.empty(kvq.workspace_bytes(lay, kvq.OP_DECODE, w.tokens), dtype=torch.uint8, device=dev)
     R = args.replicas or max(1, math.ceil(1.0e9 / lay.total_bytes))
     caches = [torch.zeros(lay.total_bytes, dtype=torch.uint8, device=dev) for _ in range(R)]
+    if w.reorder:
+        for c in caches:
+            kvq.set_channel_order(lay, c, synth.channel_orders(w), stream=stream)
     scale = 1.0 / math.sqrt(w.head_dim)
 
     def quantize(i):

@@ -265,6 +265,14 @@ __device__ inline void chunk_codes(uint4 x, uint32_t meta, float r, float one, u
   c1 = c[1];
 }
 
+// Orders the LDS accesses of one wave (stores before the loads that follow);
+// the wave's own LDS operations complete in issue order.
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Clipped group range: min and max each scaled by clip in fp32, then rounded
 // to fp16 (two roundings, kept apart from any fused form).
 __device__ inline void clip_range(uint32_t& mn, uint32_t& mx, float clip) {
@@ -275,7 +283,7 @@ __device__ inline void clip_range(uint32_t& mn, uint32_t& mx, float clip) {
 }
 
 // SKVQ selects the variant with stored channel orders and clipped group
-// ranges: each wave's rows go through LDS (natural order in, 16-byte chunks)
+// ranges: each wave's rows go through LDS (natural order in, 8-byte stores)
 // and come back gathered in the stored order, so the rest of the kernel sees
 // stored positions; codes are then bounded at both ends.
 template <int L, int G, bool SKVQ>
@@ -315,38 +323,42 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows(QuantArgs a) {
         x[p][i] = t >= 0 ? *reinterpret_cast<const uint4*>(base + (int64_t)t * a.st + 32 * i)
                          : make_uint4(0u, 0u, 0u, 0u);
     }
-    if constexpr (SKVQ) {
-      const uint8_t* ord = kv ? a.vorder : a.korder;
-      if (ord) {
-        // bytes of the channels stored at positions 32 i + 8 q .. 32 i + 8 q + 7
-        uint32_t ow[8];
+    // stored channel orders: bytes of the channels at positions
+    // 32 i + 8 q .. 32 i + 8 q + 7 of this lane
+    const uint8_t* ord = SKVQ ? (kv ? a.vorder : a.korder) : nullptr;
+    uint32_t ow[8];
+    if (SKVQ && ord) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
-            ow[2 * i + j] = *reinterpret_cast<const uint32_t*>(ord + (size_t)h * kD + 32 * i + 8 * q + 4 * j);
-        uint32_t* srow = stage[rp];
-        const uint16_t* hrow = reinterpret_cast<const uint16_t*>(srow);
+        for (int j = 0; j < 2; ++j)
+          ow[2 * i + j] = *reinterpret_cast<const uint32_t*>(ord + (size_t)h * kD + 32 * i + 8 * q + 4 * j);
+    }
+    if (SKVQ && ord) {
+      // every pass's rows through LDS, gathered back in the stored order; a
+      // wave stages and gathers only its own 16 rows, so a wave-level
+      // barrier orders its accesses (no workgroup barrier)
+      uint32_t* srow = stage[rp];
+      const uint16_t* hrow = reinterpret_cast<const uint16_t*>(srow);
 #pragma unroll
-        for (int p = 0; p < NP; ++p) {
-          __syncthreads();                           // the previous pass has been gathered
+      for (int p = 0; p < NP; ++p) {
+        wave_lds_sync();                             // the previous pass has been gathered
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            *reinterpret_cast<uint2*>(srow + 16 * i + 4 * q) = make_uint2(x[p][i].x, x[p][i].y);
-            *reinterpret_cast<uint2*>(srow + 16 * i + 4 * q + 2) = make_uint2(x[p][i].z, x[p][i].w);
+        for (int i = 0; i < 4; ++i) {
+          *reinterpret_cast<uint2*>(srow + 16 * i + 4 * q) = make_uint2(x[p][i].x, x[p][i].y);
+          *reinterpret_cast<uint2*>(srow + 16 * i + 4 * q + 2) = make_uint2(x[p][i].z, x[p][i].w);
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t w[4];
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const uint32_t ob = ow[2 * i + e / 4];
+            const uint32_t c0 = (ob >> (8 * (e % 4))) & 0x7Fu, c1 = (ob >> (8 * (e % 4) + 8)) & 0x7Fu;
+            w[e / 2] = (uint32_t)hrow[c0] | ((uint32_t)hrow[c1] << 16);
           }
-          __syncthreads();
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            uint32_t w[4];
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-              const uint32_t ob = ow[2 * i + e / 4];
-              const uint32_t c0 = (ob >> (8 * (e % 4))) & 0x7Fu, c1 = (ob >> (8 * (e % 4) + 8)) & 0x7Fu;
-              w[e / 2] = (uint32_t)hrow[c0] | ((uint32_t)hrow[c1] << 16);
-            }
-            x[p][i] = make_uint4(w[0], w[1], w[2], w[3]);
-          }
+          x[p][i] = make_uint4(w[0], w[1], w[2], w[3]);
         }
       }
     }
