@@ -119,9 +119,8 @@ __global__ __launch_bounds__(kQThreads) void k_quant_pool(QuantArgs a) {
   }
 }
 
-// ---- row kernel: sixteen lanes per slot row (fast path, L <= 8) ----
+// ---- row kernel: four lanes per slot row (fast path, L <= 8) ----
 //
-// Lane l of a 16-lane row group holds channels 8l..8l+7 of one slot row, so
 // Four lanes (a quad) per slot row: load i of lane q reads channels
 // 32 i + 8 q .. 32 i + 8 q + 7, so each load instruction covers 64
 // contiguous bytes of sixteen rows and a group of G channels is chunks
