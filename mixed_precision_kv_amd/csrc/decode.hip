@@ -353,22 +353,6 @@ __global__ __launch_bounds__(THREADS) void k_merge(const float* __restrict__ par
   }
 }
 
-// Query rows gathered into the stored key channel order of their KV head, so
-// that q . k^ over stored positions equals the product in channel order.
-__global__ __launch_bounds__(kD) void k_gather_q(const uint16_t* __restrict__ src,
-                                                 const uint8_t* __restrict__ korder,
-                                                 uint16_t* __restrict__ dst, int Hq) {
-  const int r = blockIdx.x, p = threadIdx.x;
-  const int hk = (r % Hq) / kGqa;
-  dst[(size_t)r * kD + p] = src[(size_t)r * kD + (korder[(size_t)hk * kD + p] & 0x7F)];
-}
-
-bool launch_gather_q(const uint16_t* src, const uint8_t* korder, uint16_t* dst, int rows, int Hq,
-                     void* stream) {
-  k_gather_q<<<rows, kD, 0, (hipStream_t)stream>>>(src, korder, dst, Hq);
-  return hipGetLastError() == hipSuccess;
-}
-
 // 8 slices for few chunks per unit, 32 for many (long contexts over few units)
 static void launch_merge(const float* part, uint16_t* out, int U, int nch, int Hkv, hipStream_t s,
                          float2* stats = nullptr, const uint8_t* vorder = nullptr) {
@@ -411,21 +395,13 @@ __global__ __launch_bounds__(256) void k_token_mass(const int32_t* __restrict__ 
   mass[(size_t)b * max_len + t] = sum;
 }
 
-// partials (+ raw scores and per-head sums with the mass), then, with stored
-// channel orders, the gathered query rows at the next 256-byte boundary
-static size_t decode_ws_base(const kvq_layout* L, int max_len, bool mass) {
+size_t decode_ws_bytes(const kvq_layout* L, int max_len, bool mass) {
   int a, b;
   const int n = decode_chunks(L, max_len, &a, &b);
   const size_t U = (size_t)L->cfg.batch * L->cfg.kv_heads;
   size_t bytes = U * n * kGqa * kPartStride * 4;
   if (mass) bytes += U * kGqa * ((size_t)L->cap[0] + L->cap[1]) * 4 + U * kGqa * 8;
   return bytes;
-}
-
-size_t decode_ws_bytes(const kvq_layout* L, int max_len, bool mass) {
-  const size_t base = decode_ws_base(L, max_len, mass);
-  const size_t qb = qperm_bytes(L, L->cfg.batch * L->cfg.q_heads);
-  return qb ? align256z(base) + qb : base;
 }
 
 bool launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, float scale,
@@ -461,11 +437,6 @@ bool launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, flo
     float2* stats = (float2*)(raw[1] + (size_t)U * kGqa * L->cap[1]);
     const uint8_t* korder = c.reorder ? cache + L->chan_order : nullptr;
     const uint8_t* vorder = c.reorder ? korder + (size_t)c.kv_heads * kD : nullptr;
-    if (korder) {
-      uint16_t* qp = (uint16_t*)(ws + align256z(decode_ws_base(L, max_len, mass != nullptr)));
-      if (!launch_gather_q(a.q, korder, qp, c.batch * c.q_heads, c.q_heads, stream)) return false;
-      a.q = qp;
-    }
     for (int p = 0; p < 2; ++p) {
       PoolArgs pa;
       pa.counters = a.counters;
@@ -485,6 +456,7 @@ bool launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, flo
       pa.c = a.scale_log2;
       pa.raw = mass ? raw[p] : nullptr;
       pa.cap_p = L->cap[p];
+      pa.korder = korder;
       if (nchp[p] > 0 && !launch_decode_pool(lv[p], pa, c.group, nchp[p], U, stream)) return false;
     }
     launch_merge((const float*)ws, (uint16_t*)out, U, nch_used, c.kv_heads, s, mass ? stats : nullptr,

@@ -76,8 +76,11 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int nmt = (s_end - s_begin + MT - 1) / MT;
 
   // ---- shared set-up
-  for (int i = threadIdx.x; i < kGqa * kD; i += 128)
-    qf[i / kD][i % kD] = h2f(a.q[((size_t)b * a.Hkv * kGqa + hk * kGqa) * kD + i]);
+  // q in stored channel order: position d holds channel korder[d] (7-bit)
+  for (int i = threadIdx.x; i < kGqa * kD; i += 128) {
+    const int d = i % kD, src = a.korder ? (int)(a.korder[(size_t)hk * kD + d] & 0x7F) : d;
+    qf[i / kD][d] = h2f(a.q[((size_t)b * a.Hkv * kGqa + hk * kGqa + i / kD) * kD + src]);
+  }
   for (int sl = threadIdx.x; sl < MT; sl += 128) {
     const int jj = sl / RUN, rem = sl % RUN;
     ppos_lds[sl] = jj * VK + DV::pos_of(rem / NV, rem % NV);

@@ -82,7 +82,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int Hq = a.Hkv * kGqa;
   for (int i = threadIdx.x; i < kMqR * kD; i += 128) {
     const int r = i / kD, d = i % kD, m = qg * kMqQ + (r >> 2);
-    qf[r][d] = m < a.M ? h2f(a.q[(((size_t)b * a.M + m) * Hq + hk * kGqa + (r & 3)) * kD + d]) : 0.f;
+    const int src = a.korder ? (int)(a.korder[(size_t)hk * kD + d] & 0x7F) : d;   // stored order
+    qf[r][d] = m < a.M ? h2f(a.q[(((size_t)b * a.M + m) * Hq + hk * kGqa + (r & 3)) * kD + src]) : 0.f;
   }
   for (int sl = threadIdx.x; sl < MT; sl += 128) {
     const int jj = sl / RUN, rem = sl % RUN;
@@ -456,8 +457,6 @@ static bool launch_mq_pool(int L, const PoolMqArgs& a, int G, int nch, int U, hi
   return false;
 }
 
-static size_t decode_mq_part_bytes(const kvq_layout* L, int M, int max_len);
-
 bool launch_decode_mq(const kvq_layout* L, const uint8_t* cache, const void* q, int M, float scale,
                       int max_len, void* out, float* lse, uint8_t* ws, void* stream) {
   hipStream_t s = (hipStream_t)stream;
@@ -477,16 +476,11 @@ bool launch_decode_mq(const kvq_layout* L, const uint8_t* cache, const void* q, 
   if (nch_used > nch) return false;          // workspace is sized for the finest split
   const uint8_t* korder = c.reorder ? cache + L->chan_order : nullptr;
   const uint8_t* vorder = c.reorder ? korder + (size_t)c.kv_heads * kD : nullptr;
-  const uint16_t* qs = (const uint16_t*)q;
-  if (korder) {
-    uint16_t* qp = (uint16_t*)(ws + align256z(decode_mq_part_bytes(L, M, max_len)));
-    if (!launch_gather_q(qs, korder, qp, c.batch * M * c.q_heads, c.q_heads, stream)) return false;
-    qs = qp;
-  }
   for (int p = 0; p < 2; ++p) {
     PoolMqArgs pa;
     pa.counters = (const int32_t*)(cache + L->counters);
-    pa.q = qs;
+    pa.q = (const uint16_t*)q;
+    pa.korder = korder;
     pa.part = (float*)ws;
     pa.kwords = (const uint32_t*)(cache + L->k_words[p]);
     pa.kmeta = (const uint32_t*)(cache + L->k_meta[p]);
@@ -509,19 +503,11 @@ bool launch_decode_mq(const kvq_layout* L, const uint8_t* cache, const void* q, 
   return hipGetLastError() == hipSuccess;
 }
 
-// partials, then, with stored channel orders, the gathered query rows at the
-// next 256-byte boundary
-static size_t decode_mq_part_bytes(const kvq_layout* L, int M, int max_len) {
+size_t decode_mq_ws_bytes(const kvq_layout* L, int M, int max_len) {
   int a, b;
   const int n = decode_chunks(L, max_len, &a, &b);
   const size_t U = (size_t)L->cfg.batch * L->cfg.kv_heads, nqg = (M + kMqQ - 1) / kMqQ;
   return U * nqg * (size_t)n * kMqR * kPartF * 4;
-}
-
-size_t decode_mq_ws_bytes(const kvq_layout* L, int M, int max_len) {
-  const size_t base = decode_mq_part_bytes(L, M, max_len);
-  const size_t qb = qperm_bytes(L, L->cfg.batch * M * L->cfg.q_heads);
-  return qb ? align256z(base) + qb : base;
 }
 
 }  // namespace kvq

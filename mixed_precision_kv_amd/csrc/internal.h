@@ -36,15 +36,7 @@ QuantWs quant_ws_plan(const kvq_layout* L, int T);
 // by value) to dk and dv.
 bool launch_write_order(uint8_t* dk, uint8_t* dv, const uint8_t* kbytes, const uint8_t* vbytes,
                         void* stream);
-// Query rows [rows][kD] gathered through the key channel order of their KV
-// head: dst[r][p] = src[r][order[hk][p]], hk = (r % Hq) / (Hq / Hkv).
-bool launch_gather_q(const uint16_t* src, const uint8_t* korder, uint16_t* dst, int rows, int Hq,
-                     void* stream);
-// Bytes of the gathered query rows a decode needs (0 without reorder).
-inline size_t qperm_bytes(const kvq_layout* L, int rows) {
-  return L->cfg.reorder ? (size_t)rows * 128 * 2 : 0;
-}
-inline size_t align256z(size_t x) { return (x + 255) & ~(size_t)255; }
+
 bool launch_rank_tiers(const kvq_layout* L, uint8_t* cache, const float* scores, int T, int n_hi,
                        int32_t* ranks_out, uint8_t* ws, const QuantWs& plan, void* stream);
 bool launch_quantize_tiered(const kvq_layout* L, uint8_t* cache, const void* k, const void* v,
@@ -74,6 +66,7 @@ struct PoolArgs {
   float c;            // softmax scale * log2(e)
   float* raw;         // or null: log2-domain scores out, [unit][head][cap_p]
   int cap_p;          // slots of this pool
+  const uint8_t* korder = nullptr;   // [Hkv][128] stored key channel order: q is read through it
 };
 // Slots per workgroup for one pool so that the grid fills the chip about once
 // (uses the kernel's occupancy; falls back to 8 macro tiles).
@@ -91,6 +84,7 @@ struct PoolMqArgs {
   int pool, Hkv, M, nqg, tiles, vrows, nch_total, part_off;
   int chunk;          // slots per workgroup (a whole number of macro tiles)
   float c;            // softmax scale * log2(e)
+  const uint8_t* korder = nullptr;   // [Hkv][128] stored key channel order: q is read through it
 };
 // Attention of M query tokens per sequence over a tiered cache (output and
 // log-sum-exp); false when a launch failed or the mode is not tiered.
