@@ -28,7 +28,11 @@ def _bounded(out, v):
     assert np.abs(o).max() <= vmax * 1.01 + 1e-2
 
 
-@pytest.mark.parametrize("w", [synth.W_SINGLE, synth.W_LLAMA, synth.W_LONG, synth.W_SKVQ], ids=lambda w: w.name)
+W_SKVQ_LONG = synth.W_LONG.shrink(name="skvq_long_b1_t128k", outlier_stride=32, reorder=True, clip=0.8)
+
+
+@pytest.mark.parametrize("w", [synth.W_SINGLE, synth.W_LLAMA, synth.W_LONG, synth.W_SKVQ, W_SKVQ_LONG],
+                         ids=lambda w: w.name)
 def test_tiered_fullsize(w):
     log(f"case {w.name} full size")
     inp = synth.make_inputs(w, steps=0)
