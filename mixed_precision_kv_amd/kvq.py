@@ -145,6 +145,9 @@ def set_channel_order(lay, cache, order, stream=None):
     the channel stored at position p."""
     import numpy as np
     o = np.ascontiguousarray(order, dtype=np.int32)
+    want = (2, lay.cfg.kv_heads, lay.cfg.head_dim)
+    if o.shape != want:                     # the library reads exactly this many entries
+        raise ValueError(f"channel order shape {o.shape}, expected {want}")
     st = lib().kvq_set_channel_order(ctypes.byref(lay), _ptr(cache), o.ctypes.data, _stream(stream))
     _check(st, "kvq_set_channel_order")
 

@@ -273,3 +273,5 @@ def test_set_channel_order_validation():
     with pytest.raises(kvq.KvqError) as e:                 # misaligned cache
         kvq.set_channel_order(lay, FAKE + 8, ident, stream=0)
     assert e.value.status == 1
+    with pytest.raises(ValueError):                        # too few entries for the layout
+        kvq.set_channel_order(lay, FAKE, ident[:1], stream=0)
