@@ -59,8 +59,8 @@
  *     that stream; the library never allocates, frees or synchronizes.
  *   - The caller owns every buffer.  Inputs are read-only.  The cache is one
  *     device buffer of kvq_layout.total_bytes, written by kvq_quantize and
- *     kvq_append, read by kvq_decode_attn, kvq_decode_attn_multi and
- *     kvq_decode_attn_mass.
+ *     kvq_append (and, for its channel orders, kvq_set_channel_order), read
+ *     by kvq_decode_attn, kvq_decode_attn_multi and kvq_decode_attn_mass.
  *   - Arguments are validated on the host before any launch; on error the
  *     call returns a nonzero kvq_status and launches nothing.  A failed
  *     launch returns KVQ_ERR_LAUNCH.  Faults inside kernels surface at the
@@ -200,7 +200,8 @@ kvq_status kvq_set_channel_order(const kvq_layout* lay, void* cache, const int32
 
 /* Quantize-on-write of a whole prefix (SemKV Abstract: rank, two adjacent
  * grids, every token kept; KVQuant / SKVQ for kchan mode).
- *   cache:   device, kvq_layout.total_bytes, fully (re)written.
+ *   cache:   device, kvq_layout.total_bytes, fully (re)written except for
+ *            the channel orders stored by kvq_set_channel_order, which it reads.
  *   k, v:    device fp16, element (b, t, h, d) at b*stride_b + t*stride_t +
  *            h*stride_h + d (d contiguous; strides in elements, multiples of 8).
  *   scores:  device fp32 [B][T] (tiered; NULL in kchan mode).
