@@ -404,6 +404,53 @@ def test_kchan_unit_structure():
     assert np.array_equal(vh[256:], v[256:].astype(np.float64))
 
 
+@pytest.mark.parametrize("kl,vl,vg,n_vl", [(4, 3, 32, 20), (3, 5, 64, 13), (8, 6, 128, 12)])
+def test_kchan_unit_value_half(kl, vl, vg, n_vl):
+    """The value half of a per-channel-key unit: values are quantized per
+    token in groups of v_group consecutive channels at v_levels (not at the
+    key levels, not per channel), with the exact group minimum as zero, the
+    scale within one fp16 ulp of the exact range / (v_levels - 1), codes
+    the exact round-half-even of (x - z) / s on the grid; the column words
+    unpack, n_vl digits each (worked by hand: 3^20, 5^13 and 6^12 are the
+    largest powers at most 2^32), back to the codes along the slot axis; the
+    dequantized values are z + c s and within half a step of the input."""
+    w = synth.W_KCHAN.shrink(tokens=128 * 3 + 50, batch=1, kv_heads=1, q_heads=4, name="tiny5v",
+                             k_levels=kl, v_levels=vl, v_group=vg)
+    inp = synth.make_inputs(w)
+    k, v = inp.k[0, :, 0], inp.v[0, :, 0]
+    v = v.copy()
+    v[3, :vg] = np.float16(0.625)                                # a constant group
+    v[7, 1] = np.float16(-0.0); v[7, 2] = np.float16(0.0)
+    u = O.KChanUnit(k, v, w)
+    nq, ng = u.n_q, 128 // vg
+    assert nq == 256
+    assert u.v_scale.shape == (nq, ng) and u.v_zero.shape == (nq, ng) and u.v_codes.shape == (nq, 128)
+    assert int(u.v_codes.max()) == vl - 1 and vl != kl
+    for t in range(nq):
+        for g in range(ng):
+            xs = [Fraction(float(x)) for x in v[t, g * vg:(g + 1) * vg]]
+            mn, mx = min(xs), max(xs)
+            assert Fraction(float(u.v_zero[t, g])) == mn
+            s = Fraction(float(u.v_scale[t, g]))
+            target = (mx - mn) / (vl - 1)
+            ulp = Fraction(2) ** (math.frexp(float(max(s, target)) or 1.0)[1] - 11) if target else 0
+            assert abs(s - target) <= ulp, (t, g)
+            for i, xv in enumerate(xs):
+                want = 0 if s == 0 else min(max(_rne((xv - mn) / s), 0), vl - 1)
+                assert u.v_codes[t, g * vg + i] == want, (t, g, i)
+    words = u.v_words()
+    assert words.shape == (-(-nq // n_vl), 128)
+    digits = O.unpack_digits(words, vl, n_vl)                    # [row][channel][digit]
+    assert np.array_equal(digits.transpose(0, 2, 1).reshape(-1, 128)[:nq], u.v_codes)
+    assert not digits.transpose(0, 2, 1).reshape(-1, 128)[nq:].any()
+    vh = u.v_hat()[:nq]
+    step = np.repeat(u.v_scale.astype(np.float64), vg, axis=1)
+    zero = np.repeat(u.v_zero.astype(np.float64), vg, axis=1)
+    assert np.array_equal(vh, zero + u.v_codes.astype(np.float64) * step)
+    assert np.all(np.abs(vh - v[:nq].astype(np.float64)) <= step / 2 * (1 + 2.0 ** -20) + 1e-12)
+    assert np.array_equal(u.v_hat()[nq:], v[nq:].astype(np.float64))
+
+
 # --------------------------------------------------------------- storage ---
 def test_storage_ratio_closed_forms():
     """Layout bytes per (sequence, KV head), worked by hand for the 32768-token
