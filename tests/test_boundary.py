@@ -77,7 +77,8 @@ def _cfg(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(head_dim=64), 2), (dict(q_heads=8), 2), (dict(levels_hi=2), 2), (dict(levels_lo=17), 2),
+    (dict(head_dim=64), 2), (dict(q_heads=8), 2), (dict(levels_hi=2), 2), (dict(levels_lo=17), 2), (dict(levels_hi=9), 2),
+    (dict(levels_lo=9), 2),
     (dict(group=48), 2), (dict(capacity=0), 1), (dict(batch=0), 1), (dict(mode=7), 1),
     (dict(cap_hi=100, cap_lo=100), 1), (dict(cap_hi=5000), 1),
     (dict(reorder=2), 1), (dict(clip=-0.5), 1), (dict(clip=1.5), 1), (dict(clip=float("nan")), 1),
