@@ -65,9 +65,15 @@
  *     call returns a nonzero kvq_status and launches nothing.  A failed
  *     launch returns KVQ_ERR_LAUNCH.  Faults inside kernels surface at the
  *     caller's next synchronization.
- *   - Inputs must be finite.  Group scales must be finite in fp16; value
- *     group scales must stay below 1024 (the decode kernel forms fp16
- *     products of softmax weights and value scales).
+ *   - Inputs must be finite, and so must every group scale in fp16.  The
+ *     decode kernels form fp16 products 2^6 p * s of a softmax weight p <= 1
+ *     and a value scale s; quantize and append set bit 1 of the sequence's
+ *     counters[b][3] when they store a value scale of 1024 or more, and the
+ *     decode kernels then use s / 2^6 in that product (for that sequence
+ *     only), so every finite scale is accepted.
+ *   - Per-channel-key mode: the decode kernel forms fp16 4 q_d s_d from the
+ *     query and each channel's key scale, so |q_d| * s_d must stay below
+ *     16376.
  *   - head_dim must be 128; q_heads / kv_heads must be 4 (grouped-query
  *     attention with four query heads per KV head).
  *   - Calls on one cache must not overlap (the library keeps no locks).
@@ -103,8 +109,8 @@ typedef struct kvq_config {
   int32_t head_dim;       /* D = 128 */
   int32_t capacity;       /* max tokens per sequence */
   /* tiered mode */
-  int32_t levels_hi;      /* L_hi in [3, 16] */
-  int32_t levels_lo;      /* L_lo in [3, 16] */
+  int32_t levels_hi;      /* L_hi in [3, 8]: the decode kernels expand digits through */
+  int32_t levels_lo;      /* L_lo in [3, 8]   per-level tables (else KVQ_ERR_UNSUPPORTED) */
   int32_t group;          /* 32, 64 or 128 values per (scale, zero) */
   int32_t cap_hi;         /* slots reserved per hi pool (0 -> capacity) */
   int32_t cap_lo;         /* slots reserved per lo pool (0 -> capacity) */
@@ -126,7 +132,9 @@ typedef struct kvq_config {
  *
  * unit u = b * kv_heads + h.  Tiered pools p = 0 (hi), 1 (lo).
  *
- *   counters  int32 [B][4]  = { length, n_hi, n_lo, 0 }
+ *   counters  int32 [B][4]  = { length, n_hi, n_lo, flags } (kchan: { length,
+ *             n_q, fp16 window tokens, flags }); flags bit 0: an append
+ *             found its pool full; bit 1: a value scale >= 1024 is stored
  *   tokmap    uint32 [B][capacity]: slot | tier << 31 (tokens < length)
  *   sorted    float [B][capacity]: scores present, ascending (first length)
  *   key words (uint32) of slot s in pool p, word w < kw[p]:
@@ -223,8 +231,9 @@ kvq_status kvq_quantize(const kvq_layout* lay, void* cache,
  * sequence: tier from the running median, quantize K and V of every KV head
  * on that grid, store at the tier's next slot, record the score.
  *   k_new, v_new: device fp16 [B][Hkv][D];  score_new: device fp32 [B].
- *   A sequence whose pool is full is left unchanged and its counters[b][3]
- *   is set to 1 (the host can read it back); other sequences proceed. */
+ *   A sequence whose pool is full is left unchanged and bit 0 of its
+ *   counters[b][3] is set (the host can read it back); other sequences
+ *   proceed. */
 kvq_status kvq_append(const kvq_layout* lay, void* cache,
                       const void* k_new, const void* v_new,
                       const float* score_new, void* stream);

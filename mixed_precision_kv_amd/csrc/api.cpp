@@ -226,9 +226,7 @@ extern "C" kvq_status kvq_decode_attn(const kvq_layout* lay, const void* cache, 
   if (max_len > lay->cfg.capacity) return KVQ_ERR_CAPACITY;
   size_t need = kvq_workspace_bytes(lay, KVQ_OP_DECODE, max_len);
   if (!ws || !aligned16(ws) || ws_bytes < need) return KVQ_ERR_WORKSPACE;
-  if (!launch_decode(lay, (const uint8_t*)cache, q, softmax_scale, max_len, out, (uint8_t*)ws, stream))
-    return KVQ_ERR_LAUNCH;
-  return KVQ_OK;
+  return launch_decode(lay, (const uint8_t*)cache, q, softmax_scale, max_len, out, (uint8_t*)ws, stream);
 }
 
 extern "C" size_t kvq_multi_workspace_bytes(const kvq_layout* lay, int32_t n_queries,
@@ -253,10 +251,8 @@ extern "C" kvq_status kvq_decode_attn_multi(const kvq_layout* lay, const void* c
   if (lay->cfg.mode != KVQ_MODE_TIERED) return KVQ_ERR_UNSUPPORTED;
   size_t need = kvq_multi_workspace_bytes(lay, n_queries, max_len);
   if (!ws || !aligned16(ws) || ws_bytes < need) return KVQ_ERR_WORKSPACE;
-  if (!launch_decode_mq(lay, (const uint8_t*)cache, q, n_queries, softmax_scale, max_len, out, lse,
-                        (uint8_t*)ws, stream))
-    return KVQ_ERR_LAUNCH;
-  return KVQ_OK;
+  return launch_decode_mq(lay, (const uint8_t*)cache, q, n_queries, softmax_scale, max_len, out, lse,
+                          (uint8_t*)ws, stream);
 }
 
 extern "C" kvq_status kvq_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t n_workgroups,
@@ -278,8 +274,6 @@ extern "C" kvq_status kvq_decode_attn_mass(const kvq_layout* lay, const void* ca
   if (lay->cfg.mode != KVQ_MODE_TIERED) return KVQ_ERR_UNSUPPORTED;
   size_t need = kvq_workspace_bytes(lay, KVQ_OP_DECODE_MASS, max_len);
   if (!ws || !aligned16(ws) || ws_bytes < need) return KVQ_ERR_WORKSPACE;
-  if (!launch_decode(lay, (const uint8_t*)cache, q, softmax_scale, max_len, out, (uint8_t*)ws, stream,
-                     mass))
-    return KVQ_ERR_LAUNCH;
-  return KVQ_OK;
+  return launch_decode(lay, (const uint8_t*)cache, q, softmax_scale, max_len, out, (uint8_t*)ws, stream,
+                       mass);
 }

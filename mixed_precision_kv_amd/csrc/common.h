@@ -12,6 +12,22 @@ constexpr int kD = 128;          // head_dim supported by the kernels
 constexpr int kGqa = 4;          // query heads per KV head
 constexpr int kTile = 16;        // slots per key tile
 
+// Bits of counters[b][3]: the pool of the new token was full (append), and a
+// value group scale of 1024 or more is stored (the decode kernels then scale
+// their fp16 value operand down).
+constexpr int kFlagPoolFull = 1;
+constexpr int kFlagBigValueScale = 2;
+constexpr uint32_t kBigScaleBits = 0x6400u;   // fp16 1024.0
+
+// Sets kFlagBigValueScale of sequence b when any lane of the wave formed a
+// value scale (fp16 bits s_bits, non-negative) of 1024 or more: one atomic
+// per wave, only in waves that hold one.
+__device__ inline void flag_big_value_scale(int32_t* counters, int b, uint32_t s_bits) {
+  const unsigned long long m = __ballot((s_bits & 0x7FFFu) >= kBigScaleBits);
+  if (__builtin_expect(m != 0ull, 0) && (int)(threadIdx.x & 63) == __builtin_ctzll(m))
+    atomicOr(counters + b * 4 + 3, kFlagBigValueScale);
+}
+
 // Base-L digits per 32-bit word: max{n : L^n <= 2^32}.
 __host__ __device__ inline int codes_per_word(int L) {
   uint64_t p = 1;

@@ -404,8 +404,8 @@ size_t decode_ws_bytes(const kvq_layout* L, int max_len, bool mass) {
   return bytes;
 }
 
-bool launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, float scale,
-                   int max_len, void* out, uint8_t* ws, void* stream, float* mass) {
+kvq_status launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, float scale,
+                         int max_len, void* out, uint8_t* ws, void* stream, float* mass) {
   hipStream_t s = (hipStream_t)stream;
   const kvq_config& c = L->cfg;
   const int U = c.batch * c.kv_heads;
@@ -429,7 +429,7 @@ bool launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, flo
       nchp[p] = ceil_div(slots, chunk[p]);
     }
     const int nch_used = nchp[0] + nchp[1];
-    if (nch_used > nch) return false;          // workspace is sized for the finest split
+    if (nch_used > nch) return KVQ_ERR_WORKSPACE;   // the workspace holds the finest split
     // with the token mass: raw scores of both pools, then per-head (max, sum)
     float* raw[2];
     raw[0] = (float*)(ws + (size_t)U * nch * kGqa * kPartStride * 4);
@@ -457,7 +457,7 @@ bool launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, flo
       pa.raw = mass ? raw[p] : nullptr;
       pa.cap_p = L->cap[p];
       pa.korder = korder;
-      if (nchp[p] > 0 && !launch_decode_pool(lv[p], pa, c.group, nchp[p], U, stream)) return false;
+      if (nchp[p] > 0 && !launch_decode_pool(lv[p], pa, c.group, nchp[p], U, stream)) return KVQ_ERR_LAUNCH;
     }
     launch_merge((const float*)ws, (uint16_t*)out, U, nch_used, c.kv_heads, s, mass ? stats : nullptr,
                  vorder);
@@ -465,7 +465,7 @@ bool launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, flo
       k_token_mass<<<dim3(ceil_div(max_len, 256), c.batch), 256, 0, s>>>(
           a.counters, (const uint32_t*)(cache + L->tokmap), raw[0], raw[1], stats, mass, c.capacity,
           L->cap[0], L->cap[1], c.kv_heads, max_len);
-    return hipGetLastError() == hipSuccess;
+    return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
   } else {
     a.kwords[0] = (const uint32_t*)(cache + L->k_words[0]);
     a.kmeta[0] = (const uint32_t*)(cache + L->k_meta[0]);
@@ -474,21 +474,21 @@ bool launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, flo
     a.L[0] = c.k_levels; a.nv[0] = L->nv[0]; a.kw[0] = L->kw[0]; a.tiles[0] = L->tiles[0];
     a.vrows[0] = L->vrows[0];
     a.chunk[0] = decode_chunk_kchan(L);
-    if (a.chunk[0] > 640) return false;
+    if (a.chunk[0] > 640) return KVQ_ERR_UNSUPPORTED;
     a.vL = c.v_levels; a.vnv = L->vnv; a.vgroup = c.v_group; a.spv = c.sparse_per_vec;
     a.cap = c.capacity; a.kblocks = L->kblocks; a.win_cap = L->win_cap;
     a.sparse = (const uint32_t*)(cache + L->sparse);
     a.nwch = nch1;
     a.kwin = (const uint16_t*)(cache + L->k_win);
     a.vwin = (const uint16_t*)(cache + L->v_win);
-    if (L->win_cap > 640) return false;
+    if (L->win_cap > 640) return KVQ_ERR_UNSUPPORTED;
     if (!launch_decode_kchan_mfma(L, cache, q, a.scale_log2, a.part, nch0, nch1, nch, stream)) {
       const int gx = nch0 > nch1 ? nch0 : nch1;
       k_decode_kchan<<<dim3(gx, U, 2), kDecThreads, 0, s>>>(a);
     }
   }
   launch_merge((const float*)ws, (uint16_t*)out, U, nch, c.kv_heads, s);
-  return hipGetLastError() == hipSuccess;
+  return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
 }
 
 }  // namespace kvq

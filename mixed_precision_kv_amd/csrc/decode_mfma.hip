@@ -19,6 +19,8 @@
 // fp16 product of the weight and the scale; the zero-point term sum p_h z_g
 // is a dot product on the VALU.  Online softmax (base 2) per macro tile;
 // partials (m, l, acc) go to the workspace for the log-sum-exp merge.
+#include <atomic>
+
 #include "common.h"
 #include "internal.h"
 #include "tiling.h"
@@ -54,7 +56,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
   __shared__ float qf[kGqa][kD];
   __shared__ __attribute__((aligned(16))) _Float16 pw_lds[2][kGqa][4 * VK];  // 2^6 p, operand order (wave 0 -> 1)
   __shared__ float al_lds[2][kGqa];          // rescale factor per head
-  __shared__ __attribute__((aligned(16))) _Float16 vs_lds[NG][4 * VK];  // value scale (x MUL), operand order
+  __shared__ __attribute__((aligned(16))) _Float16 vs_lds[NG][4 * VK];  // value scale, operand order
   __shared__ __attribute__((aligned(16))) _Float16 vz_lds[NG][4 * VK];  // value zero, same order
   __shared__ int ppos_lds[MT];               // slot -> position in that order
   __shared__ int mpos_lds[64 * META_PER_LANE];
@@ -236,6 +238,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
     };
     VBuf nxt;
     load_v(nxt, s_begin);
+    // value scales of 1024 and above (flagged per sequence by quantize and
+    // append) enter the fp16 product divided by 2^6, so that 2^6 p * s stays
+    // finite for every finite fp16 scale
+    const bool vbig = (a.counters[b * 4 + 3] & kFlagBigValueScale) != 0;
     // A-operand view: lane (r, j) holds row r = (sub-group sg, head h) over
     // the operand positions of lane group j
     const int h = n & 3, g = (n >> 2) / SUB;
@@ -263,18 +269,16 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
           zacc *= alh;
         }
         // value (scale, zero) in operand order, as fp16.  Operand digits are
-        // 1 + d/MUL on power-of-two grids, so the scale carries MUL (exact)
-        // and the affine offset is removed at the end through asum.  Only
-        // this wave uses vs/vz; its LDS accesses execute in order.
+        // 1 + d/MUL on power-of-two grids; MUL and the affine offset (removed
+        // through asum) are applied in fp32 at the end.  Only this wave uses
+        // vs/vz; its LDS accesses execute in order.
 #pragma unroll
         for (int k = 0; k < META_PER_LANE; ++k) {
           const int e = lane + 64 * k;
           if (META % 64 == 0 || e < META) {
             const int gg = (e / 16) % NG;
             const uint32_t mw = cur.vm[k];
-            const _Float16 sv = AFF ? (_Float16)(h2f(mw & 0xFFFFu) * MUL)
-                                    : __builtin_bit_cast(_Float16, (uint16_t)(mw & 0xFFFFu));
-            vs_lds[gg][mpos[k]] = sv;
+            vs_lds[gg][mpos[k]] = value_scale_operand(mw, vbig);
             vz_lds[gg][mpos[k]] = __builtin_bit_cast(_Float16, (uint16_t)(mw >> 16));
           }
         }
@@ -315,13 +319,14 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
     // acc rows (sg = j, h) hold channels of sub-group j
+    const float vfac = MUL * (vbig ? kBigValueShift : 1.0f);
 #pragma unroll
     for (int v = 0; v < 8; ++v) {
       if ((v >> 1) != j) continue;           // channels 16v..16v+15 belong to sub-group v/2
       const int d = 16 * v + n;
 #pragma unroll
       for (int hh = 0; hh < 4; ++hh) {
-        const float t = acc[v][hh] + zred[4 * j + hh] - (AFF ? asum[hh] : 0.f);
+        const float t = (acc[v][hh] - (AFF ? asum[hh] : 0.f)) * vfac + zred[4 * j + hh];
         part[hh * kPartF + 4 + d] = t * (1.0f / kAScale);
       }
     }
@@ -373,25 +378,31 @@ static int occupancy(int L, int G) {
   return 0;
 }
 
+// Per-device caches of the CU count and of the pool kernels' occupancy
+// (value + 1; 0: not read yet).  Threads that race on a first read compute
+// the same value, so relaxed atomics suffice.
+constexpr int kMaxDevices = 64;
+static std::atomic<int> g_cus[kMaxDevices];
+static std::atomic<int> g_occ[kMaxDevices][9][3];
+
 int decode_pool_chunk(int L, int G, int U, int slots_per_unit) {
-  static int cus = -1;
-  static int occ[17][3];
-  static bool have[17][3];
   const int gi = G == 32 ? 0 : G == 64 ? 1 : 2;
   const int mt = macro_tile_slots(L);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  const bool cached = dev >= 0 && dev < kMaxDevices && L >= 0 && L <= 8;
+  int cus = cached ? g_cus[dev].load(std::memory_order_relaxed) - 1 : -1;
   if (cus < 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
-      cus = n;
-    else
-      cus = 0;
+    int n = 0;
+    cus = (dev >= 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) ? n : 0;
+    if (cached) g_cus[dev].store(cus + 1, std::memory_order_relaxed);
   }
-  if (!have[L][gi]) {
-    occ[L][gi] = occupancy(L, G);
-    have[L][gi] = true;
+  int occ = cached ? g_occ[dev][L][gi].load(std::memory_order_relaxed) - 1 : -1;
+  if (occ < 0) {
+    occ = occupancy(L, G);
+    if (cached) g_occ[dev][L][gi].store(occ + 1, std::memory_order_relaxed);
   }
-  const long waves = (long)cus * occ[L][gi];
+  const long waves = (long)cus * occ;
   if (waves <= 0 || slots_per_unit <= 0) return 8 * mt;
   // macro tiles per wave so that U * chunks ~ waves (one round of the chip)
   const long tiles_per_unit = (slots_per_unit + mt - 1) / mt;
@@ -718,6 +729,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   }
   __syncthreads();
   // ---- softmax over the chunk (wave w: head w) and value meta staging
+  // (flagged sequences: value scales enter the fp16 product divided by 2^6)
+  const bool vbig = (a.counters[b * 4 + 3] & kFlagBigValueScale) != 0;
   {
     const int h = w;
     float mx = -INFINITY;
@@ -743,7 +756,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       const int jj = sl / (R * NVV), rr = sl % (R * NVV);
       const int pos = w * 4 * VK + jj * VK + DV::pos_of(rr / NVV, rr % NVV);
       const bool ok = s_begin + VU * w + sl < s_end;
-      vsl[g][pos] = __builtin_bit_cast(_Float16, (uint16_t)(ok ? (vm[k] & 0xFFFFu) : 0u));
+      vsl[g][pos] = value_scale_operand(ok ? vm[k] : 0u, vbig);
       vzl[g][pos] = __builtin_bit_cast(_Float16, (uint16_t)(ok ? (vm[k] >> 16) : 0u));
     }
   }
@@ -783,7 +796,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     for (int v = 0; v < 8; ++v) {
       if ((v >> 1) != j) continue;             // channels 16v..16v+15 are in group v/2
 #pragma unroll
-      for (int hh = 0; hh < kGqa; ++hh) red[w][hh][16 * v + n] = acc[v][hh] + zr[w][4 * j + hh];
+      for (int hh = 0; hh < kGqa; ++hh)
+        red[w][hh][16 * v + n] = acc[v][hh] * (vbig ? kBigValueShift : 1.0f) + zr[w][4 * j + hh];
     }
   }
   __syncthreads();

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
   __shared__ uint32_t km_lds[META_PER_LANE * 64];   // key (scale, zero) of the macro tile
   __shared__ __attribute__((aligned(16))) _Float16 pw_lds[2][kMqR][4 * VK];  // 2^6 p, operand order
   __shared__ float al_lds[2][kMqR];          // rescale factor per row
-  __shared__ __attribute__((aligned(16))) _Float16 vs_lds[NG][4 * VK];  // value scale (x MUL)
+  __shared__ __attribute__((aligned(16))) _Float16 vs_lds[NG][4 * VK];  // value scale
   __shared__ __attribute__((aligned(16))) _Float16 vz_lds[NG][4 * VK];  // value zero
   __shared__ int ppos_lds[MT];               // slot -> operand position
   __shared__ int mpos_lds[64 * META_PER_LANE];
@@ -270,6 +270,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
     };
     VBuf nxt;
     load_v(nxt, s_begin);
+    // flagged sequences: value scales enter the fp16 product divided by 2^6
+    const bool vbig = (a.counters[b * 4 + 3] & kFlagBigValueScale) != 0;
     // A-operand view: lane (n, j) holds row n = (query n / 4, head n % 4)
     // over the operand positions of lane group j
     float zacc[NG];                          // 2^6 sum p z per group (row n)
@@ -310,9 +312,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
           if (META % 64 == 0 || e < META) {
             const int gg = (e / 16) % NG;
             const uint32_t mw = cur.vm[k];
-            const _Float16 sv = AFF ? (_Float16)(h2f(mw & 0xFFFFu) * MUL)
-                                    : __builtin_bit_cast(_Float16, (uint16_t)(mw & 0xFFFFu));
-            vs_lds[gg][mpos[k]] = sv;
+            vs_lds[gg][mpos[k]] = value_scale_operand(mw, vbig);
             vz_lds[gg][mpos[k]] = __builtin_bit_cast(_Float16, (uint16_t)(mw >> 16));
           }
         }
@@ -370,12 +370,14 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
+    // power-of-two grids: digits are 1 + d/MUL, so sum p s d = MUL (acc - asum)
+    const float vfac = MUL * (vbig ? kBigValueShift : 1.0f);
 #pragma unroll
     for (int v = 0; v < 8; ++v) {
       const int sg = v >> 1, g = sg / SUB, d = 16 * v + n;
 #pragma unroll
       for (int hh = 0; hh < kGqa; ++hh) {
-        const float t = acc[v][hh] + zred[g][4 * j + hh] - (AFF ? asum[sg][hh] : 0.f);
+        const float t = (acc[v][hh] - (AFF ? asum[sg][hh] : 0.f)) * vfac + zred[g][4 * j + hh];
         part[(4 * j + hh) * kPartF + 4 + d] = t * (1.0f / kAScale);
       }
     }
@@ -457,11 +459,11 @@ static bool launch_mq_pool(int L, const PoolMqArgs& a, int G, int nch, int U, hi
   return false;
 }
 
-bool launch_decode_mq(const kvq_layout* L, const uint8_t* cache, const void* q, int M, float scale,
-                      int max_len, void* out, float* lse, uint8_t* ws, void* stream) {
+kvq_status launch_decode_mq(const kvq_layout* L, const uint8_t* cache, const void* q, int M, float scale,
+                            int max_len, void* out, float* lse, uint8_t* ws, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   const kvq_config& c = L->cfg;
-  if (c.mode != KVQ_MODE_TIERED) return false;
+  if (c.mode != KVQ_MODE_TIERED) return KVQ_ERR_UNSUPPORTED;
   const int U = c.batch * c.kv_heads, nqg = (M + kMqQ - 1) / kMqQ;
   int nch0, nch1;
   const int nch = decode_chunks(L, max_len, &nch0, &nch1);
@@ -473,7 +475,7 @@ bool launch_decode_mq(const kvq_layout* L, const uint8_t* cache, const void* q, 
     nchp[p] = ceil_div(slots, chunk[p]);
   }
   const int nch_used = nchp[0] + nchp[1];
-  if (nch_used > nch) return false;          // workspace is sized for the finest split
+  if (nch_used > nch) return KVQ_ERR_WORKSPACE;   // the workspace holds the finest split
   const uint8_t* korder = c.reorder ? cache + L->chan_order : nullptr;
   const uint8_t* vorder = c.reorder ? korder + (size_t)c.kv_heads * kD : nullptr;
   for (int p = 0; p < 2; ++p) {
@@ -496,11 +498,11 @@ bool launch_decode_mq(const kvq_layout* L, const uint8_t* cache, const void* q, 
     pa.part_off = p ? nchp[0] : 0;
     pa.chunk = chunk[p];
     pa.c = scale * 1.4426950408889634f;
-    if (nchp[p] > 0 && !launch_mq_pool(lv[p], pa, c.group, nchp[p], U, s)) return false;
+    if (nchp[p] > 0 && !launch_mq_pool(lv[p], pa, c.group, nchp[p], U, s)) return KVQ_ERR_LAUNCH;
   }
   k_merge_mq<<<U * nqg * kMqR, kD, 0, s>>>((const float*)ws, (uint16_t*)out, lse, nch_used, nqg, M,
                                            c.kv_heads, vorder);
-  return hipGetLastError() == hipSuccess;
+  return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
 }
 
 size_t decode_mq_ws_bytes(const kvq_layout* L, int M, int max_len) {

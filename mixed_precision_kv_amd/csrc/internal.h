@@ -46,8 +46,11 @@ bool launch_quantize_kchan(const kvq_layout* L, uint8_t* cache, const void* k, c
                            int64_t sb, int64_t st, int64_t sh, int T, void* stream);
 bool launch_append(const kvq_layout* L, uint8_t* cache, const void* k_new, const void* v_new,
                    const float* score_new, void* stream);
-bool launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, float scale,
-                   int max_len, void* out, uint8_t* ws, void* stream, float* mass = nullptr);
+// Decode launchers return KVQ_ERR_WORKSPACE when the chunk split they chose
+// needs more partials than the workspace holds, KVQ_ERR_LAUNCH when a launch
+// failed.
+kvq_status launch_decode(const kvq_layout* L, const uint8_t* cache, const void* q, float scale,
+                         int max_len, void* out, uint8_t* ws, void* stream, float* mass = nullptr);
 // Workspace of a decode (partials), plus, with the token mass, the pools'
 // raw scores and the per-head (max, sum) after the merge.
 size_t decode_ws_bytes(const kvq_layout* L, int max_len, bool mass);
@@ -87,9 +90,9 @@ struct PoolMqArgs {
   const uint8_t* korder = nullptr;   // [Hkv][128] stored key channel order: q is read through it
 };
 // Attention of M query tokens per sequence over a tiered cache (output and
-// log-sum-exp); false when a launch failed or the mode is not tiered.
-bool launch_decode_mq(const kvq_layout* L, const uint8_t* cache, const void* q, int M, float scale,
-                      int max_len, void* out, float* lse, uint8_t* ws, void* stream);
+// log-sum-exp); KVQ_ERR_UNSUPPORTED when the mode is not tiered.
+kvq_status launch_decode_mq(const kvq_layout* L, const uint8_t* cache, const void* q, int M, float scale,
+                            int max_len, void* out, float* lse, uint8_t* ws, void* stream);
 size_t decode_mq_ws_bytes(const kvq_layout* L, int M, int max_len);
 // Read-stream probe (every byte once, 16-byte loads) over nwg workgroups.
 bool launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int nwg, void* stream);

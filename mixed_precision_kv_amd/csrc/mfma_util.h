@@ -12,6 +12,16 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPartF = 4 + kD;      // floats per head in a partial: m, l, pad, pad, acc[128]
 constexpr float kAScale = 64.0f;    // value-operand weights carry 2^6 (fp16 range)
+constexpr float kBigValueShift = 64.0f;   // flagged sequences: value scales enter as s / 2^6
+
+// fp16 value scale of a (scale, zero) word as the factor of the value
+// operand A = 2^6 p * s.  p <= 1, so A <= 2^6 s, which is finite for
+// s < 1024; a sequence holding a larger value scale is flagged by the
+// quantizers and its scales enter divided by 2^6 (exact unless subnormal).
+__device__ inline _Float16 value_scale_operand(uint32_t meta, bool big) {
+  const uint16_t sb = (uint16_t)(meta & 0xFFFFu);
+  return big ? (_Float16)(h2f(sb) * (1.0f / kBigValueShift)) : __builtin_bit_cast(_Float16, sb);
+}
 
 __device__ inline float dpp_ror(float v, int n) {
   // row_ror:n within each row of 16 lanes

@@ -35,6 +35,7 @@ struct QuantArgs {
   const uint8_t* korder = nullptr;   // [Hkv][128] stored key channel order, or null
   const uint8_t* vorder = nullptr;   // [Hkv][128] stored value channel order, or null
   float clip = 1.0f;                 // group min/max scale factor (1: none)
+  int32_t* counters = nullptr;       // [B][4]: flags word 3 gets kFlagBigValueScale
 };
 
 // Quantize one group of G fp16 values at src (16-byte aligned); codes to LDS.
@@ -85,6 +86,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_pool(QuantArgs a) {
       const int t = a.inv ? a.inv[(size_t)b * a.inv_cap + s] : s;
       const uint16_t* src = (kv ? a.v : a.k) + b * a.sb + (int64_t)t * a.st + h * a.sh + g * G;
       meta = quant_group<G>(src, a.L, dst);
+      if (kv && (meta & 0x7FFFu) >= kBigScaleBits) atomicOr(a.counters + b * 4 + 3, kFlagBigValueScale);
     } else {
 #pragma unroll
       for (int i2 = 0; i2 < G; ++i2) dst[i2] = 0;
@@ -380,6 +382,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows(QuantArgs a) {
       if constexpr (SKVQ) clip_range(mn, mx, a.clip);
       GroupQ gq = group_setup(mn, mx, L);
       if (gq.s == 0.0f) gq.r = 0.0f;               // all codes 0
+      if (kv) flag_big_value_scale(a.counters, b, gq.s_bits);
       const uint32_t meta = gq.s_bits | (mn << 16);
       const bool sub = (gq.s_bits & 0x7C00u) == 0u;    // zero or subnormal scale
       if (r < SL && (q % LPG) == 0) {
@@ -511,6 +514,7 @@ bool launch_quantize_tiered(const kvq_layout* L, uint8_t* cache, const void* k, 
     a.korder = L->cfg.reorder ? cache + L->chan_order : nullptr;
     a.vorder = L->cfg.reorder ? cache + L->chan_order + (size_t)L->cfg.kv_heads * kD : nullptr;
     a.clip = L->cfg.clip > 0.0f ? L->cfg.clip : 1.0f;
+    a.counters = (int32_t*)(cache + L->counters);
     if (!launch_pool(a, L->cfg.group, U, s)) return false;
   }
   return hipGetLastError() == hipSuccess;
@@ -809,6 +813,12 @@ bool launch_quantize_kchan(const kvq_layout* L, uint8_t* cache, const void* k, c
   const int nq = kchan_nq(L, T);
   const int nwin = T - nq;
   if (nwin > L->win_cap) return false;
+  // the window kernel also resets the counters, so it runs before the value
+  // quantizer, which may set a flag in them
+  k_kchan_window<<<dim3(std::max(1, ceil_div(L->win_cap * (kD / 8), 256)), U), 256, 0, s>>>(
+      (const uint16_t*)k, (const uint16_t*)v, sb, st, sh, c.kv_heads, nq, nwin, L->win_cap,
+      (uint16_t*)(cache + L->k_win), (uint16_t*)(cache + L->v_win),
+      (int32_t*)(cache + L->counters), c.batch);
   if (nq > 0) {
     KchanArgs ka;
     ka.k = (const uint16_t*)k;
@@ -837,11 +847,8 @@ bool launch_quantize_kchan(const kvq_layout* L, uint8_t* cache, const void* k, c
   a.kmeta = nullptr;
   a.vwords = (uint32_t*)(cache + L->v_words[0]);
   a.vmeta = (uint32_t*)(cache + L->v_meta[0]);
+  a.counters = (int32_t*)(cache + L->counters);
   if (!launch_pool(a, c.v_group, U, s)) return false;
-  k_kchan_window<<<dim3(std::max(1, ceil_div(L->win_cap * (kD / 8), 256)), U), 256, 0, s>>>(
-      (const uint16_t*)k, (const uint16_t*)v, sb, st, sh, c.kv_heads, nq, nwin, L->win_cap,
-      (uint16_t*)(cache + L->k_win), (uint16_t*)(cache + L->v_win),
-      (int32_t*)(cache + L->counters), c.batch);
   return hipGetLastError() == hipSuccess;
 }
 
@@ -923,7 +930,7 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
   }
   __syncthreads();
   if (!s_ok) {
-    if (tid == 0) cnt[3] = 1;
+    if (tid == 0) atomicOr(cnt + 3, kFlagPoolFull);
     return;
   }
   const int tier = s_tier, len = s_len, slot = s_slot;
@@ -958,6 +965,7 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
     const int u = b * a.Hkv + h;
     uint32_t* mp = kv ? a.vmeta[tier] : a.kmeta[tier];
     mp[(((size_t)u * tiles + slot / kTile) * NG + g) * kTile + (slot % kTile)] = meta;
+    if (kv && (meta & 0x7FFFu) >= kBigScaleBits) atomicOr(cnt + 3, kFlagBigValueScale);
   }
   __syncthreads();
   const uint32_t pos = s_le;

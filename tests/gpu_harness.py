@@ -140,3 +140,63 @@ def compare_tiered_unit(buf, lay, pools, u, what=""):
 def oracle_unit_attention(w, q, b, h, khat, vhat, scale):
     g = w.q_heads // w.kv_heads
     return O.decode_unit(q[b, h * g:(h + 1) * g].astype(np.float64), khat, vhat, float(scale))
+
+
+def check_tiered(w, inp, run, decode=True):
+    rank, tokmap, counts, inv = oracle_tiers(w, inp)
+    buf = run.buf()
+    lay = run.lay
+    assert np.array_equal(run.ranks.cpu().numpy(), rank), "ranks"
+    assert np.array_equal(LV.tokmap(buf, lay)[:, :w.tokens], tokmap), "token map"
+    cnt = LV.counters(buf, lay)
+    assert np.array_equal(cnt[:, 0], np.full(w.batch, w.tokens)) and np.array_equal(cnt[:, 1:3], counts)
+    srt = LV.sorted_scores(buf, lay)[:, :w.tokens]
+    assert np.array_equal(srt, np.sort(inp.scores, axis=1)), "sorted scores"
+    out = run.decode(inp.q) if decode else None
+    errs = []
+    for b in range(w.batch):
+        for h in range(w.kv_heads):
+            u = b * w.kv_heads + h
+            pools = oracle_unit(w, inp, inv, b, h)
+            compare_tiered_unit(buf, lay, pools, u, f"{w.name} b{b} h{h}")
+            if decode:
+                kh = np.concatenate([pools[0].k_hat(), pools[1].k_hat()])
+                vh = np.concatenate([pools[0].v_hat(), pools[1].v_hat()])
+                ref = oracle_unit_attention(w, inp.q, b, h, kh, vh, run.scale)
+                g = w.q_heads // w.kv_heads
+                errs.append(O.row_rel_err(out[b, h * g:(h + 1) * g], ref))
+    if decode:
+        log(f"{w.name}: max row rel err {max(errs):.3e}")
+        assert max(errs) <= TOL
+
+
+def check_kchan(w, inp, run, units=None):
+    buf = run.buf()
+    g = LV.kchan_unit_arrays(buf, run.lay)
+    out = run.decode(inp.q)
+    errs = []
+    for b in range(w.batch):
+        for h in range(w.kv_heads):
+            u = b * w.kv_heads + h
+            if units is not None and u not in units:
+                continue
+            ref = O.KChanUnit(inp.k[b, :, h], inp.v[b, :, h], w)
+            nq = ref.n_q
+            nb = nq // w.k_block
+            assert np.array_equal(g["k_words"][u, :nq], ref.k_words()), f"k_words u{u}"
+            assert np.array_equal(g["k_scale"][u, :nb].view(np.uint16), ref.k_scale.view(np.uint16))
+            assert np.array_equal(g["k_zero"][u, :nb].view(np.uint16), ref.k_zero.view(np.uint16))
+            sp = g["sparse"][u, :nq]
+            assert np.array_equal(sp >> 16, ref.sp_ch), f"sparse channels u{u}"
+            assert np.array_equal((sp & 0xFFFF).astype(np.uint16), ref.sp_val.view(np.uint16))
+            rows = -(-nq // O.codes_per_word(w.v_levels))
+            assert np.array_equal(g["v_words"][u, :rows], ref.v_words()), f"v_words u{u}"
+            assert np.array_equal(g["v_scale"][u, :nq].view(np.uint16), ref.v_scale.view(np.uint16))
+            assert np.array_equal(g["v_zero"][u, :nq].view(np.uint16), ref.v_zero.view(np.uint16))
+            nw = w.tokens - nq
+            assert np.array_equal(g["k_win"][u, :nw], ref.k_win) and np.array_equal(g["v_win"][u, :nw], ref.v_win)
+            r = oracle_unit_attention(w, inp.q, b, h, ref.k_hat(), ref.v_hat(), run.scale)
+            gq = w.q_heads // w.kv_heads
+            errs.append(O.row_rel_err(out[b, h * gq:(h + 1) * gq], r))
+    log(f"{w.name}: max row rel err {max(errs):.3e}")
+    assert max(errs) <= TOL

@@ -7,38 +7,11 @@ import pytest
 from mixed_precision_kv_amd import synth
 from oracle import kvq_oracle as O
 import layout_view as LV
-from gpu_harness import GpuRun, TOL, compare_tiered_unit, log, oracle_tiers, oracle_unit, oracle_unit_attention
+from gpu_harness import (GpuRun, TOL, check_kchan as _check_kchan, check_tiered as _check_tiered,
+                         compare_tiered_unit, log, oracle_tiers, oracle_unit, oracle_unit_attention)
 
 pytestmark = pytest.mark.gpu
 
-
-
-def _check_tiered(w, inp, run, decode=True):
-    rank, tokmap, counts, inv = oracle_tiers(w, inp)
-    buf = run.buf()
-    lay = run.lay
-    assert np.array_equal(run.ranks.cpu().numpy(), rank), "ranks"
-    assert np.array_equal(LV.tokmap(buf, lay)[:, :w.tokens], tokmap), "token map"
-    cnt = LV.counters(buf, lay)
-    assert np.array_equal(cnt[:, 0], np.full(w.batch, w.tokens)) and np.array_equal(cnt[:, 1:3], counts)
-    srt = LV.sorted_scores(buf, lay)[:, :w.tokens]
-    assert np.array_equal(srt, np.sort(inp.scores, axis=1)), "sorted scores"
-    out = run.decode(inp.q) if decode else None
-    errs = []
-    for b in range(w.batch):
-        for h in range(w.kv_heads):
-            u = b * w.kv_heads + h
-            pools = oracle_unit(w, inp, inv, b, h)
-            compare_tiered_unit(buf, lay, pools, u, f"{w.name} b{b} h{h}")
-            if decode:
-                kh = np.concatenate([pools[0].k_hat(), pools[1].k_hat()])
-                vh = np.concatenate([pools[0].v_hat(), pools[1].v_hat()])
-                ref = oracle_unit_attention(w, inp.q, b, h, kh, vh, run.scale)
-                g = w.q_heads // w.kv_heads
-                errs.append(O.row_rel_err(out[b, h * g:(h + 1) * g], ref))
-    if decode:
-        log(f"{w.name}: max row rel err {max(errs):.3e}")
-        assert max(errs) <= TOL
 
 
 SMALL = [
@@ -165,38 +138,6 @@ def test_tiered_ties_zeros_and_constant_groups():
     run = GpuRun(w, inp)
     run.quantize()
     _check_tiered(w, inp, run)
-
-
-def _check_kchan(w, inp, run, units=None):
-    buf = run.buf()
-    g = LV.kchan_unit_arrays(buf, run.lay)
-    out = run.decode(inp.q)
-    errs = []
-    for b in range(w.batch):
-        for h in range(w.kv_heads):
-            u = b * w.kv_heads + h
-            if units is not None and u not in units:
-                continue
-            ref = O.KChanUnit(inp.k[b, :, h], inp.v[b, :, h], w)
-            nq = ref.n_q
-            nb = nq // w.k_block
-            assert np.array_equal(g["k_words"][u, :nq], ref.k_words()), f"k_words u{u}"
-            assert np.array_equal(g["k_scale"][u, :nb].view(np.uint16), ref.k_scale.view(np.uint16))
-            assert np.array_equal(g["k_zero"][u, :nb].view(np.uint16), ref.k_zero.view(np.uint16))
-            sp = g["sparse"][u, :nq]
-            assert np.array_equal(sp >> 16, ref.sp_ch), f"sparse channels u{u}"
-            assert np.array_equal((sp & 0xFFFF).astype(np.uint16), ref.sp_val.view(np.uint16))
-            rows = -(-nq // O.codes_per_word(w.v_levels))
-            assert np.array_equal(g["v_words"][u, :rows], ref.v_words()), f"v_words u{u}"
-            assert np.array_equal(g["v_scale"][u, :nq].view(np.uint16), ref.v_scale.view(np.uint16))
-            assert np.array_equal(g["v_zero"][u, :nq].view(np.uint16), ref.v_zero.view(np.uint16))
-            nw = w.tokens - nq
-            assert np.array_equal(g["k_win"][u, :nw], ref.k_win) and np.array_equal(g["v_win"][u, :nw], ref.v_win)
-            r = oracle_unit_attention(w, inp.q, b, h, ref.k_hat(), ref.v_hat(), run.scale)
-            gq = w.q_heads // w.kv_heads
-            errs.append(O.row_rel_err(out[b, h * gq:(h + 1) * gq], r))
-    log(f"{w.name}: max row rel err {max(errs):.3e}")
-    assert max(errs) <= TOL
 
 
 @pytest.mark.parametrize("T", [100, 255, 256, 434, 1408, 2000])
