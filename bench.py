@@ -1,17 +1,24 @@
 """Throughput of the mixed-precision KV-cache hot path on one MI355X.
 
-One step = quantize-on-write of the whole batch (rank, tier split, group
-quantize, base-L packing of K and V) followed by one decode-attention step of
-every sequence over the packed cache (split over the context, merged by
-log-sum-exp).  Default workload: the Llama-3.1-8B-shaped decode layer
-(batch 8, 8 KV heads, 32 query heads, head_dim 128, 32768 context tokens,
-6/5 levels, groups of 32).  Inputs are synthetic and resident in HBM before
-the timed region.
+Default workload: generation over a packed cache (batch 64, 8 KV heads, 32
+query heads, head_dim 128; a 16384-token prefix on 6/5-level grids with
+groups of 32, then 256 generation steps).  One step is the whole hot path
+over that batch: quantize-on-write of the prefix (rank, tier split, group
+quantize, base-L packing of K and V), then 256 times: append one token per
+sequence (running-median tier, quantize, pack) and one decode-attention step
+of every sequence over the packed cache (split over the context, merged by
+log-sum-exp).  Inputs, including every step's new tokens and queries, are
+synthetic and resident in HBM before the timed region.
 
-Prints one JSON line.  `value` is context tokens per second per query head
-over the whole step (B * Hq * T / step time).  Decode and quantize are also
-timed on their own with HIP events on the stream they run on; the decode
-loop rotates cache replicas so that its reads come from HBM rather than the
+Prints one JSON line.  `value` is decode-attention context tokens per second
+per query head over the whole step: the sum over the 256 decodes of
+B * Hq * (tokens in the cache) divided by the step time (prefix quantize and
+appends included).  Every quantize, append and decode of the timed steps is
+also bracketed by HIP events on the stream it runs on; `decode` and
+`quantize` report those live durations and `roofline` the dominant entry
+point (decode) against 8 TB/s with its algorithmic bytes.  Workloads
+without generation steps (--config) time quantize + one decode per step and
+rotate cache replicas so that decode reads come from HBM rather than the
 256 MB Infinity Cache.
 """
 from __future__ import annotations
@@ -84,67 +91,146 @@ def kernel_hash(*names):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel, khash):
+def measured_traffic(kernel, khash, workload):
     """HBM bytes per launch from committed rocprofv3 PMC summaries, only if the
-    kernel source is unchanged since the counters were taken."""
+    kernel source is unchanged since the counters were taken and they were
+    taken on this workload."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         tr = json.load(f)
     e = tr.get(kernel)
-    if not e or e.get("source_hash") != khash:
+    if not e or e.get("source_hash") != khash or e.get("workload") != workload:
         return None
     return e.get("bytes_per_launch")
 
 
 # ----------------------------------------------------------- cpu baseline ---
+def cpu_share():
+    """CPUs this process may use: its affinity set, bounded by a cgroup CPU
+    quota and by OMP_NUM_THREADS when the environment sets one (a GPU host
+    may allot a share of its cores to each GPU)."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            quota, period = f.read().split()[:2]
+        if quota != "max":
+            n = min(n, max(1, math.ceil(int(quota) / int(period))))
+    except (OSError, ValueError):
+        pass
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _one_blas_thread():
+    try:
+        import threadpoolctl
+        threadpoolctl.threadpool_limits(1)
+    except ImportError:
+        pass
+
+
 def _oracle_unit(args):
+    """Oracle work of one (sequence, KV head): quantize + pack of its prefix,
+    then `gen` generation steps (running-median tier, quantize + store of the
+    new token, fp64 attention over the whole cache), or one fp64 decode when
+    the workload has no generation steps.  Returns (prefix s, per-step s)."""
     import numpy as np
     from oracle import kvq_oracle as O
-    k_unit, v_unit, inv_b, q_group, w_fields, scale = args
+    k_unit, v_unit, inv_b, scores_b, q_group, w_fields, scale, gen = args
     L_hi, L_lo, G, skvq = w_fields
+    t0 = time.perf_counter()
     pools = O.quantize_tiered_unit(k_unit, v_unit, inv_b, L_hi, L_lo, G, **skvq)
-    pools[0].k_words(), pools[0].v_words(), pools[1].k_words(), pools[1].v_words()
-    kh = np.concatenate([pools[0].k_hat(), pools[1].k_hat()])
-    vh = np.concatenate([pools[0].v_hat(), pools[1].v_hat()])
-    return O.decode_unit(q_group, kh, vh, scale)
+    for p in pools:
+        p.k_words(), p.v_words()
+    t1 = time.perf_counter()
+    if not gen:
+        kh = np.concatenate([pools[0].k_hat(), pools[1].k_hat()])
+        vh = np.concatenate([pools[0].v_hat(), pools[1].v_hat()])
+        O.decode_unit(q_group, kh, vh, scale)
+        return t1 - t0, time.perf_counter() - t1
+    med = O.RunningMedian(scores_b)
+    for st in gen:
+        tier = med.decide_and_insert(st["score"])
+        pools[tier].add_rows(st["k"][None], st["v"][None])
+        pools[tier].k_words(), pools[tier].v_words()
+        kh = np.concatenate([pools[0].k_hat(), pools[1].k_hat()])
+        vh = np.concatenate([pools[0].v_hat(), pools[1].v_hat()])
+        O.decode_unit(st["q"], kh, vh, scale)
+    return t1 - t0, (time.perf_counter() - t1) / len(gen)
 
 
-def cpu_baseline(w, inp, scale, max_units, workers):
-    """The oracle as it is (rank + tier split of every sequence; quantize,
-    pack and fp64 attention of a sample of (sequence, KV head) units) on the
-    host, units spread over `workers` processes."""
+def cpu_baseline(w, inp, scale, units_per_worker, gen_sample, workers):
+    """The oracle as it is, on the host's CPU share: rank + tier split of
+    every sequence, then for a sample of (sequence, KV head) units (spread
+    over `workers` processes) the quantize + pack of the prefix and, for a
+    generation workload, `gen_sample` of its append + fp64 decode steps.
+    The measured per-unit times are scaled to one whole bench step (every
+    unit, every generation step) at `workers`-way parallelism."""
     import numpy as np
     from mixed_precision_kv_amd import synth
     from oracle import kvq_oracle as O
-    os.environ.setdefault("OMP_NUM_THREADS", "1")
     t0 = time.perf_counter()
     rank = O.rank_desc(inp.scores)
     _, _, inv = O.tiers_and_slots(rank, w.n_hi)
     t_rank = time.perf_counter() - t0
     g = w.q_heads // w.kv_heads
-    units = [(b, h) for b in range(w.batch) for h in range(w.kv_heads)][:max_units]
+    n_all = w.batch * w.kv_heads
+    n_units = min(n_all, units_per_worker * workers)
+    stride = max(1, n_all // n_units)
+    units = [(u // w.kv_heads, u % w.kv_heads) for u in range(0, n_all, stride)][:n_units]
     orders = synth.channel_orders(w) if w.reorder else None
 
     def skvq(h):
         kw = dict(order_k=orders[0, h], order_v=orders[1, h]) if w.reorder else {}
         return dict(kw, clip=w.clip) if w.clip else kw
 
+    n_gen = min(gen_sample, len(inp.steps))
+
+    def gen_of(b, h):
+        return [dict(score=float(st["score_new"][b]), k=st["k_new"][b, h], v=st["v_new"][b, h],
+                     q=st["q"][b, h * g:(h + 1) * g].astype(np.float64)) for st in inp.steps[:n_gen]]
+
     jobs = [(np.ascontiguousarray(inp.k[b, :, h]), np.ascontiguousarray(inp.v[b, :, h]), inv[b],
-             inp.q[b, h * g:(h + 1) * g].astype(np.float64), (w.levels_hi, w.levels_lo, w.group, skvq(h)),
-             scale) for b, h in units]
+             inp.scores[b], inp.q[b, h * g:(h + 1) * g].astype(np.float64),
+             (w.levels_hi, w.levels_lo, w.group, skvq(h)), scale, gen_of(b, h)) for b, h in units]
     t0 = time.perf_counter()
-    with mp.get_context("fork").Pool(workers) as pool:
-        pool.map(_oracle_unit, jobs, chunksize=1)
+    with mp.get_context("fork").Pool(workers, initializer=_one_blas_thread) as pool:
+        res = pool.map(_oracle_unit, jobs, chunksize=1)
     t_units = time.perf_counter() - t0
-    n_all = w.batch * w.kv_heads
-    t_step = t_rank + t_units * n_all / len(units)        # scale the sample to the batch
-    return dict(value=w.batch * w.q_heads * w.tokens / t_step, unit="context tokens/s per head",
-                cores=workers, kind="oracle",
-                sample=f"rank+tiers of all {w.batch} sequences, quantize+pack+fp64 attention of "
-                       f"{len(units)} of {n_all} (sequence, KV head) units, scaled to the batch",
-                seconds=round(t_rank + t_units, 3))
+    t_pre = float(np.mean([r[0] for r in res]))
+    t_gen = float(np.mean([r[1] for r in res]))
+    steps = w.append_steps if w.append_steps else 1
+    cpu_s = n_all * (t_pre + steps * t_gen)          # CPU-seconds of one whole step
+    t_step = t_rank + cpu_s / workers
+    if w.append_steps:
+        ctx = w.batch * w.q_heads * sum(w.tokens + i + 1 for i in range(w.append_steps))
+        sample = (f"rank+tiers of all {w.batch} sequences; for {len(units)} of {n_all} (sequence, KV head) "
+                  f"units: prefix quantize+pack and {n_gen} of {w.append_steps} generation steps "
+                  f"(running-median append, fp64 attention over the cache); per-unit times scaled to "
+                  f"every unit and every step at {workers}-way parallelism")
+    else:
+        ctx = w.batch * w.q_heads * w.tokens
+        sample = (f"rank+tiers of all {w.batch} sequences; quantize+pack+fp64 attention of {len(units)} of "
+                  f"{n_all} (sequence, KV head) units, scaled to the batch at {workers}-way parallelism")
+    return dict(value=ctx / t_step, unit="decode-attention context tokens/s per query head",
+                cores=workers, kind="oracle", sample=sample, host_cpus=os.cpu_count(),
+                cpu_model=cpu_model(), seconds=round(t_rank + t_units, 3),
+                est_step_s=round(t_step, 3))
 
 
 # ------------------------------------------------------------------- main ---
@@ -303,15 +389,35 @@ def sweep_one(w, args, torch, np, kvq, synth, dev):
     return res
 
 
+def gen_step_counts(torch, kvq, lay, cache, quantize, steps, w, stream):
+    """Tier counts of every sequence after each generation step (one untimed
+    pass that reads the counters back after every append; the timed steps
+    replay the same inputs, so they see the same counts)."""
+    import numpy as np
+    quantize()
+    counts = []
+    for st in steps:
+        kvq.append(lay, cache, st["k"], st["v"], st["s"], stream=stream)
+        raw = cache[lay.counters:lay.counters + w.batch * 16].cpu().numpy().tobytes()
+        cnt = np.frombuffer(raw, dtype=np.int32).reshape(w.batch, 4)
+        assert not cnt[:, 3].any(), "append flagged a sequence"
+        counts.append([[int(cnt[b, 1]), int(cnt[b, 2])] for b in range(w.batch)])
+    torch.cuda.synchronize()
+    return counts
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="c2_llama8b_b8_t32k")
-    ap.add_argument("--decode-iters", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="c4_append_b64_t16k")
+    ap.add_argument("--decode-iters", type=int, default=100,
+                    help="workloads without generation steps, and --only decode: decode calls timed")
     ap.add_argument("--replicas", type=int, default=0, help="decode cache replicas (0: auto, >= 1 GB)")
-    ap.add_argument("--cpu-units", type=int, default=16)
+    ap.add_argument("--cpu-units-per-worker", type=int, default=2)
+    ap.add_argument("--cpu-gen-steps", type=int, default=6,
+                    help="generation steps per sampled unit in the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="time quantize / decode (and append) of every workload; one JSON line each")
@@ -329,8 +435,27 @@ def main():
         sys.exit(2)
 
     import numpy as np
+    from mixed_precision_kv_amd import synth
+
+    w = None if args.sweep else synth.BY_NAME[args.config]
+    if w is not None:
+        assert w.mode == "tiered", "the step bench covers the tiered workloads"
+        print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)
+        inp = synth.make_inputs(w, steps=None if args.only == "all" else 0)
+    scale = 1.0 / math.sqrt(128)
+
+    # the oracle baseline runs before anything touches the GPU (its workers are forked)
+    cpu = None
+    if w is not None and args.only == "all" and not args.no_cpu_baseline:
+        workers = cpu_share()
+        print(f"[bench] cpu baseline (oracle) on {workers} of {os.cpu_count()} host CPUs", file=sys.stderr,
+              flush=True)
+        cpu = cpu_baseline(w, inp, float(np.float32(scale)), args.cpu_units_per_worker, args.cpu_gen_steps,
+                           workers)
+        print(f"[bench] cpu baseline done in {cpu['seconds']} s", file=sys.stderr, flush=True)
+
     import torch
-    from mixed_precision_kv_amd import kvq, synth
+    from mixed_precision_kv_amd import kvq
 
     dev = torch.device("cuda:0")
     if args.sweep:
@@ -342,13 +467,9 @@ def main():
                 continue
             print(json.dumps(sweep_one(cw, args, torch, np, kvq, synth, dev)), flush=True)
         return
-    w = synth.BY_NAME[args.config]
-    assert w.mode == "tiered", "the step bench covers the tiered workloads"
-    print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)
-    inp = synth.make_inputs(w, steps=0)
+
     lay = kvq.layout_init(kvq.config_for(w))
     stream = torch.cuda.current_stream()
-
     if args.only == "copy":
         # plain copy of a known size: calibrates the PMC byte counters
         n = 1 << 30
@@ -366,25 +487,26 @@ def main():
     q = torch.from_numpy(inp.q).to(dev)
     out = torch.empty_like(q)
     ranks = torch.empty((w.batch, w.tokens), dtype=torch.int32, device=dev)
+    max_len = w.capacity
     wsq = torch.empty(kvq.workspace_bytes(lay, kvq.OP_QUANTIZE, w.tokens), dtype=torch.uint8, device=dev)
-    wsd = torch.empty(kvq.workspace_bytes(lay, kvq.OP_DECODE, w.tokens), dtype=torch.uint8, device=dev)
-    R = args.replicas or max(1, math.ceil(1.0e9 / lay.total_bytes))
+    wsd = torch.empty(kvq.workspace_bytes(lay, kvq.OP_DECODE, max_len), dtype=torch.uint8, device=dev)
+    gen = bool(w.append_steps) and args.only == "all"
+    R = 1 if w.append_steps else (args.replicas or max(1, math.ceil(1.0e9 / lay.total_bytes)))
     caches = [torch.zeros(lay.total_bytes, dtype=torch.uint8, device=dev) for _ in range(R)]
     if w.reorder:
         for c in caches:
             kvq.set_channel_order(lay, c, synth.channel_orders(w), stream=stream)
-    scale = 1.0 / math.sqrt(w.head_dim)
 
-    def quantize(i):
+    def quantize(i=0):
         kvq.quantize(lay, caches[i % R], k, v, scores, w.tokens, w.n_hi, ranks, wsq, stream=stream)
 
-    def decode(i):
-        kvq.decode_attn(lay, caches[i % R], q, scale, w.tokens, out, wsd, stream=stream)
+    def decode(i=0, qq=None):
+        kvq.decode_attn(lay, caches[i % R], q if qq is None else qq, scale, max_len, out, wsd, stream=stream)
 
     for i in range(R):
         quantize(i)
     torch.cuda.synchronize()
-    print(f"[bench] {R} cache replicas of {lay.total_bytes / 1e6:.1f} MB ready", file=sys.stderr, flush=True)
+    print(f"[bench] {R} cache(s) of {lay.total_bytes / 1e6:.1f} MB ready", file=sys.stderr, flush=True)
 
     if args.only == "decode":
         for i in range(args.decode_iters):
@@ -397,91 +519,126 @@ def main():
         torch.cuda.synchronize()
         return
 
-    # ---- the step: quantize then decode, K timed steps
-    for i in range(args.warmup):
+    steps = []
+    if gen:
+        steps = [dict(k=torch.from_numpy(st["k_new"]).to(dev), v=torch.from_numpy(st["v_new"]).to(dev),
+                      s=torch.from_numpy(st["score_new"]).to(dev), q=torch.from_numpy(st["q"]).to(dev))
+                 for st in inp.steps]
+        counts = gen_step_counts(torch, kvq, lay, caches[0], quantize, steps, w, stream)
+        dec_bytes = [packed_decode_bytes(lay, c) for c in counts]
+        ctx_pairs = [w.batch * w.q_heads * (w.tokens + i + 1) for i in range(len(steps))]
+    else:
+        dec_bytes = [packed_decode_bytes(lay, [[w.n_hi, w.tokens - w.n_hi]] * w.batch)]
+        ctx_pairs = [w.batch * w.q_heads * w.tokens]
+    n_dec = len(dec_bytes)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def one_step(i, rec):
+        """The whole hot path once: prefix quantize, then every generation
+        step (append + decode), or one decode.  rec: event lists or None."""
+        if rec is not None:
+            rec["q"][i][0].record(stream)
         quantize(i)
-        decode(i)
+        if rec is not None:
+            rec["q"][i][1].record(stream)
+        for j in range(n_dec):
+            if gen:
+                st = steps[j]
+                if rec is not None:
+                    rec["a"][i][j][0].record(stream)
+                kvq.append(lay, caches[0], st["k"], st["v"], st["s"], stream=stream)
+                if rec is not None:
+                    rec["a"][i][j][1].record(stream)
+            if rec is not None:
+                rec["d"][i][j][0].record(stream)
+            decode(i, steps[j]["q"] if gen else None)
+            if rec is not None:
+                rec["d"][i][j][1].record(stream)
+
+    for i in range(args.warmup):
+        one_step(i, None)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    K = args.steps
+    rec = {"q": [[ev(), ev()] for _ in range(K)],
+           "a": [[[ev(), ev()] for _ in range(n_dec)] for _ in range(K)],
+           "d": [[[ev(), ev()] for _ in range(n_dec)] for _ in range(K)]}
+    e0, e1 = ev(), ev()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record(stream)
-    for i in range(args.steps):
-        quantize(i)
-        decode(i)
+    for i in range(K):
+        one_step(i, rec)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = e0.elapsed_time(e1) / args.steps
-    print(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (wall {wall:.2f} s)", file=sys.stderr, flush=True)
+    ms_step = e0.elapsed_time(e1) / K
+    print(f"[bench] {K} steps: {ms_step:.3f} ms/step (wall {wall:.2f} s)", file=sys.stderr, flush=True)
 
-    # ---- per-kernel live timing with events around every call on the same stream
-    def timed(fn, iters):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(iters)]
-        for i in range(iters):
-            evs[i][0].record(stream)
-            fn(i)
-            evs[i][1].record(stream)
-        torch.cuda.synchronize()
-        t = np.array([a.elapsed_time(b) for a, b in evs])
-        return float(np.median(t)), float(np.percentile(t, 10)), float(np.percentile(t, 90))
-
-    for i in range(5):
-        decode(i)
-    dec_med, dec_p10, dec_p90 = timed(decode, args.decode_iters)
-    q_med, q_p10, q_p90 = timed(quantize, max(10, args.steps))
-    counts = [[w.n_hi, w.tokens - w.n_hi]] * w.batch
-    dec_bytes = packed_decode_bytes(lay, counts)
+    # live durations of every call in the timed steps (HIP events on `stream`)
+    q_t = np.array([a.elapsed_time(b) for a, b in rec["q"]])
+    d_t = np.array([[a.elapsed_time(b) for a, b in r] for r in rec["d"]])          # [K][n_dec]
+    a_t = np.array([[a.elapsed_time(b) for a, b in r] for r in rec["a"]]) if gen else None
+    dec_total_bytes = float(sum(dec_bytes))
+    dec_mean_ms = float(d_t.mean())
+    dec_gbs = dec_total_bytes / n_dec / (dec_mean_ms * 1e-3) / 1e9   # bytes per launch / mean duration
+    if not gen and R == 1:
+        print("[bench] note: decode reads the cache the same step's quantize wrote", file=sys.stderr)
     q_bytes = quantize_bytes(w, lay)
-    dec_gbs = dec_bytes / (dec_med * 1e-3) / 1e9
+    q_med = float(np.median(q_t))
     q_gbs = q_bytes / (q_med * 1e-3) / 1e9
-    ctx_pairs = w.batch * w.q_heads * w.tokens
-    decode_info = dict(ms=dec_med, ms_p10=dec_p10, ms_p90=dec_p90, bytes=dec_bytes, gbs=round(dec_gbs, 1),
-                       frac_hbm=round(dec_gbs / HBM_PEAK_GBS, 4), replicas=R,
-                       ctx_tokens_per_s_per_qhead=ctx_pairs / (dec_med * 1e-3),
-                       ctx_tokens_per_s_per_kvhead=w.batch * w.kv_heads * w.tokens / (dec_med * 1e-3))
-    quant_info = dict(ms=q_med, ms_p10=q_p10, ms_p90=q_p90, bytes=q_bytes, gbs=round(q_gbs, 1),
-                      frac_hbm=round(q_gbs / HBM_PEAK_GBS, 4))
-    dominant = "decode" if dec_med >= q_med else "quantize"
-    if dominant == "decode":
-        khash = kernel_hash(*DECODE_SOURCES)
-        roof = dict(bound="hbm", achieved=round(dec_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(dec_gbs / HBM_PEAK_GBS, 4),
-                    traffic=measured_traffic("decode", khash), kernel="kvq_decode_attn (decode + merge)")
-    else:
-        khash = kernel_hash(*QUANTIZE_SOURCES)
-        roof = dict(bound="hbm", achieved=round(q_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(q_gbs / HBM_PEAK_GBS, 4),
-                    traffic=measured_traffic("quantize", khash), kernel="kvq_quantize (rank + quantize)")
 
-    # achievable HBM read bandwidth of this device (read-stream probe, 1 GiB)
+    # workloads without generation steps: decode alone over rotating replicas (HBM reads)
+    dec_rot = None
+    if not gen and R > 1:
+        for i in range(3):
+            decode(i)
+        dm, dp10, dp90 = _timed(torch, stream, decode, args.decode_iters)
+        dec_rot = dict(ms=dm, ms_p10=dp10, ms_p90=dp90, replicas=R,
+                       gbs=round(dec_bytes[0] / (dm * 1e-3) / 1e9, 1))
+        dec_gbs = dec_bytes[0] / (dm * 1e-3) / 1e9
+        dec_mean_ms = dm
+
+    decode_info = dict(calls=int(d_t.size), ms_mean=dec_mean_ms, ms_median=float(np.median(d_t)),
+                       ms_p10=float(np.percentile(d_t, 10)), ms_p90=float(np.percentile(d_t, 90)),
+                       bytes_per_call=dec_total_bytes / n_dec, gbs=round(dec_gbs, 1),
+                       frac_hbm=round(dec_gbs / HBM_PEAK_GBS, 4),
+                       ctx_tokens_per_s_per_qhead=sum(ctx_pairs) / (float(d_t.mean(axis=0).sum()) * 1e-3),
+                       ctx_tokens_per_s_per_kvhead=sum(ctx_pairs) / (w.q_heads // w.kv_heads)
+                       / (float(d_t.mean(axis=0).sum()) * 1e-3))
+    if dec_rot:
+        decode_info["rotating_replicas"] = dec_rot
+    quant_info = dict(ms=q_med, ms_p10=float(np.percentile(q_t, 10)), ms_p90=float(np.percentile(q_t, 90)),
+                      bytes=q_bytes, gbs=round(q_gbs, 1), frac_hbm=round(q_gbs / HBM_PEAK_GBS, 4))
+    khash = kernel_hash(*DECODE_SOURCES)
+    roof = dict(bound="hbm", achieved=round(dec_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(dec_gbs / HBM_PEAK_GBS, 4),
+                traffic=measured_traffic("decode", khash, w.name),
+                kernel="kvq_decode_attn (two tier-pool kernels + merge)",
+                bytes_per_launch=round(dec_total_bytes / n_dec), launch_ms=round(dec_mean_ms, 5))
     read_gbs = stream_read_gbs(torch, kvq, dev, stream)
     roof["achievable_read_gbs"] = round(read_gbs, 1)
     roof["frac_of_achievable"] = round(roof["achieved"] / read_gbs, 4)
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        workers = max(1, min(16, os.cpu_count() or 1))
-        print(f"[bench] cpu baseline on {workers} workers", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w, inp, float(np.float32(scale)), args.cpu_units, workers)
-
     res = {
         "metric": "decode-attn over packed KV: context tokens/s per head & HBM GB/s; quantize GB/s",
-        "value": ctx_pairs / (ms_step * 1e-3),
-        "unit": "context tokens/s per query head (quantize + decode step)",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "value": sum(ctx_pairs) / (ms_step * 1e-3),
+        "unit": "decode-attention context tokens/s per query head (whole step: prefix quantize"
+                + (f" + {n_dec} x (append + decode))" if gen else " + decode)"),
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16 operands (MFMA), f32 accumulate",
         "data": "synthetic (seeded N(0,1) K/V with 4 outlier key channels x10, lognormal scores)",
         "config": {"workload": w.name, "batch": w.batch, "kv_heads": w.kv_heads, "q_heads": w.q_heads,
-                   "head_dim": w.head_dim, "context": w.tokens, "levels": [w.levels_hi, w.levels_lo],
-                   "group": w.group, "n_hi": w.n_hi},
+                   "head_dim": w.head_dim, "context": w.tokens, "append_steps": w.append_steps,
+                   "levels": [w.levels_hi, w.levels_lo], "group": w.group, "n_hi": w.n_hi},
         "roofline": roof,
         "cpu_baseline": cpu,
         "decode": decode_info,
         "quantize": quant_info,
     }
+    if gen:
+        res["append"] = dict(calls=int(a_t.size), ms_median=float(np.median(a_t)),
+                             ms_p90=float(np.percentile(a_t, 90)))
     print(json.dumps(res))
 
 
