@@ -250,6 +250,21 @@ kvq_status kvq_decode_attn(const kvq_layout* lay, const void* cache,
                            const void* q, float softmax_scale, int32_t max_len,
                            void* out, void* ws, size_t ws_bytes, void* stream);
 
+/* Decode attention as kvq_decode_attn for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): no workspace argument; the chunk partials live in a fixed
+ * device array of the library (16 MiB per GPU, held until the process ends).
+ * The call allocates and frees nothing.  Same arguments, outputs and kernels
+ * as kvq_decode_attn (results are identical).  Returns KVQ_ERR_WORKSPACE,
+ * launching nothing, when the partials of this call (4 x 132 fp32 per chunk
+ * of every (sequence, KV head); the chunk split depends on the device and on
+ * max_len) exceed 16 MiB.  Calls on one GPU share the array: calls that
+ * overlap on one GPU (different streams or host threads) race and give
+ * undefined results; calls on different GPUs are independent. */
+kvq_status kvq_decode_attn_noalloc(const kvq_layout* lay, const void* cache,
+                                   const void* q, float softmax_scale, int32_t max_len,
+                                   void* out, void* stream);
+
 /* Decode attention as kvq_decode_attn, plus the attention mass of every
  * cached token: the softmax weight it receives, summed over the sequence's
  * query heads (SemKV, Abstract: tokens are ranked by a model-internal score;

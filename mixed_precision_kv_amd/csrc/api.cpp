@@ -229,6 +229,17 @@ extern "C" kvq_status kvq_decode_attn(const kvq_layout* lay, const void* cache, 
   return launch_decode(lay, (const uint8_t*)cache, q, softmax_scale, max_len, out, (uint8_t*)ws, stream);
 }
 
+extern "C" kvq_status kvq_decode_attn_noalloc(const kvq_layout* lay, const void* cache, const void* q,
+                                              float softmax_scale, int32_t max_len, void* out,
+                                              void* stream) {
+  if (!lay || !cache || !q || !out) return KVQ_ERR_ARG;
+  if (!aligned16(cache) || !aligned16(q) || !aligned16(out)) return KVQ_ERR_ARG;
+  if (!(softmax_scale > 0.0f) || softmax_scale > 1e30f) return KVQ_ERR_ARG;
+  if (max_len < 1) return KVQ_ERR_ARG;
+  if (max_len > lay->cfg.capacity) return KVQ_ERR_CAPACITY;
+  return launch_decode_noalloc(lay, (const uint8_t*)cache, q, softmax_scale, max_len, out, stream);
+}
+
 extern "C" size_t kvq_multi_workspace_bytes(const kvq_layout* lay, int32_t n_queries,
                                             int32_t max_len) {
   if (!lay || n_queries < 1 || n_queries > 4096 || max_len < 1 || max_len > lay->cfg.capacity)

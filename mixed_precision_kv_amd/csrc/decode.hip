@@ -13,6 +13,8 @@
 // so keys are never dequantized value by value.
 #include <string.h>
 
+#include <atomic>
+
 #include "common.h"
 #include "internal.h"
 
@@ -395,6 +397,24 @@ __global__ __launch_bounds__(256) void k_token_mass(const int32_t* __restrict__ 
   mass[(size_t)b * max_len + t] = sum;
 }
 
+// Partial bytes a decode of sequences of at most max_len tokens writes with
+// the chunk split launch_decode chooses (decode_ws_bytes bounds every split).
+size_t decode_ws_used(const kvq_layout* L, int max_len) {
+  const kvq_config& c = L->cfg;
+  const size_t U = (size_t)c.batch * c.kv_heads;
+  int nch0, nch1;
+  int nch = decode_chunks(L, max_len, &nch0, &nch1);
+  if (c.mode == KVQ_MODE_TIERED) {
+    const int lv[2] = {c.levels_hi, c.levels_lo};
+    nch = 0;
+    for (int p = 0; p < 2; ++p) {
+      const int slots = L->cap[p] < max_len ? L->cap[p] : max_len;
+      nch += ceil_div(slots, decode_pool_chunk(lv[p], c.group, (int)U, slots));
+    }
+  }
+  return U * nch * kGqa * kPartStride * 4;
+}
+
 size_t decode_ws_bytes(const kvq_layout* L, int max_len, bool mass) {
   int a, b;
   const int n = decode_chunks(L, max_len, &a, &b);
@@ -489,6 +509,42 @@ kvq_status launch_decode(const kvq_layout* L, const uint8_t* cache, const void* 
   }
   launch_merge((const float*)ws, (uint16_t*)out, U, nch, c.kv_heads, s);
   return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
+}
+
+// ---- allocation-free decode ----
+// The partials live in a fixed device array instead of a caller workspace.
+// Host code never passes the array's name to a kernel: it is a host-side
+// stand-in there.  The device address comes from hipGetSymbolAddress, taken
+// once per device with that device current, and is kept per device (each
+// GPU holds its own copy of the array).  Every call on one GPU shares the
+// array; the decode writes every partial it reads, so nothing needs clearing,
+// and calls that overlap on one GPU race on it.
+constexpr int kMaxScratchDevices = 64;
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kNoAllocScratchBytes];
+static std::atomic<uintptr_t> g_scratch_addr[kMaxScratchDevices];
+
+static uint8_t* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  uintptr_t p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    p = (uintptr_t)ptr;
+    g_scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  return (uint8_t*)p;
+}
+
+kvq_status launch_decode_noalloc(const kvq_layout* L, const uint8_t* cache, const void* q, float scale,
+                                 int max_len, void* out, void* stream) {
+  const size_t U = (size_t)L->cfg.batch * L->cfg.kv_heads;
+  // every split needs at least one partial per unit and pool (checked before any HIP call)
+  if (U * 2 * kGqa * kPartStride * 4 > kNoAllocScratchBytes) return KVQ_ERR_WORKSPACE;
+  if (decode_ws_used(L, max_len) > kNoAllocScratchBytes) return KVQ_ERR_WORKSPACE;
+  uint8_t* ws = scratch_ptr();
+  if (!ws) return KVQ_ERR_LAUNCH;
+  return launch_decode(L, cache, q, scale, max_len, out, ws, stream);
 }
 
 }  // namespace kvq

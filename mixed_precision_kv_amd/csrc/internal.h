@@ -54,6 +54,13 @@ kvq_status launch_decode(const kvq_layout* L, const uint8_t* cache, const void* 
 // Workspace of a decode (partials), plus, with the token mass, the pools'
 // raw scores and the per-head (max, sum) after the merge.
 size_t decode_ws_bytes(const kvq_layout* L, int max_len, bool mass);
+// Partial bytes written with the split launch_decode chooses (<= decode_ws_bytes).
+size_t decode_ws_used(const kvq_layout* L, int max_len);
+// Decode with its partials in the library's fixed device array (at most
+// kNoAllocScratchBytes; KVQ_ERR_WORKSPACE beyond it); allocates nothing.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+kvq_status launch_decode_noalloc(const kvq_layout* L, const uint8_t* cache, const void* q, float scale,
+                                 int max_len, void* out, void* stream);
 
 // One tier pool of the matrix-core decode kernel.
 struct PoolArgs {

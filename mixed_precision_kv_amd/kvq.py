@@ -84,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_decode_attn_mass.restype = ctypes.c_int
         L.kvq_set_channel_order.argtypes = [cp(KvqLayout), vp, vp, vp]
         L.kvq_set_channel_order.restype = ctypes.c_int
+        L.kvq_decode_attn_noalloc.argtypes = [cp(KvqLayout), vp, vp, ctypes.c_float, _i32, vp, vp]
+        L.kvq_decode_attn_noalloc.restype = ctypes.c_int
         L.kvq_stream_read.argtypes = [vp, ctypes.c_size_t, vp, _i32, vp]
         L.kvq_stream_read.restype = ctypes.c_int
         _lib = L
@@ -178,6 +180,13 @@ def decode_attn(lay, cache, q, scale, max_len, out, ws, ws_bytes=None, stream=No
     st = lib().kvq_decode_attn(ctypes.byref(lay), _ptr(cache), _ptr(q), float(scale), max_len,
                                _ptr(out), _ptr(ws), ws_bytes, _stream(stream))
     _check(st, "kvq_decode_attn")
+
+
+def decode_attn_noalloc(lay, cache, q, scale, max_len, out, stream=None):
+    """kvq_decode_attn with the library's fixed device array as workspace."""
+    st = lib().kvq_decode_attn_noalloc(ctypes.byref(lay), _ptr(cache), _ptr(q), float(scale), max_len,
+                                       _ptr(out), _stream(stream))
+    _check(st, "kvq_decode_attn_noalloc")
 
 
 def multi_workspace_bytes(lay: KvqLayout, n_queries: int, max_len: int) -> int:

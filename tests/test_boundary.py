@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol():
     assert {"kvq_layout_init", "kvq_workspace_bytes", "kvq_status_str", "kvq_quantize",
             "kvq_append", "kvq_decode_attn", "kvq_multi_workspace_bytes",
             "kvq_decode_attn_multi", "kvq_stream_read", "kvq_decode_attn_mass",
-            "kvq_set_channel_order"} <= set(names)
+            "kvq_set_channel_order", "kvq_decode_attn_noalloc"} <= set(names)
     L = kvq.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -276,3 +276,20 @@ def test_set_channel_order_validation():
     assert e.value.status == 1
     with pytest.raises(ValueError):                        # too few entries for the layout
         kvq.set_channel_order(lay, FAKE, ident[:1], stream=0)
+
+
+def test_noalloc_decode_validation():
+    """The allocation-free decode rejects bad arguments, and partials beyond
+    its fixed 16 MiB array (512 x 8 units need at least 17.3 MB), on the
+    host before any launch."""
+    lay = kvq.layout_init(_cfg())
+    for args, status in (((0, FAKE, 0.088, 64, FAKE), 1), ((FAKE, FAKE + 2, 0.088, 64, FAKE), 1),
+                         ((FAKE, FAKE, 0.0, 64, FAKE), 1), ((FAKE, FAKE, 0.088, 0, FAKE), 1),
+                         ((FAKE, FAKE, 0.088, lay.cfg.capacity + 1, FAKE), 3)):
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.decode_attn_noalloc(lay, args[0], args[1], args[2], args[3], args[4], stream=0)
+        assert e.value.status == status
+    big = kvq.layout_init(kvq.config_for(synth.W_LLAMA.shrink(name="huge", batch=512, tokens=64)))
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.decode_attn_noalloc(big, FAKE, FAKE, 0.088, 64, FAKE, stream=0)
+    assert e.value.status == 4
