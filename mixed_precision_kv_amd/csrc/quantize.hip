@@ -900,58 +900,74 @@ __device__ inline uint32_t quant_group_skvq(const uint16_t* __restrict__ row, co
   return gq.s_bits | (mn << 16);
 }
 
-constexpr int kAppendBatch = 16;              // sorted-score elements per thread per round trip
+constexpr int kAppendThreads = 1024;
+constexpr int kAppendPerThread = 20;                  // sorted scores per thread per pass
+constexpr int kAppendPass = kAppendThreads * kAppendPerThread;
 
+// One workgroup per sequence.  The sorted scores are moved in passes of
+// kAppendPass elements from the top down: a pass is read whole into registers
+// before any of it is written, so a score greater than the new one can move up
+// by one place in the same pass (a lower pass's writes end where this pass
+// begins, after this pass has read it).  The scores at most equal to the new
+// one stay; their count is the new score's position.
 template <int G>
-__global__ __launch_bounds__(256) void k_append(AppendArgs a) {
+__global__ __launch_bounds__(kAppendThreads) void k_append(AppendArgs a) {
   constexpr int NG = kD / G;
-  __shared__ int s_tier, s_len, s_slot, s_ok;
+  __shared__ int s_tier, s_slot, s_ok;
   __shared__ uint32_t s_le;
   __shared__ uint8_t codes[2][64][kD];     // [k/v][head][d], Hkv <= 64
   const int tid = threadIdx.x, b = blockIdx.x;
   int32_t* cnt = a.counters + b * 4;
   float* srt = a.sorted + (size_t)b * a.capacity;
   const float snew = a.score_new[b];
+  const int len = cnt[0];
+  float x[kAppendPerThread];
+  auto load_pass = [&](int hi) {             // elements hi - 1 - tid - kAppendThreads k
+#pragma unroll
+    for (int k = 0; k < kAppendPerThread; ++k) {
+      const int i = hi - 1 - tid - kAppendThreads * k;
+      x[k] = i >= 0 ? srt[i] : 0.0f;
+    }
+  };
   if (tid == 0) {
-    const int len = cnt[0];
-    int tier = 1;
+    int tier = 0;                            // an empty sequence takes the hi grid
     if (len > 0) {
       const double m = ((double)srt[(len - 1) / 2] + (double)srt[len / 2]) * 0.5;
       tier = ((double)snew > m) ? 0 : 1;
-    } else {
-      tier = 0;
     }
     const int slot = cnt[1 + tier];
     s_tier = tier;
-    s_len = len;
     s_slot = slot;
     s_ok = (len < a.capacity && slot < a.cap[tier]) ? 1 : 0;
     s_le = 0;
   }
+  load_pass(len);                            // the top pass, read while the tier is decided
   __syncthreads();
   if (!s_ok) {
     if (tid == 0) atomicOr(cnt + 3, kFlagPoolFull);
     return;
   }
-  const int tier = s_tier, len = s_len, slot = s_slot;
+  const int tier = s_tier, slot = s_slot;
   const int L = a.L[tier], nv = a.nv[tier], kw = a.kw[tier], tiles = a.tiles[tier],
             vrows = a.vrows[tier];
-  // position of the new score: number of present scores <= snew (sixteen
-  // loads per thread in flight per round trip)
   uint32_t le = 0;
-  for (int i0 = 0; i0 < len; i0 += 256 * kAppendBatch) {
-    float x[kAppendBatch];
-#pragma unroll
-    for (int k = 0; k < kAppendBatch; ++k) {
-      const int i = i0 + 256 * k + tid;
-      x[k] = i < len ? srt[i] : 0.0f;
+  for (int hi = len; hi > 0; hi -= kAppendPass) {
+    if (hi != len) {
+      load_pass(hi);
+      __syncthreads();                       // the pass is read whole before it is written
     }
 #pragma unroll
-    for (int k = 0; k < kAppendBatch; ++k) le += (i0 + 256 * k + tid < len && x[k] <= snew) ? 1u : 0u;
+    for (int k = 0; k < kAppendPerThread; ++k) {
+      const int i = hi - 1 - tid - kAppendThreads * k;
+      if (i >= 0) {
+        if (x[k] <= snew) ++le;
+        else srt[i + 1] = x[k];
+      }
+    }
   }
   atomicAdd(&s_le, le);
   // quantize every (head, k/v, group)
-  for (int task = tid; task < a.Hkv * 2 * NG; task += 256) {
+  for (int task = tid; task < a.Hkv * 2 * NG; task += kAppendThreads) {
     const int h = task / (2 * NG), kv = (task / NG) % 2, g = task % NG;
     const uint16_t* row = (kv ? a.v_new : a.k_new) + ((size_t)b * a.Hkv + h) * kD;
     uint32_t meta;
@@ -969,7 +985,7 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
   }
   __syncthreads();
   const uint32_t pos = s_le;
-  for (int task = tid; task < a.Hkv * kw; task += 256) {
+  for (int task = tid; task < a.Hkv * kw; task += kAppendThreads) {
     const int h = task / kw, w = task % kw;
     const int u = b * a.Hkv + h;
     const int d0 = w * nv, d1 = min(kD, d0 + nv);
@@ -980,30 +996,13 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
   const int r = slot / nv, j = slot % nv;
   uint32_t pw = 1;
   for (int i = 0; i < j; ++i) pw *= (uint32_t)L;
-  for (int task = tid; task < a.Hkv * kD; task += 256) {
+  for (int task = tid; task < a.Hkv * kD; task += kAppendThreads) {
     const int h = task / kD, d = task % kD;
     const int u = b * a.Hkv + h;
     uint32_t* wp = &a.vwords[tier][((size_t)u * vrows + r) * kD + d];
     *wp = *wp + pw * (uint32_t)codes[1][h][d];
   }
-  // insert the score: shift srt[pos..len) up by one, highest chunk first;
-  // a chunk is read whole before any of it is written
-  for (int hi = len; hi > (int)pos; hi -= 256 * kAppendBatch) {
-    float val[kAppendBatch];
-#pragma unroll
-    for (int k = 0; k < kAppendBatch; ++k) {
-      const int i = hi - 1 - tid - 256 * k;
-      val[k] = i >= (int)pos ? srt[i] : 0.0f;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < kAppendBatch; ++k) {
-      const int i = hi - 1 - tid - 256 * k;
-      if (i >= (int)pos) srt[i + 1] = val[k];
-    }
-    __syncthreads();
-  }
-  if (tid == 0) {
+  if (tid == 0) {                            // after every move (the barrier above)
     srt[pos] = snew;
     a.tokmap[(size_t)b * a.capacity + len] = (uint32_t)slot | ((uint32_t)tier << 31);
     cnt[0] = len + 1;
@@ -1041,9 +1040,9 @@ bool launch_append(const kvq_layout* L, uint8_t* cache, const void* k_new, const
   a.clip = c.clip > 0.0f ? c.clip : 1.0f;
   a.skvq = (c.reorder || a.clip != 1.0f) ? 1 : 0;
   switch (c.group) {
-    case 32: k_append<32><<<c.batch, 256, 0, s>>>(a); break;
-    case 64: k_append<64><<<c.batch, 256, 0, s>>>(a); break;
-    case 128: k_append<128><<<c.batch, 256, 0, s>>>(a); break;
+    case 32: k_append<32><<<c.batch, kAppendThreads, 0, s>>>(a); break;
+    case 64: k_append<64><<<c.batch, kAppendThreads, 0, s>>>(a); break;
+    case 128: k_append<128><<<c.batch, kAppendThreads, 0, s>>>(a); break;
     default: return false;
   }
   return hipGetLastError() == hipSuccess;
