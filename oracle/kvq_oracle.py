@@ -48,6 +48,10 @@ supports; all are listed in the design notes):
   values per token in groups of v_group.  k^ = deq(dense) + sparse.
 * Attention: o = softmax(scale * q . k^) v^ in fp64 over every cached token,
   query head hq reads KV head hq // (Hq / Hkv).
+* [KVQuant] "techniques", pre-RoPE keys (tiered mode, optional): keys are
+  stored as given (before the rotary embedding) and rotated at attention time
+  by their token positions (adjacent channel pairs, theta_i = base^(-2i/D));
+  the query is given already rotated.
 * [SKVQ] Abstract, channel rearrangement and clipped group ranges (tiered
   mode, optional): a fixed channel order per KV head for keys and for values
   (stored position p holds channel order[p]; groups are runs of G positions);
@@ -348,6 +352,33 @@ def token_attention_mass(q_seq: np.ndarray, k_hat_heads, scale: float) -> np.nda
         p = np.exp(s - s.max())
         mass += p / p.sum()
     return mass
+
+
+# -------------------------------------------------- pre-RoPE keys (KVQuant) ---
+def rope_thetas(D: int, base: float) -> np.ndarray:
+    """Rotary frequencies of the D/2 channel pairs, fp64: theta_i =
+    base ** (-2 i / D).  [KVQuant] summary, "techniques" (Pre-RoPE Key
+    Quantization: keys are quantized before the rotary position embedding,
+    which mixes channels).  The pages give no formula; this is the standard
+    rotary embedding (pairs of adjacent channels (2i, 2i + 1), each turned by
+    the angle position * theta_i)."""
+    i = np.arange(D // 2, dtype=F64)
+    return np.power(F64(base), -2.0 * i / F64(D))
+
+
+def rope_rotate(x: np.ndarray, positions, base: float) -> np.ndarray:
+    """Rows x [N][D] (fp64) turned by their positions [N]: pair i of row t,
+    (x[2i], x[2i+1]), becomes (x cos a - y sin a, x sin a + y cos a) with
+    a = positions[t] * theta_i.  Position 0 is the identity."""
+    x = np.asarray(x, dtype=F64)
+    N, D = x.shape
+    ang = np.asarray(positions, dtype=F64)[:, None] * rope_thetas(D, base)[None, :]   # [N][D/2]
+    c, s = np.cos(ang), np.sin(ang)
+    xe, xo = x[:, 0::2], x[:, 1::2]
+    out = np.empty_like(x)
+    out[:, 0::2] = xe * c - xo * s
+    out[:, 1::2] = xe * s + xo * c
+    return out
 
 
 def row_rel_err(o: np.ndarray, r: np.ndarray) -> float:

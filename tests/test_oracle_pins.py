@@ -451,6 +451,50 @@ def test_kchan_unit_value_half(kl, vl, vg, n_vl):
     assert np.array_equal(u.v_hat()[nq:], v[nq:].astype(np.float64))
 
 
+# ------------------------------------------------------- pre-RoPE keys ---
+# KVQuant summary, "techniques" (Pre-RoPE Key Quantization).  The pins fix
+# the rotation by what any rotary embedding must satisfy plus quarter turns
+# whose images are exact, without restating the formula.
+
+def test_rope_position_zero_is_identity_and_norms_are_kept():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((50, 128))
+    assert np.array_equal(O.rope_rotate(x, np.zeros(50), 10000.0), x)
+    y = O.rope_rotate(x, rng.integers(0, 131072, 50), 500000.0)
+    pairs = lambda z: np.hypot(z[:, 0::2], z[:, 1::2])           # noqa: E731
+    assert np.allclose(pairs(y), pairs(x), rtol=1e-13, atol=0)
+    assert not np.allclose(y, x)
+
+
+def test_rope_quarter_turns_fix_direction_pairing_and_frequencies():
+    """Pair 0 turns at rate 1, pair i at base^(-2i/D): (1, 0) in pair 0 at
+    position pi/2, and in pair 1 (D = 4, base 10^4: rate 10^-2) at 50 pi,
+    becomes (0, 1) -- counterclockwise, within its own adjacent pair; a
+    half turn maps it to (-1, 0)."""
+    e0 = np.array([[1.0, 0.0, 0.0, 0.0]])
+    e2 = np.array([[0.0, 0.0, 1.0, 0.0]])
+    assert np.allclose(O.rope_rotate(e0, [math.pi / 2], 1e4), [[0, 1, 0, 0]], atol=1e-15)
+    assert np.allclose(O.rope_rotate(e2, [50 * math.pi], 1e4), [[0, 0, 0, 1]], atol=1e-13)
+    assert np.allclose(O.rope_rotate(e2, [100 * math.pi], 1e4), [[0, 0, -1, 0]], atol=1e-13)
+    # pair 0 is untouched by pair 1's quarter turn position and vice versa
+    assert np.allclose(O.rope_rotate(e0, [2 * math.pi], 1e4), e0, atol=1e-14)
+    th = O.rope_thetas(128, 500000.0)
+    assert th[0] == 1.0 and abs(th[-1] - 500000.0 ** (-126 / 128)) < 1e-20 and np.all(np.diff(th) < 0)
+
+
+def test_rope_composes_and_scores_depend_on_relative_position():
+    rng = np.random.default_rng(12)
+    q, k = rng.standard_normal((2, 30, 128))
+    a, b = rng.integers(0, 40000, 30), rng.integers(0, 40000, 30)
+    ab = O.rope_rotate(O.rope_rotate(k, a, 1e4), b, 1e4)
+    assert np.allclose(ab, O.rope_rotate(k, a + b, 1e4), rtol=0, atol=1e-10)
+    m, n, sh = rng.integers(0, 60000, 30), rng.integers(0, 60000, 30), rng.integers(0, 60000, 30)
+    s1 = np.einsum("td,td->t", O.rope_rotate(q, m, 5e5), O.rope_rotate(k, n, 5e5))
+    s2 = np.einsum("td,td->t", O.rope_rotate(q, m + sh, 5e5), O.rope_rotate(k, n + sh, 5e5))
+    s3 = np.einsum("td,td->t", q, O.rope_rotate(k, n - m, 5e5))
+    assert np.allclose(s1, s2, rtol=0, atol=1e-9) and np.allclose(s1, s3, rtol=0, atol=1e-9)
+
+
 # --------------------------------------------------------------- storage ---
 def test_storage_ratio_closed_forms():
     """Layout bytes per (sequence, KV head), worked by hand for the 32768-token
