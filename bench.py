@@ -331,7 +331,7 @@ def sweep_one(w, args, torch, np, kvq, synth, dev):
         dm_ms = _timed(torch, stream, decode_mass, 30)
         res["decode_mass"] = {"ms": dm_ms[0], "ms_p10": dm_ms[1], "ms_p90": dm_ms[2],
                               "overhead_vs_decode": round(dm_ms[0] / d_ms[0] - 1.0, 4)}
-    if tiered and args.multi_queries > 0:
+    if tiered and args.multi_queries > 0 and not w.rope_theta:
         # a block of M new query tokens per sequence over the same caches
         M = args.multi_queries
         qm = torch.from_numpy(synth.make_queries(w, M)).to(dev)
@@ -462,7 +462,7 @@ def main():
         rg = stream_read_gbs(torch, kvq, dev, torch.cuda.current_stream())
         print(json.dumps({"probe": "stream_read", "bytes": 1 << 30, "gbs": round(rg, 1),
                           "frac_hbm": round(rg / HBM_PEAK_GBS, 4)}), flush=True)
-        for cw in synth.CONFIGS + [synth.W_SKVQ]:
+        for cw in synth.CONFIGS + [synth.W_SKVQ, synth.W_ROPE, synth.W_ROPE_LONG]:
             if args.sweep_only and cw.name not in args.sweep_only.split(","):
                 continue
             print(json.dumps(sweep_one(cw, args, torch, np, kvq, synth, dev)), flush=True)

@@ -125,6 +125,14 @@ typedef struct kvq_config {
    * quantization group holds alike channels; clipped group ranges) */
   int32_t reorder;        /* 1: stored channel orders (kvq_set_channel_order); 0: none */
   float clip;             /* 0: none; else in (0, 1]: group min and max scaled by clip */
+  /* tiered mode, optional (KVQuant summary, "techniques": pre-RoPE key
+   * quantization): keys are stored as given, before the rotary embedding,
+   * and kvq_decode_attn / kvq_decode_attn_mass turn each dequantized key by
+   * its token position: channel pair (2i, 2i + 1) by the angle
+   * position * rope_theta^(-2i/128).  The query is passed already rotated.
+   * A token's position is its index in the sequence (appended tokens
+   * continue it).  Not with reorder = 1. */
+  float rope_theta;       /* 0: none; else > 1: the rotary base (10000, 500000, ...) */
 } kvq_config;
 
 /* Filled by kvq_layout_init.  All offsets are bytes from the cache base;
@@ -144,6 +152,8 @@ typedef struct kvq_config {
  *       k_meta[p] / v_meta[p] + (((u * tiles[p] + s/16) * (D/group) + g) * 16 + s%16)
  *   value words (uint32), slot s at digit s % nv[p] of row r = s / nv[p]:
  *       v_words[p] + ((u * vrows[p] + r) * D + d)
+ *   with rope_theta > 0, slot positions int32 of slot s of pool p of sequence b:
+ *       slot_pos[p] + (b * cap[p] + s) = the token index the slot holds
  *   with reorder = 1, channel orders uint8 [2][kv_heads][D] (keys, values):
  *       chan_order + (kv * kv_heads + h) * D + p = the channel whose code,
  *       like every index d above, sits at position p (groups are runs of
@@ -174,6 +184,7 @@ typedef struct kvq_layout {
   int64_t k_words[2], k_meta[2], v_words[2], v_meta[2];
   int64_t sparse, k_win, v_win;
   int64_t chan_order;     /* tiered with reorder = 1; else 0 */
+  int64_t slot_pos[2];    /* tiered with rope_theta > 0: int32 [B][cap[p]] token position of each slot; else 0 */
   int64_t total_bytes;
 } kvq_layout;
 
@@ -297,7 +308,8 @@ size_t kvq_multi_workspace_bytes(const kvq_layout* lay, int32_t n_queries, int32
  *   lse:       device fp32 [B][n_queries][Hq] or NULL: ln sum_t exp(scale q.k^_t)
  *              of each row, for merging with attention over the new tokens.
  *   ws:        device workspace >= kvq_multi_workspace_bytes(lay, n_queries, max_len).
- * Returns KVQ_ERR_UNSUPPORTED for the per-channel-key mode. */
+ * Returns KVQ_ERR_UNSUPPORTED for the per-channel-key mode and for caches
+ * laid out with rope_theta > 0. */
 kvq_status kvq_decode_attn_multi(const kvq_layout* lay, const void* cache,
                                  const void* q, int32_t n_queries, float softmax_scale,
                                  int32_t max_len, void* out, float* lse,

@@ -81,6 +81,8 @@ extern "C" kvq_status kvq_layout_init(const kvq_config* cfg, kvq_layout* out) {
       return KVQ_ERR_UNSUPPORTED;
     if (c.reorder != 0 && c.reorder != 1) return KVQ_ERR_ARG;
     if (!(c.clip == 0.0f || (c.clip > 0.0f && c.clip <= 1.0f))) return KVQ_ERR_ARG;
+    if (!(c.rope_theta == 0.0f || (c.rope_theta > 1.0f && c.rope_theta < 1e30f))) return KVQ_ERR_ARG;
+    if (c.rope_theta != 0.0f && c.reorder) return KVQ_ERR_UNSUPPORTED;   // pairs are original channels
     if (c.cap_hi < 0 || c.cap_lo < 0) return KVQ_ERR_ARG;
     L.cap[0] = c.cap_hi ? c.cap_hi : c.capacity;
     L.cap[1] = c.cap_lo ? c.cap_lo : c.capacity;
@@ -102,8 +104,10 @@ extern "C" kvq_status kvq_layout_init(const kvq_config* cfg, kvq_layout* out) {
       L.v_meta[p] = off;  off = align256(off + U * L.tiles[p] * ng * kTile * 4);
     }
     if (c.reorder) { L.chan_order = off; off = align256(off + 2 * (int64_t)c.kv_heads * D); }
+    if (c.rope_theta != 0.0f)
+      for (int p = 0; p < 2; ++p) { L.slot_pos[p] = off; off = align256(off + B * (int64_t)L.cap[p] * 4); }
   } else if (c.mode == KVQ_MODE_KCHAN) {
-    if (c.reorder != 0 || c.clip != 0.0f) return KVQ_ERR_UNSUPPORTED;
+    if (c.reorder != 0 || c.clip != 0.0f || c.rope_theta != 0.0f) return KVQ_ERR_UNSUPPORTED;
     if (!levels_ok(c.k_levels) || !levels_ok(c.v_levels) || !group_ok(c.v_group))
       return KVQ_ERR_UNSUPPORTED;
     if (c.k_block != 128 || c.window < 0 || c.sparse_per_vec < 0 || c.sparse_per_vec > 8)
@@ -259,7 +263,7 @@ extern "C" kvq_status kvq_decode_attn_multi(const kvq_layout* lay, const void* c
   if (!(softmax_scale > 0.0f) || softmax_scale > 1e30f) return KVQ_ERR_ARG;
   if (max_len < 1) return KVQ_ERR_ARG;
   if (max_len > lay->cfg.capacity) return KVQ_ERR_CAPACITY;
-  if (lay->cfg.mode != KVQ_MODE_TIERED) return KVQ_ERR_UNSUPPORTED;
+  if (lay->cfg.mode != KVQ_MODE_TIERED || lay->cfg.rope_theta != 0.0f) return KVQ_ERR_UNSUPPORTED;
   size_t need = kvq_multi_workspace_bytes(lay, n_queries, max_len);
   if (!ws || !aligned16(ws) || ws_bytes < need) return KVQ_ERR_WORKSPACE;
   return launch_decode_mq(lay, (const uint8_t*)cache, q, n_queries, softmax_scale, max_len, out, lse,

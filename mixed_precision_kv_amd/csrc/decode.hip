@@ -477,6 +477,8 @@ kvq_status launch_decode(const kvq_layout* L, const uint8_t* cache, const void* 
       pa.raw = mass ? raw[p] : nullptr;
       pa.cap_p = L->cap[p];
       pa.korder = korder;
+      pa.spos = L->slot_pos[p] ? (const int32_t*)(cache + L->slot_pos[p]) : nullptr;
+      pa.rope_theta = c.rope_theta;
       if (nchp[p] > 0 && !launch_decode_pool(lv[p], pa, c.group, nchp[p], U, stream)) return KVQ_ERR_LAUNCH;
     }
     launch_merge((const float*)ws, (uint16_t*)out, U, nch_used, c.kv_heads, s, mass ? stats : nullptr,

@@ -37,7 +37,15 @@ namespace kvq {
 //   wave 1 (values) macro tile i-1: A = p * s from that buffer, column-word
 //                   digits, matrix ops into the accumulators.
 // One barrier per macro tile hands buffer (i & 1) from wave 0 to wave 1.
-template <int L, int G>
+// ROPE (pre-RoPE keys, KVQuant summary "techniques"): the key wave turns
+// every dequantized key by its token position before the dot product.  Per
+// key tile the lane's expanded digits go to LDS in channel order; lane (n, j)
+// then takes channels 32 j .. 32 j + 31 of slot n (16 adjacent pairs),
+// dequantizes them in fp32, turns pair i by position * theta_i (the angle in
+// revolutions reduced in fp64, then the hardware sine and cosine), and hands
+// the rotated key to the matrix cores as fp16 high and low parts against A
+// rows 4h .. 4h + 3 = query head h, so lane (n, j) receives head j's score.
+template <int L, int G, bool ROPE>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k_decode_pool(PoolArgs a) {
   using T = Tiling<L>;
   constexpr int NV = T::NV, KW = T::KW, KWL = T::KWL, R = T::R, RUN = T::RUN, MT = T::MT,
@@ -62,6 +70,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
   __shared__ int mpos_lds[64 * META_PER_LANE];
   __shared__ float zred[16];
   __shared__ uint2 ctab[DK::kTableEntries];   // chunk -> four fp16 digits
+  __shared__ double rev_lds[ROPE ? kD / 2 : 1];   // theta_i / 2 pi: revolutions per position
+  __shared__ __attribute__((aligned(16))) _Float16 kc_lds[ROPE ? 16 : 1][ROPE ? kD + 8 : 1];  // a key tile, channel order
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, j = lane >> 4;    // B/C-operand view: slot/channel n, group j
@@ -94,6 +104,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
     mpos_lds[e] = jj * VK + DV::pos_of(rem / NV, rem % NV);
   }
   DK::fill(ctab, threadIdx.x, 128);
+  if (ROPE && threadIdx.x < kD / 2)
+    rev_lds[threadIdx.x] = exp2(-(double)(2 * threadIdx.x) / kD * log2((double)a.rope_theta)) *
+                           0.15915494309189533577;   // / (2 pi)
   // operand positions that hold no slot keep weight and scale 0
   for (int i = threadIdx.x; i < 4 * VK; i += 128) {
     for (int h = 0; h < 4; ++h) { pw_lds[0][h][i] = (_Float16)0.0f; pw_lds[1][h][i] = (_Float16)0.0f; }
@@ -112,9 +125,11 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
       kwoff[wi] = w < KW ? (uint32_t)(w * 16 + n) * 4u : kOutOfRange;
     }
     const uint32_t kmoff = (uint32_t)((j / SUB) * 16 + n) * 4u;
+    const BufRes rSP = make_res(ROPE ? a.spos + (size_t)b * a.cap_p : a.counters, ROPE ? a.cap_p * 4 : 4);
     struct KBuf {
       uint32_t kw[KT][KWL];
       uint32_t km[KT];
+      uint32_t pos[ROPE ? KT : 1];             // token positions of the tile's slots
     };
     auto load_k = [&](KBuf& kb, int s0) {
       const uint32_t tile0 = s0 / 16;
@@ -123,6 +138,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
         for (int wi = 0; wi < KWL; ++wi) kb.kw[t][wi] = bload(rK, kwoff[wi] + (tile0 + t) * (KW * 16 * 4));
         kb.km[t] = bload(rKM, kmoff + (tile0 + t) * (NG * 16 * 4));
+        if (ROPE) kb.pos[t] = bload(rSP, ((tile0 + t) * 16 + n) * 4u);
       }
     };
     KBuf nxt;
@@ -151,9 +167,57 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
           aq[m][i] = (_Float16)(ok ? qv : 0.0f);   // q is fp16: exact
         }
     }
+    h8 aqr[ROPE ? 4 : 1];                    // rotated keys: A[r][k] = q_{r/4}[32 (k/8) + 8 m + k%8]
+    if (ROPE) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) aqr[m][e] = (_Float16)qf[n >> 2][32 * j + 8 * m + e];
+    }
     int spos[KT];                            // operand position of slot 16 t + n
 #pragma unroll
     for (int t = 0; t < KT; ++t) spos[t] = ppos_lds[16 * t + n];
+    // score of head j for slot n with the key turned by its position: the
+    // expanded operand values v (digits, or 1 + d/MUL on power-of-two grids)
+    // give the key sg v + zz
+    auto rope_score = [&](const h8 (&bk)[KM], float sg, float zz, uint32_t pos) -> float {
+      wave_lds_fence();                      // the previous tile's gather is done
+#pragma unroll
+      for (int m = 0; m < KM; ++m)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int tt = 8 * m + i, wi = DK::word_of(tt);
+          if (wi >= 0) {
+            const int w = j + 4 * wi, d = w * NV + DK::digit_of(tt);
+            if (w < KW && d < kD) kc_lds[n][d] = bk[m][i];
+          }
+        }
+      wave_lds_fence();
+      const double pd = (double)pos;
+      f4 pr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const h8 cv = *reinterpret_cast<const h8*>(&kc_lds[n][32 * j + 8 * m]);
+        h8 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float x = __builtin_fmaf(sg, (float)cv[e], zz);
+          const float y = __builtin_fmaf(sg, (float)cv[e + 1], zz);
+          double r = pd * rev_lds[16 * j + 4 * m + e / 2];
+          r -= floor(r);                     // revolutions in [0, 1)
+          const float rv = (float)r;
+          const float cs = __builtin_amdgcn_cosf(rv), sn = __builtin_amdgcn_sinf(rv);
+          const float xr = x * cs - y * sn, yr = x * sn + y * cs;
+          hi[e] = (_Float16)xr;
+          hi[e + 1] = (_Float16)yr;
+          lo[e] = (_Float16)(xr - (float)hi[e]);
+          lo[e + 1] = (_Float16)(yr - (float)hi[e + 1]);
+        }
+        pr = __builtin_amdgcn_mfma_f32_16x16x32_f16(aqr[m], hi, pr, 0, 0, 0);
+        pr = __builtin_amdgcn_mfma_f32_16x16x32_f16(aqr[m], lo, pr, 0, 0, 0);
+      }
+      return pr[0];
+    };
     float m_run = -INFINITY, l_run = 0.f;
     for (int it = 0; it <= nmt; ++it) {
       if (it < nmt) {
@@ -166,16 +230,22 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
         for (int t = 0; t < KT; ++t) {
           h8 bk[KM];
           DK::run(cur.kw[t], ctab, bk);
-          f4 pr = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int m = 0; m < KM; ++m) pr = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[m], bk[m], pr, 0, 0, 0);
           const uint32_t meta = cur.km[t];
           const float sg = h2f(meta & 0xFFFFu) * MUL;
-          const float ssc = sg * a.c, zz = AFF ? h2f(meta >> 16) - sg : h2f(meta >> 16);
-          f4 x;
+          const float zz = AFF ? h2f(meta >> 16) - sg : h2f(meta >> 16);
+          float sc;
+          if constexpr (ROPE) {
+            sc = rope_score(bk, sg, zz, cur.pos[t]) * a.c;
+          } else {
+            f4 pr = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int h = 0; h < 4; ++h) x[h] = __builtin_fmaf(ssc, pr[h], zz * qc[h]);
-          float sc = reduce_scatter4(x);
+            for (int m = 0; m < KM; ++m) pr = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[m], bk[m], pr, 0, 0, 0);
+            const float ssc = sg * a.c;
+            f4 x;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) x[h] = __builtin_fmaf(ssc, pr[h], zz * qc[h]);
+            sc = reduce_scatter4(x);
+          }
           scs[t] = (s0 + 16 * t + n < s_end) ? sc : -INFINITY;
           if (a.raw && s0 + 16 * t + n < s_end)     // lane (n, j): head j of slot n
             a.raw[((size_t)u * kGqa + j) * a.cap_p + s0 + 16 * t + n] = sc;
@@ -335,13 +405,16 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
 
 template <int L, int G>
 static void launch_one(const PoolArgs& a, int nch, int U, hipStream_t s) {
-  k_decode_pool<L, G><<<dim3(nch, U), 128, 0, s>>>(a);
+  if (a.spos)
+    k_decode_pool<L, G, true><<<dim3(nch, U), 128, 0, s>>>(a);
+  else
+    k_decode_pool<L, G, false><<<dim3(nch, U), 128, 0, s>>>(a);
 }
 
 template <int L, int G>
 static int occupancy_one() {
   int blocks = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_decode_pool<L, G>, 128, 0) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_decode_pool<L, G, false>, 128, 0) != hipSuccess)
     return 0;
   return blocks;
 }

@@ -77,6 +77,8 @@ struct PoolArgs {
   float* raw;         // or null: log2-domain scores out, [unit][head][cap_p]
   int cap_p;          // slots of this pool
   const uint8_t* korder = nullptr;   // [Hkv][128] stored key channel order: q is read through it
+  const int32_t* spos = nullptr;     // pre-RoPE keys: [B][cap_p] token position of each slot
+  float rope_theta = 0.0f;           // rotary base (with spos)
 };
 // Slots per workgroup for one pool so that the grid fills the chip about once
 // (uses the kernel's occupancy; falls back to 8 macro tiles).

@@ -61,6 +61,14 @@ __device__ inline float reduce_scatter4(f4 x) {
   return __uint_as_float(s01[0]) + __uint_as_float(s01[1]);
 }
 
+// Orders one wave's LDS accesses: its stores land before the loads that
+// follow (the wave's own LDS operations complete in issue order).
+__device__ inline void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 typedef __amdgpu_buffer_rsrc_t BufRes;
 constexpr uint32_t kOutOfRange = 0x80000000u;   // beyond every region: reads 0
 

@@ -874,6 +874,7 @@ struct AppendArgs {
   const uint8_t* vorder = nullptr;
   float clip = 1.0f;                 // group min/max scale factor (1: none)
   int skvq = 0;                      // orders or clipping in use
+  int32_t* spos[2] = {nullptr, nullptr};   // pre-RoPE keys: token position of each slot
 };
 
 // One group of a new token's row with a stored channel order (ord: the
@@ -1003,6 +1004,7 @@ __global__ __launch_bounds__(kAppendThreads) void k_append(AppendArgs a) {
     *wp = *wp + pw * (uint32_t)codes[1][h][d];
   }
   if (tid == 0) {                            // after every move (the barrier above)
+    if (a.spos[tier]) a.spos[tier][(size_t)b * a.cap[tier] + slot] = len;
     srt[pos] = snew;
     a.tokmap[(size_t)b * a.capacity + len] = (uint32_t)slot | ((uint32_t)tier << 31);
     cnt[0] = len + 1;
@@ -1026,6 +1028,7 @@ bool launch_append(const kvq_layout* L, uint8_t* cache, const void* k_new, const
     a.vmeta[p] = (uint32_t*)(cache + L->v_meta[p]);
     a.nv[p] = L->nv[p]; a.kw[p] = L->kw[p]; a.tiles[p] = L->tiles[p];
     a.vrows[p] = L->vrows[p]; a.cap[p] = L->cap[p];
+    a.spos[p] = L->slot_pos[p] ? (int32_t*)(cache + L->slot_pos[p]) : nullptr;
   }
   a.L[0] = c.levels_hi;
   a.L[1] = c.levels_lo;

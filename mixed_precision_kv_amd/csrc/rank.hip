@@ -48,6 +48,8 @@ __global__ __launch_bounds__(256) void k_rank_slots(const int32_t* __restrict__ 
                                                     uint32_t* __restrict__ tokmap,
                                                     int32_t* __restrict__ inv_hi,
                                                     int32_t* __restrict__ inv_lo,
+                                                    int32_t* __restrict__ pos_hi,
+                                                    int32_t* __restrict__ pos_lo,
                                                     int32_t* __restrict__ counters, int T, int n_hi,
                                                     int cap, int cap_hi, int cap_lo, int nseg, int B) {
   constexpr int kChunks = SEG / 4 / 64;               // 64-token chunks per wave
@@ -96,10 +98,12 @@ __global__ __launch_bounds__(256) void k_rank_slots(const int32_t* __restrict__ 
       if ((m[k] >> lane) & 1ull) {
         tokmap[(size_t)b * cap + t] = hb;
         inv_hi[(size_t)b * cap_hi + hb] = t;
+        if (pos_hi) pos_hi[(size_t)b * cap_hi + hb] = t;   // pre-RoPE keys: slot -> position
       } else {
         const uint32_t slot = (uint32_t)t - hb;
         tokmap[(size_t)b * cap + t] = slot | 0x80000000u;
         inv_lo[(size_t)b * cap_lo + slot] = t;
+        if (pos_lo) pos_lo[(size_t)b * cap_lo + slot] = t;
       }
     }
     pre += (uint32_t)__popcll(m[k]);
@@ -420,8 +424,11 @@ bool launch_rank_tiers(const kvq_layout* L, uint8_t* cache, const float* scores,
     k_rank_merge_part<<<seq_grid(4 * nb4 * m.ngrp, B), 1024, 0, s>>>(m);
     k_rank_finish<<<seq_grid(4 * nb4, B), 1024, 0, s>>>(m);
   }
-  k_rank_slots<kSortTile><<<gblk, 256, 0, s>>>(ranks, segcnt, tokmap, inv_hi, inv_lo, counters, T, n_hi,
-                                               L->cfg.capacity, L->cap[0], L->cap[1], nblk, B);
+  int32_t* pos_hi = L->slot_pos[0] ? (int32_t*)(cache + L->slot_pos[0]) : nullptr;
+  int32_t* pos_lo = L->slot_pos[1] ? (int32_t*)(cache + L->slot_pos[1]) : nullptr;
+  k_rank_slots<kSortTile><<<gblk, 256, 0, s>>>(ranks, segcnt, tokmap, inv_hi, inv_lo, pos_hi, pos_lo,
+                                               counters, T, n_hi, L->cfg.capacity, L->cap[0], L->cap[1],
+                                               nblk, B);
   return hipGetLastError() == hipSuccess;
 }
 

@@ -27,7 +27,7 @@ class KvqConfig(ctypes.Structure):
         "mode", "batch", "kv_heads", "q_heads", "head_dim", "capacity",
         "levels_hi", "levels_lo", "group", "cap_hi", "cap_lo",
         "k_levels", "k_block", "v_levels", "v_group", "window", "sparse_per_vec",
-        "reorder")] + [("clip", ctypes.c_float)]
+        "reorder")] + [("clip", ctypes.c_float), ("rope_theta", ctypes.c_float)]
 
 
 class KvqLayout(ctypes.Structure):
@@ -40,6 +40,7 @@ class KvqLayout(ctypes.Structure):
         ("k_words", _i64 * 2), ("k_meta", _i64 * 2), ("v_words", _i64 * 2), ("v_meta", _i64 * 2),
         ("sparse", _i64), ("k_win", _i64), ("v_win", _i64),
         ("chan_order", _i64),
+        ("slot_pos", _i64 * 2),
         ("total_bytes", _i64),
     ]
 
@@ -126,6 +127,7 @@ def config_for(w) -> KvqConfig:
         c.cap_lo = min(w.capacity, w.tokens - w.n_hi + w.append_steps)
         c.reorder = 1 if w.reorder else 0
         c.clip = w.clip
+        c.rope_theta = getattr(w, "rope_theta", 0.0)
     else:
         c.k_levels, c.k_block, c.v_levels, c.v_group = w.k_levels, w.k_block, w.v_levels, w.v_group
         c.window, c.sparse_per_vec = w.window, w.sparse_per_vec

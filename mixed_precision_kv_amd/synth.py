@@ -66,6 +66,8 @@ class Workload:
     # channel rearrangement and clipped group ranges (tiered mode)
     reorder: bool = False             # store the channel orders of channel_orders()
     clip: float = 0.0                 # group min/max scale factor; 0: no clipping
+    # pre-RoPE keys (tiered mode): rotary base; 0: keys used as given
+    rope_theta: float = 0.0
     seed: int = 0
 
     @property
@@ -108,6 +110,13 @@ W_KCHAN = BY_NAME["c5_kchan_b4_t64k"]          # 4 x 65536, per-channel keys
 # brought into one group by the stored order; clip factor 0.9.
 W_SKVQ = W_LLAMA.shrink(name="skvq_llama8b_b8_t32k", outlier_stride=32, reorder=True, clip=0.9)
 BY_NAME[W_SKVQ.name] = W_SKVQ
+# The Llama-shaped layer and the long-context workload with pre-RoPE keys
+# (KVQuant summary, "techniques"): keys drawn as above stand for the keys
+# before the rotary embedding; Llama-3.1's rotary base 500000.
+W_ROPE = W_LLAMA.shrink(name="rope_llama8b_b8_t32k", rope_theta=500000.0)
+W_ROPE_LONG = W_LONG.shrink(name="rope_long_b1_t128k", rope_theta=500000.0)
+BY_NAME[W_ROPE.name] = W_ROPE
+BY_NAME[W_ROPE_LONG.name] = W_ROPE_LONG
 
 
 CHUNK = 1 << 22

@@ -69,3 +69,9 @@ def kchan_unit_arrays(buf, lay):
     vs, vz = _split_meta(vm)
     return dict(k_words=kwd, k_scale=ks, k_zero=kz, sparse=sp, v_words=vwd, v_scale=vs, v_zero=vz,
                 k_win=kwin, v_win=vwin)
+
+
+def slot_positions(buf, lay, p):
+    """Token position of every slot of pool p, [B][cap[p]] (pre-RoPE keys)."""
+    B, cap = lay.cfg.batch, lay.cap[p]
+    return np.frombuffer(buf, dtype=np.int32, count=B * cap, offset=lay.slot_pos[p]).reshape(B, cap)

@@ -82,6 +82,8 @@ def _cfg(**kw):
     (dict(group=48), 2), (dict(capacity=0), 1), (dict(batch=0), 1), (dict(mode=7), 1),
     (dict(cap_hi=100, cap_lo=100), 1), (dict(cap_hi=5000), 1),
     (dict(reorder=2), 1), (dict(clip=-0.5), 1), (dict(clip=1.5), 1), (dict(clip=float("nan")), 1),
+    (dict(rope_theta=0.5), 1), (dict(rope_theta=-1.0), 1), (dict(rope_theta=float("inf")), 1),
+    (dict(rope_theta=10000.0, reorder=1), 2),
 ])
 def test_layout_rejects(kw, status):
     with pytest.raises(kvq.KvqError) as e:
@@ -92,7 +94,7 @@ def test_layout_rejects(kw, status):
 def test_kchan_rejects_unsupported():
     w = synth.W_KCHAN
     for kw in (dict(k_block=64), dict(v_levels=5), dict(window=600), dict(sparse_per_vec=9),
-               dict(reorder=1), dict(clip=0.9)):
+               dict(reorder=1), dict(clip=0.9), dict(rope_theta=10000.0)):
         c = kvq.config_for(w)
         for k, v in kw.items():
             setattr(c, k, v)
@@ -293,3 +295,17 @@ def test_noalloc_decode_validation():
     with pytest.raises(kvq.KvqError) as e:
         kvq.decode_attn_noalloc(big, FAKE, FAKE, 0.088, 64, FAKE, stream=0)
     assert e.value.status == 4
+
+
+def test_rope_layout_and_multi_query_unsupported():
+    """Pre-RoPE keys add the per-pool slot positions to the layout; the
+    multi-query entry point refuses such a cache on the host."""
+    w = synth.W_ROPE.shrink(name="rope_small", batch=2, kv_heads=2, q_heads=8, tokens=1000)
+    lay = kvq.layout_init(kvq.config_for(w))
+    plain = kvq.layout_init(kvq.config_for(w.shrink(rope_theta=0.0)))
+    assert plain.slot_pos[0] == plain.slot_pos[1] == 0
+    assert lay.slot_pos[0] > 0 and lay.slot_pos[1] > lay.slot_pos[0] and lay.slot_pos[0] % 256 == 0
+    assert lay.total_bytes - plain.total_bytes >= 4 * 2 * (lay.cap[0] + lay.cap[1])
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.decode_attn_multi(lay, FAKE, FAKE, 4, 0.088, 1000, FAKE, None, FAKE, 1 << 30, stream=0)
+    assert e.value.status == 2
