@@ -247,9 +247,15 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
             sc = reduce_scatter4(x);
           }
           scs[t] = (s0 + 16 * t + n < s_end) ? sc : -INFINITY;
-          if (a.raw && s0 + 16 * t + n < s_end)     // lane (n, j): head j of slot n
-            a.raw[((size_t)u * kGqa + j) * a.cap_p + s0 + 16 * t + n] = sc;
           mx = fmaxf(mx, scs[t]);
+        }
+        // raw scores after the tile loop: a branch inside it would cut the
+        // six tiles into separate blocks that the scheduler cannot overlap
+        if (a.raw) {
+#pragma unroll
+          for (int t = 0; t < KT; ++t)
+            if (s0 + 16 * t + n < s_end)     // lane (n, j): head j of slot n
+              a.raw[((size_t)u * kGqa + j) * a.cap_p + s0 + 16 * t + n] = scs[t];
         }
         // online softmax (lane (n, h): head h).  Weights go to the value wave
         // as fp16 2^6 p, rounded half up: add half an fp16 spacing to the fp32
