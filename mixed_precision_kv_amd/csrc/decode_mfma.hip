@@ -116,6 +116,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
 
   if (wave == 0) {
     // ================= keys: scores, softmax, weights =================
+    // The key wave's long dependent chain (table reads, matrix ops, lane
+    // reduction per tile) sets the pace of the pair; it gets the higher
+    // issue priority so the value waves sharing its SIMD fill the gaps.
+    __builtin_amdgcn_s_setprio(3);
     const BufRes rK = make_res(a.kwords + (size_t)u * a.tiles * KW * 16, a.tiles * KW * 16 * 4);
     const BufRes rKM = make_res(a.kmeta + (size_t)u * a.tiles * NG * 16, a.tiles * NG * 16 * 4);
     uint32_t kwoff[KWL];
