@@ -415,8 +415,8 @@ def main():
     ap.add_argument("--decode-iters", type=int, default=100,
                     help="workloads without generation steps, and --only decode: decode calls timed")
     ap.add_argument("--replicas", type=int, default=0, help="decode cache replicas (0: auto, >= 1 GB)")
-    ap.add_argument("--cpu-units-per-worker", type=int, default=2)
-    ap.add_argument("--cpu-gen-steps", type=int, default=6,
+    ap.add_argument("--cpu-units-per-worker", type=int, default=4)
+    ap.add_argument("--cpu-gen-steps", type=int, default=160,
                     help="generation steps per sampled unit in the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
