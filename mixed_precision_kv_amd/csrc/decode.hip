@@ -271,38 +271,24 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_kchan(DecodeArgs a) {
   finish_partial(part, sm, sl, accs);
 }
 
-// Log-sum-exp merge of every chunk partial of one (unit, head) -> fp16 output,
-// in one pass.  Thread (slice sl, quad q) owns chunks c = sl, sl + S, ... and
-// channels 4q..4q+3; it issues the loads of a batch of kMergeBatch chunks
-// (running max m_c, sum l_c, four acc values, 16-byte aligned: 132 floats
-// per head) before using any, so one memory round trip serves the batch, and
-// keeps its own running max, rescaling what it has summed when the max
-// grows.  The slices are then combined through LDS against the largest max.
+// Merge of the chunk partials: a partial per (unit, chunk, head) is the
+// chunk's running max m_c, its sum l_c, two pad words and the 128 sums
+// (132 floats, 16-byte aligned).
 constexpr int kMergeBatch = 8;                // chunks per thread per round trip
 
-template <int THREADS>
-__global__ __launch_bounds__(THREADS) void k_merge(const float* __restrict__ part,
-                                                   uint16_t* __restrict__ out, int nch_total,
-                                                   int Hkv, float2* __restrict__ stats,
-                                                   const uint8_t* __restrict__ vorder) {
-  constexpr int S = THREADS / 32;             // slices
-  __shared__ float smax[S];
-  __shared__ float4 racc[S][32];
-  __shared__ float rl[S];
-  const int u = blockIdx.x, hh = blockIdx.y, t = threadIdx.x;
-  const int b = u / Hkv, hk = u % Hkv;
-  const float* pu = part + (size_t)u * nch_total * kGqa * kPartStride + hh * kPartStride;
-  const size_t cs = (size_t)kGqa * kPartStride;
-  const int q = t & 31, sl = t >> 5;
-  float M = -INFINITY, lsum = 0.f;
-  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int c0 = sl; c0 < nch_total; c0 += S * kMergeBatch) {
+// Chunks c0, c0 + step, ... (< nch) of one head, partials at pu with cs
+// floats between chunks, into (M, lsum, o): a batch's loads are issued
+// before any is used; the running max grows batch by batch, rescaling what
+// has been summed.  Lane q owns channels 4q .. 4q + 3.
+__device__ inline void merge_accumulate(const float* __restrict__ pu, size_t cs, int c0, int step, int nch,
+                                        int q, float& M, float& lsum, float4& o) {
+  for (int cb = c0; cb < nch; cb += step * kMergeBatch) {
     float mv[kMergeBatch], lv[kMergeBatch];
     float4 av[kMergeBatch];
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) {
-      const int c = c0 + k * S;
-      const bool ok = c < nch_total;
+      const int c = cb + k * step;
+      const bool ok = c < nch;
       const float* pc = pu + (size_t)(ok ? c : 0) * cs;
       mv[k] = ok ? pc[0] : -INFINITY;
       lv[k] = pc[1];
@@ -325,6 +311,41 @@ __global__ __launch_bounds__(THREADS) void k_merge(const float* __restrict__ par
     }
     M = mb;
   }
+}
+
+// Lane q's four channels of one head's output r / l as fp16; position p of
+// the sums is channel vorder_h[p] of the output (stored value order).
+__device__ inline void merge_write(uint16_t* __restrict__ po, const uint8_t* __restrict__ vorder_h, int q,
+                                   float4 r, float l) {
+  const uint32_t ch = vorder_h ? *reinterpret_cast<const uint32_t*>(vorder_h + 4 * q) & 0x7F7F7F7Fu
+                               : 0x03020100u + 0x04040404u * (uint32_t)q;
+  po[ch & 0xFF] = f2h_rne(r.x / l);
+  po[(ch >> 8) & 0xFF] = f2h_rne(r.y / l);
+  po[(ch >> 16) & 0xFF] = f2h_rne(r.z / l);
+  po[ch >> 24] = f2h_rne(r.w / l);
+}
+
+// Log-sum-exp merge of every chunk partial of one (unit, head) -> fp16 output,
+// in one pass.  Thread (slice sl, quad q) owns chunks c = sl, sl + S, ... and
+// channels 4q..4q+3; the slices are combined through LDS against the largest
+// max.
+template <int THREADS>
+__global__ __launch_bounds__(THREADS) void k_merge(const float* __restrict__ part,
+                                                   uint16_t* __restrict__ out, int nch_total,
+                                                   int Hkv, float2* __restrict__ stats,
+                                                   const uint8_t* __restrict__ vorder) {
+  constexpr int S = THREADS / 32;             // slices
+  __shared__ float smax[S];
+  __shared__ float4 racc[S][32];
+  __shared__ float rl[S];
+  const int u = blockIdx.x, hh = blockIdx.y, t = threadIdx.x;
+  const int b = u / Hkv, hk = u % Hkv;
+  const float* pu = part + (size_t)u * nch_total * kGqa * kPartStride + hh * kPartStride;
+  const size_t cs = (size_t)kGqa * kPartStride;
+  const int q = t & 31, sl = t >> 5;
+  float M = -INFINITY, lsum = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  merge_accumulate(pu, cs, sl, S, nch_total, q, M, lsum, o);
   if (q == 0) smax[sl] = M;
   __syncthreads();
   float Mg = smax[0];
@@ -345,20 +366,34 @@ __global__ __launch_bounds__(THREADS) void k_merge(const float* __restrict__ par
     }
     uint16_t* po = out + ((size_t)b * Hkv * kGqa + hk * kGqa + hh) * kD;
     if (stats && t == 0) stats[u * kGqa + hh] = make_float2(Mg, l);   // (max, sum) of the head
-    // position p of the sums is channel vorder[p] of the output (stored order)
-    const uint32_t ch = vorder ? *reinterpret_cast<const uint32_t*>(vorder + (size_t)hk * kD + 4 * t) & 0x7F7F7F7Fu
-                               : 0x03020100u + 0x04040404u * (uint32_t)t;
-    po[ch & 0xFF] = f2h_rne(r.x / l);
-    po[(ch >> 8) & 0xFF] = f2h_rne(r.y / l);
-    po[(ch >> 16) & 0xFF] = f2h_rne(r.z / l);
-    po[ch >> 24] = f2h_rne(r.w / l);
+    merge_write(po, vorder ? vorder + (size_t)hk * kD : nullptr, t, r, l);
   }
 }
 
-// 8 slices for few chunks per unit, 32 for many (long contexts over few units)
+// Few chunks per unit: one workgroup of 128 threads per unit; lane (head
+// t / 32, quad t % 32) merges every chunk of its head by itself (one slice,
+// no LDS combine), so a unit costs two waves instead of four workgroups.
+__global__ __launch_bounds__(128) void k_merge_unit(const float* __restrict__ part, uint16_t* __restrict__ out,
+                                                    int nch_total, int Hkv, float2* __restrict__ stats,
+                                                    const uint8_t* __restrict__ vorder) {
+  const int u = blockIdx.x, t = threadIdx.x, hh = t >> 5, q = t & 31;
+  const int b = u / Hkv, hk = u % Hkv;
+  const float* pu = part + (size_t)u * nch_total * kGqa * kPartStride + hh * kPartStride;
+  float M = -INFINITY, lsum = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  merge_accumulate(pu, (size_t)kGqa * kPartStride, 0, 1, nch_total, q, M, lsum, o);
+  if (stats && q == 0) stats[u * kGqa + hh] = make_float2(M, lsum);
+  merge_write(out + ((size_t)b * Hkv * kGqa + hk * kGqa + hh) * kD, vorder ? vorder + (size_t)hk * kD : nullptr,
+              q, o, lsum);
+}
+
+// One slice per head for a batch of chunks or two, 8 slices for more, 32 for
+// many (long contexts over few units)
 static void launch_merge(const float* part, uint16_t* out, int U, int nch, int Hkv, hipStream_t s,
                          float2* stats = nullptr, const uint8_t* vorder = nullptr) {
-  if (nch <= 8 * kMergeBatch)
+  if (nch <= 2 * kMergeBatch)
+    k_merge_unit<<<U, 128, 0, s>>>(part, out, nch, Hkv, stats, vorder);
+  else if (nch <= 8 * kMergeBatch)
     k_merge<256><<<dim3(U, kGqa), 256, 0, s>>>(part, out, nch, Hkv, stats, vorder);
   else
     k_merge<1024><<<dim3(U, kGqa), 1024, 0, s>>>(part, out, nch, Hkv, stats, vorder);
