@@ -42,7 +42,8 @@ namespace kvq {
 // key tile the lane's expanded digits go to LDS in channel order; lane (n, j)
 // then takes channels 32 j .. 32 j + 31 of slot n (16 adjacent pairs),
 // dequantizes them in fp32, turns pair i by position * theta_i (the angle in
-// revolutions reduced in fp64, then the hardware sine and cosine), and hands
+// revolutions, reduced mod 1 in 32-bit fixed point from a 64-bit fraction
+// theta_i / 2 pi, then the hardware sine and cosine), and hands
 // the rotated key to the matrix cores as fp16 high and low parts against A
 // rows 4h .. 4h + 3 = query head h, so lane (n, j) receives head j's score.
 template <int L, int G, bool ROPE>
@@ -70,7 +71,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
   __shared__ int mpos_lds[64 * META_PER_LANE];
   __shared__ float zred[16];
   __shared__ uint2 ctab[DK::kTableEntries];   // chunk -> four fp16 digits
-  __shared__ double rev_lds[ROPE ? kD / 2 : 1];   // theta_i / 2 pi: revolutions per position
+  __shared__ uint2 rev_lds[ROPE ? kD / 2 : 1];    // theta_i / 2 pi as a 64-bit binary fraction (hi, lo)
   __shared__ __attribute__((aligned(16))) _Float16 kc_lds[ROPE ? 16 : 1][ROPE ? kD + 8 : 1];  // a key tile, channel order
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -104,9 +105,15 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
     mpos_lds[e] = jj * VK + DV::pos_of(rem / NV, rem % NV);
   }
   DK::fill(ctab, threadIdx.x, 128);
-  if (ROPE && threadIdx.x < kD / 2)
-    rev_lds[threadIdx.x] = exp2(-(double)(2 * threadIdx.x) / kD * log2((double)a.rope_theta)) *
-                           0.15915494309189533577;   // / (2 pi)
+  if (ROPE && threadIdx.x < kD / 2) {
+    // revolutions per position, f = theta_i / 2 pi < 1/(2 pi), split exactly
+    // into its first 64 fraction bits (f * 2^32 and its remainder are exact
+    // in fp64)
+    const double f = exp2(-(double)(2 * threadIdx.x) / kD * log2((double)a.rope_theta)) *
+                     0.15915494309189533577;   // / (2 pi)
+    const double f32 = f * 4294967296.0, fh = floor(f32);
+    rev_lds[threadIdx.x] = make_uint2((uint32_t)fh, (uint32_t)floor((f32 - fh) * 4294967296.0));
+  }
   // operand positions that hold no slot keep weight and scale 0
   for (int i = threadIdx.x; i < 4 * VK; i += 128) {
     for (int h = 0; h < 4; ++h) { pw_lds[0][h][i] = (_Float16)0.0f; pw_lds[1][h][i] = (_Float16)0.0f; }
@@ -197,7 +204,6 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
           }
         }
       wave_lds_fence();
-      const double pd = (double)pos;
       f4 pr = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
@@ -207,9 +213,11 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
         for (int e = 0; e < 8; e += 2) {
           const float x = __builtin_fmaf(sg, (float)cv[e], zz);
           const float y = __builtin_fmaf(sg, (float)cv[e + 1], zz);
-          double r = pd * rev_lds[16 * j + 4 * m + e / 2];
-          r -= floor(r);                     // revolutions in [0, 1)
-          const float rv = (float)r;
+          // pos * f mod 1 in 32-bit fixed point: the low word of pos * hi
+          // plus the carry of pos * lo (error below 2^-32 revolutions)
+          const uint2 fr = rev_lds[16 * j + 4 * m + e / 2];
+          const uint32_t t = pos * fr.x + __umulhi(pos, fr.y);
+          const float rv = (float)t * 0x1p-32f;   // revolutions in [0, 1]
           const float cs = __builtin_amdgcn_cosf(rv), sn = __builtin_amdgcn_sinf(rv);
           const float xr = x * cs - y * sn, yr = x * sn + y * cs;
           hi[e] = (_Float16)xr;
