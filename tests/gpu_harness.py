@@ -137,6 +137,22 @@ def compare_tiered_unit(buf, lay, pools, u, what=""):
         assert not g["v_words"][u, rows:].any(), f"{what} v_words slack pool {p}"
 
 
+def keys_in_token_order(pools, inv_b, n):
+    """Dequantized keys of one unit in token order from its two pools
+    (inv_b[p]: the token index of each slot of pool p)."""
+    d = pools[0].k_hat().shape[1] if pools[0].n else pools[1].k_hat().shape[1]
+    kh = np.zeros((n, d))
+    for p in range(2):
+        if pools[p].n:
+            kh[np.asarray(inv_b[p], dtype=np.int64)] = pools[p].k_hat()
+    return kh
+
+
+def mass_mismatches(got, ref):
+    """Tokens whose attention mass is off by more than 1e-4 ref + 1e-6."""
+    return np.abs(got - ref) > 1e-4 * ref + 1e-6
+
+
 def oracle_unit_attention(w, q, b, h, khat, vhat, scale):
     g = w.q_heads // w.kv_heads
     return O.decode_unit(q[b, h * g:(h + 1) * g].astype(np.float64), khat, vhat, float(scale))

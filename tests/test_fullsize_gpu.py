@@ -1,16 +1,18 @@
 """GPU parity at the five full workload sizes, in the launch configuration the
 bench times.  Ranks, token maps, counters and sorted scores are compared for
 every sequence; packed words, codes and scale/zero bit-exact and attention
-within 2e-3 for sampled (sequence, KV head) units; every output is checked
-for properties that hold at any size (finite, inside the value range)."""
+within 2e-3 for sampled (sequence, KV head) units; the per-token attention
+mass of one whole sequence within 1e-4 ref + 1e-6 per token; every output is
+checked for properties that hold at any size (finite, inside the value
+range, masses summing to the number of query heads)."""
 import numpy as np
 import pytest
 
 from mixed_precision_kv_amd import synth
 from oracle import kvq_oracle as O
 import layout_view as LV
-from gpu_harness import (GpuRun, TOL, compare_tiered_unit, log, oracle_tiers, oracle_unit,
-                         oracle_unit_attention)
+from gpu_harness import (GpuRun, TOL, compare_tiered_unit, keys_in_token_order, log, mass_mismatches,
+                         oracle_tiers, oracle_unit, oracle_unit_attention)
 
 pytestmark = pytest.mark.gpu
 
@@ -51,6 +53,15 @@ def test_tiered_fullsize(w):
     assert np.all(np.isfinite(mass)) and np.all(mass >= 0)
     assert np.allclose(mass[:, :w.tokens].astype(np.float64).sum(1), w.q_heads, rtol=1e-4)
     assert np.all(mass[:, w.tokens:] == 0)
+    # and element by element for the last sequence, every token, against the
+    # oracle over all of that sequence's KV heads
+    bm = w.batch - 1
+    ks = [keys_in_token_order(oracle_unit(w, inp, inv, bm, h), inv[bm], w.tokens) for h in range(w.kv_heads)]
+    ref_m = O.token_attention_mass(inp.q[bm].astype(np.float64), ks, float(run.scale))
+    got_m = mass[bm, :w.tokens].astype(np.float64)
+    bad = mass_mismatches(got_m, ref_m)
+    assert not bad.any(), f"mass b{bm}: {int(bad.sum())} tokens, worst {np.abs(got_m - ref_m).max():.3e}"
+    log(f"{w.name}: mass of sequence {bm} ({w.tokens} tokens) max abs err {np.abs(got_m - ref_m).max():.3e}")
     # a block of 16 new query tokens, in the bench's launch configuration
     M = 16
     qm = synth.make_queries(w, M)

@@ -12,7 +12,8 @@ import pytest
 
 from mixed_precision_kv_amd import kvq, synth
 from oracle import kvq_oracle as O
-from gpu_harness import GpuRun, TOL, log, oracle_tiers, oracle_unit, oracle_unit_attention, to_dev
+from gpu_harness import (GpuRun, TOL, keys_in_token_order, log, mass_mismatches, oracle_tiers, oracle_unit,
+                         oracle_unit_attention, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -29,24 +30,15 @@ def _decode_mass(run, q_np, max_len):
     return out.cpu().numpy(), mass.cpu().numpy()
 
 
-def _token_order(pools, inv_b, n):
-    """Dequantized keys of one unit in token order from its two pools."""
-    kh = np.zeros((n, pools[0].k_hat().shape[1] if pools[0].n else pools[1].k_hat().shape[1]))
-    for p in range(2):
-        if pools[p].n:
-            kh[np.asarray(inv_b[p], dtype=np.int64)] = pools[p].k_hat()
-    return kh
-
-
 def _check(w, inp, run, q, n, pools, inv, max_len):
     out, mass = _decode_mass(run, q, max_len)
     g = w.q_heads // w.kv_heads
     errs = []
     for b in range(w.batch):
-        ks = [_token_order(pools[(b, h)], inv[b], n) for h in range(w.kv_heads)]
+        ks = [keys_in_token_order(pools[(b, h)], inv[b], n) for h in range(w.kv_heads)]
         ref = O.token_attention_mass(q[b].astype(np.float64), ks, float(run.scale))
         got = mass[b, :n].astype(np.float64)
-        bad = np.abs(got - ref) > 1e-4 * ref + 1e-6
+        bad = mass_mismatches(got, ref)
         assert not bad.any(), f"b{b}: {int(bad.sum())} tokens, worst {np.abs(got - ref).max():.3e}"
         assert abs(got.sum() - w.q_heads) <= 1e-4 * w.q_heads
         assert np.all(mass[b, n:] == 0.0)
