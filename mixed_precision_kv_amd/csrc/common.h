@@ -19,6 +19,15 @@ constexpr int kFlagPoolFull = 1;
 constexpr int kFlagBigValueScale = 2;
 constexpr uint32_t kBigScaleBits = 0x6400u;   // fp16 1024.0
 
+// Cache policy of the decode kernels' loads of packed words and (scale,
+// zero) pairs, which each call reads exactly once: non-temporal (the `nt`
+// bit), a hint that the data is streamed.  Measured on MI355X: a 16-byte
+// read stream runs at 6.9 instead of 6.1 TB/s with it, and the decode pools
+// run 2-4 % faster at unchanged counted HBM traffic.  Quantize keeps the
+// default policy: with this one its counted fetch grew by 5.6 % and its time
+// by 3-7 %.
+constexpr int kStreamPolicy = 2;
+
 // Sets kFlagBigValueScale of sequence b when any lane of the wave formed a
 // value scale (fp16 bits s_bits, non-negative) of 1024 or more: one atomic
 // per wave, only in waves that hold one.

@@ -76,11 +76,11 @@ __device__ inline BufRes make_res(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
 __device__ inline uint32_t bload(BufRes r, uint32_t byte_off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, 0);
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, kStreamPolicy);
 }
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ inline u32x2 bload2(BufRes r, uint32_t byte_off) {
-  return __builtin_amdgcn_raw_buffer_load_b64(r, (int)byte_off, 0, 0);
+  return __builtin_amdgcn_raw_buffer_load_b64(r, (int)byte_off, 0, kStreamPolicy);
 }
 
 }  // namespace kvq

@@ -1,7 +1,8 @@
 // Read-stream probe: the achievable HBM read bandwidth of this device, the
 // second reference (beside the published 8 TB/s) against which the decode
 // and quantize rates are reported.  Every byte of the buffer is read once
-// with 16-byte loads, each workgroup a contiguous slab, coalesced per wave;
+// with 16-byte non-temporal loads (the policy the kernels use for their
+// read-once streams), each workgroup a contiguous slab, coalesced per wave;
 // the xor of everything read is kept so the loads cannot be dropped.
 #include "common.h"
 #include "internal.h"
@@ -23,7 +24,7 @@ __global__ __launch_bounds__(kProbeThreads) void k_stream_read(const u32x4* __re
 #pragma unroll
     for (int k = 0; k < kProbeUnroll; ++k) {
       const size_t i = i0 + (size_t)k * kProbeThreads;
-      v[k] = i < s1 ? src[i] : (u32x4){0u, 0u, 0u, 0u};
+      v[k] = i < s1 ? __builtin_nontemporal_load(src + i) : (u32x4){0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int k = 0; k < kProbeUnroll; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
