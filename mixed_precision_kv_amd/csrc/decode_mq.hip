@@ -70,8 +70,12 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int b = u / a.Hkv, hk = u % a.Hkv;
   float* part = a.part + (((size_t)u * a.nqg + qg) * a.nch_total + a.part_off + c) * kMqR * kPartF;
   const int n_valid = a.counters[b * 4 + 1 + a.pool];
-  const int s_begin = c * a.chunk;
-  const int s_end = min(n_valid, s_begin + a.chunk);
+  // the unit's filled slots split evenly over the launch's chunks, in whole
+  // macro tiles (the grid is sized for the pool's capacity, which can exceed
+  // the filled slots by a whole chunk's share)
+  const int span = ((n_valid + MT - 1) / MT + (int)gridDim.x - 1) / (int)gridDim.x * MT;
+  const int s_begin = c * span;
+  const int s_end = min(n_valid, s_begin + span);
   if (s_begin >= s_end) {
     for (int i = threadIdx.x; i < kMqR * kPartF; i += 128) part[i] = (i % kPartF == 0) ? -INFINITY : 0.f;
     return;

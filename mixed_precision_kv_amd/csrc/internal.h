@@ -72,7 +72,8 @@ struct PoolArgs {
   const uint32_t* vwords;
   const uint32_t* vmeta;
   int pool, Hkv, tiles, vrows, nch_total, part_off;
-  int chunk;          // slots per workgroup (a whole number of macro tiles)
+  int chunk;          // slots per workgroup at full capacity (sets the grid; the kernel
+                      // splits the filled slots evenly over gridDim.x chunks)
   float c;            // softmax scale * log2(e)
   float* raw;         // or null: log2-domain scores out, [unit][head][cap_p]
   int cap_p;          // slots of this pool
@@ -94,7 +95,8 @@ struct PoolMqArgs {
   const uint32_t* vwords;
   const uint32_t* vmeta;
   int pool, Hkv, M, nqg, tiles, vrows, nch_total, part_off;
-  int chunk;          // slots per workgroup (a whole number of macro tiles)
+  int chunk;          // slots per workgroup at full capacity (sets the grid; the kernel
+                      // splits the filled slots evenly over gridDim.x chunks)
   float c;            // softmax scale * log2(e)
   const uint8_t* korder = nullptr;   // [Hkv][128] stored key channel order: q is read through it
 };
