@@ -19,14 +19,23 @@ constexpr int kFlagPoolFull = 1;
 constexpr int kFlagBigValueScale = 2;
 constexpr uint32_t kBigScaleBits = 0x6400u;   // fp16 1024.0
 
-// Cache policy of the decode kernels' loads of packed words and (scale,
-// zero) pairs, which each call reads exactly once: non-temporal (the `nt`
-// bit), a hint that the data is streamed.  Measured on MI355X: a 16-byte
-// read stream runs at 6.9 instead of 6.1 TB/s with it, and the decode pools
-// run 2-4 % faster at unchanged counted HBM traffic.  Quantize keeps the
-// default policy: with this one its counted fetch grew by 5.6 % and its time
-// by 3-7 %.
+// Cache policy of loads whose data a kernel reads exactly once (the decode's
+// packed words and (scale, zero) pairs, the fp16 rows quantize reads):
+// non-temporal (the `nt` bit), a hint that the data is streamed.  Measured
+// on MI355X: a 16-byte read stream runs at 6.9 instead of 6.1 TB/s with it,
+// the decode pools 2-4 % faster at unchanged counted HBM traffic.  It pays
+// only where each load instruction covers whole 128-byte lines: quantize's
+// row gather read 64-byte halves with four lanes per row, and with the
+// policy it fetched 5.6 % more and ran 3-7 % slower; with eight lanes per
+// row it reads whole lines.
 constexpr int kStreamPolicy = 2;
+
+// 16 bytes (16-byte aligned) of a read-once stream, non-temporal.
+__device__ inline uint4 ld_stream16(const void* p) {
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
 
 // Sets kFlagBigValueScale of sequence b when any lane of the wave formed a
 // value scale (fp16 bits s_bits, non-negative) of 1024 or more: one atomic

@@ -291,9 +291,7 @@ template <int L, int G, bool SKVQ>
 __global__ __launch_bounds__(kQThreads) void k_quant_rows(QuantArgs a) {
   using P = RowPack<L>;
   constexpr int NV = P::NV, KW = P::KW, NG = kD / G, SL = P::SL, ROWS = P::ROWS;
-  constexpr int CPG = G / 32;                      // chunks per group per lane
-  constexpr int LPG = 4 / NG;                      // lanes of a quad per owned group
-  constexpr int NP = (SL + 63) / 64;               // rows per thread
+  constexpr int NP = (SL + 31) / 32;               // rows per thread (32 rows per pass)
   constexpr int CW = kD / 4 + 1;                   // dwords per code row (+1: bank spread)
   static_assert(NG >= 1 && NG <= 4, "group of 32, 64 or 128 channels");
   __shared__ uint32_t codes[SL][CW];               // byte codes, [slot][channel]
@@ -303,7 +301,11 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows(QuantArgs a) {
   const int tid = threadIdx.x, u = blockIdx.y;
   const int b = u / a.Hkv, h = u % a.Hkv;
   const int s0 = blockIdx.x * SL;
-  const int q = tid & 3, rp = tid >> 2;            // lane in quad, row of the pass
+  // eight lanes per row: lane q holds channels 64 i + 8 q .. 64 i + 8 q + 7
+  // (i = 0, 1), so one load instruction reads whole 128-byte lines of eight
+  // rows; a 32-channel group is one quad of the eight
+  const int q = tid & 7, rp = tid >> 3;            // lane in the row's eight, row of the pass
+  const int qh = q >> 2, ql = q & 3;               // quad of the row, lane in the quad
   {
     const int s = s0 + tid;
     tok[tid] = (tid < SL && s < a.n) ? (a.inv ? a.inv[(size_t)b * a.inv_cap + s] : s) : -1;
@@ -312,32 +314,34 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows(QuantArgs a) {
   float one = 1.0f;
   asm volatile("" : "+v"(one));
   const int tiled = a.tiles * kTile;
-  const int gown = q / LPG;                        // the group whose scale this lane forms
+  // the group whose scale this lane forms (two lanes per group for G 32,
+  // four for G 64, all eight for G 128), and whether it writes its (scale, zero)
+  const int gown = G == 32 ? 2 * (ql & 1) + qh : G == 64 ? (ql & 1) : 0;
+  const bool owner = G == 32 ? ql < 2 : q < NG;
   for (int kv = a.kwords ? 0 : 1; kv < 2; ++kv) {
     const uint16_t* base = (kv ? a.v : a.k) + b * a.sb + h * a.sh + 8 * q;
-    uint4 x[NP][4];
+    uint4 x[NP][2];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-      const int t = tok[rp + 64 * p];              // -1: no token (values 0, codes 0)
+      const int t = tok[rp + 32 * p];              // -1: no token (values 0, codes 0)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        x[p][i] = t >= 0 ? *reinterpret_cast<const uint4*>(base + (int64_t)t * a.st + 32 * i)
-                         : make_uint4(0u, 0u, 0u, 0u);
+      for (int i = 0; i < 2; ++i)
+        x[p][i] = t >= 0 ? ld_stream16(base + (int64_t)t * a.st + 64 * i) : make_uint4(0u, 0u, 0u, 0u);
     }
     // stored channel orders: bytes of the channels at positions
-    // 32 i + 8 q .. 32 i + 8 q + 7 of this lane
+    // 64 i + 8 q .. 64 i + 8 q + 7 of this lane
     const uint8_t* ord = SKVQ ? (kv ? a.vorder : a.korder) : nullptr;
-    uint32_t ow[8];
+    uint32_t ow[4];
     if (SKVQ && ord) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          ow[2 * i + j] = *reinterpret_cast<const uint32_t*>(ord + (size_t)h * kD + 32 * i + 8 * q + 4 * j);
+          ow[2 * i + j] = *reinterpret_cast<const uint32_t*>(ord + (size_t)h * kD + 64 * i + 8 * q + 4 * j);
     }
     if (SKVQ && ord) {
       // every pass's rows through LDS, gathered back in the stored order; a
-      // wave stages and gathers only its own 16 rows, so a wave-level
+      // wave stages and gathers only its own 8 rows, so a wave-level
       // barrier orders its accesses (no workgroup barrier)
       uint32_t* srow = stage[rp];
       const uint16_t* hrow = reinterpret_cast<const uint16_t*>(srow);
@@ -345,13 +349,13 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows(QuantArgs a) {
       for (int p = 0; p < NP; ++p) {
         wave_lds_sync();                             // the previous pass has been gathered
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          *reinterpret_cast<uint2*>(srow + 16 * i + 4 * q) = make_uint2(x[p][i].x, x[p][i].y);
-          *reinterpret_cast<uint2*>(srow + 16 * i + 4 * q + 2) = make_uint2(x[p][i].z, x[p][i].w);
+        for (int i = 0; i < 2; ++i) {
+          *reinterpret_cast<uint2*>(srow + 32 * i + 4 * q) = make_uint2(x[p][i].x, x[p][i].y);
+          *reinterpret_cast<uint2*>(srow + 32 * i + 4 * q + 2) = make_uint2(x[p][i].z, x[p][i].w);
         }
         wave_lds_sync();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 2; ++i) {
           uint32_t w[4];
 #pragma unroll
           for (int e = 0; e < 8; e += 2) {
@@ -366,18 +370,20 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows(QuantArgs a) {
     uint32_t* mp = kv ? a.vmeta : a.kmeta;
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-      const int r = rp + 64 * p;
-      // group extremes over the quad, then lane q keeps group gown
-      uint32_t e[NG];
+      const int r = rp + 32 * p;
+      // extremes of each load's chunk over its quad (G 32), over the row's
+      // eight lanes (G 64: the two quads through the half-row mirror), and
+      // over both loads as well (G 128); lane q keeps group gown
+      uint32_t e[2];
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        uint32_t v = chunk_extremes<CPG>(&x[p][g * CPG]);
+      for (int i = 0; i < 2; ++i) {
+        uint32_t v = chunk_extremes<1>(&x[p][i]);
         v = hmin(v, quad_perm<kQuadXor1>(v));
-        e[g] = hmin(v, quad_perm<kQuadXor2>(v));
+        v = hmin(v, quad_perm<kQuadXor2>(v));
+        if (G >= 64) v = hmin(v, quad_perm<kRowHalfMirror>(v));
+        e[i] = v;
       }
-      uint32_t eo = e[0];
-#pragma unroll
-      for (int g = 1; g < NG; ++g) eo = gown == g ? e[g] : eo;
+      const uint32_t eo = G == 128 ? hmin(e[0], e[1]) : e[ql & 1];
       uint32_t mn = eo & 0xFFFFu, mx = (eo >> 16) ^ 0x8000u;
       if constexpr (SKVQ) clip_range(mn, mx, a.clip);
       GroupQ gq = group_setup(mn, mx, L);
@@ -385,40 +391,41 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows(QuantArgs a) {
       if (kv) flag_big_value_scale(a.counters, b, gq.s_bits);
       const uint32_t meta = gq.s_bits | (mn << 16);
       const bool sub = (gq.s_bits & 0x7C00u) == 0u;    // zero or subnormal scale
-      if (r < SL && (q % LPG) == 0) {
+      if (r < SL && owner) {
         const int s = s0 + r;
         if (s < tiled) mp[(((size_t)u * a.tiles + s / kTile) * NG + gown) * kTile + (s % kTile)] = meta;
       }
-      // every group's (meta, r) from its owner lane
-      uint32_t gm[NG], gr[NG];
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        if (NG == 1) { gm[g] = meta; gr[g] = __float_as_uint(gq.r); continue; }
-        if (g * LPG == 0) { gm[g] = quad_bcast<0>(meta); gr[g] = quad_bcast<0>(__float_as_uint(gq.r)); }
-        else if (g * LPG == 1) { gm[g] = quad_bcast<1>(meta); gr[g] = quad_bcast<1>(__float_as_uint(gq.r)); }
-        else if (g * LPG == 2) { gm[g] = quad_bcast<2>(meta); gr[g] = quad_bcast<2>(__float_as_uint(gq.r)); }
-        else { gm[g] = quad_bcast<3>(meta); gr[g] = quad_bcast<3>(__float_as_uint(gq.r)); }
+      // each load's (meta, r) from its group's owner in the quad: lane i of
+      // the quad forms the group of load i (G 32 and 64); G 128 has one group
+      uint32_t gm[2], gr[2];
+      if (G == 128) {
+        gm[0] = gm[1] = meta;
+        gr[0] = gr[1] = __float_as_uint(gq.r);
+      } else {
+        gm[0] = quad_bcast<0>(meta);
+        gr[0] = quad_bcast<0>(__float_as_uint(gq.r));
+        gm[1] = quad_bcast<1>(meta);
+        gr[1] = quad_bcast<1>(__float_as_uint(gq.r));
       }
-      uint32_t c[4][2];
+      uint32_t c[2][2];
       if constexpr (SKVQ) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          chunk_codes<L, true, true>(x[p][i], gm[i / CPG], __uint_as_float(gr[i / CPG]), one, c[i][0],
-                                     c[i][1]);
+        for (int i = 0; i < 2; ++i)
+          chunk_codes<L, true, true>(x[p][i], gm[i], __uint_as_float(gr[i]), one, c[i][0], c[i][1]);
       } else if (__builtin_expect(__ballot(sub && gq.s != 0.0f) != 0ull, 0)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          chunk_codes<L, true>(x[p][i], gm[i / CPG], __uint_as_float(gr[i / CPG]), one, c[i][0], c[i][1]);
+        for (int i = 0; i < 2; ++i)
+          chunk_codes<L, true>(x[p][i], gm[i], __uint_as_float(gr[i]), one, c[i][0], c[i][1]);
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          chunk_codes<L, false>(x[p][i], gm[i / CPG], __uint_as_float(gr[i / CPG]), one, c[i][0], c[i][1]);
+        for (int i = 0; i < 2; ++i)
+          chunk_codes<L, false>(x[p][i], gm[i], __uint_as_float(gr[i]), one, c[i][0], c[i][1]);
       }
       if (r < SL) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          codes[r][8 * i + 2 * q] = c[i][0];
-          codes[r][8 * i + 2 * q + 1] = c[i][1];
+        for (int i = 0; i < 2; ++i) {
+          codes[r][16 * i + 2 * q] = c[i][0];
+          codes[r][16 * i + 2 * q + 1] = c[i][1];
         }
       }
     }
