@@ -24,6 +24,8 @@
 //                VALU.
 // Partials (m, l, acc) per (unit, query group, chunk, row) are merged by
 // k_merge_mq, which also writes the log-sum-exp.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 #include "mfma_util.h"
@@ -34,9 +36,71 @@ namespace kvq {
 
 constexpr int kMqQ = 4;               // query tokens per workgroup
 constexpr int kMqR = kMqQ * kGqa;     // result rows (query, head), r = 4 m + h
+constexpr int kMqAqRegsMax = 12;     // key A operands held in registers up to this count
+
+// Key operands per (scale group g, operand mo): lane group jl's elements of
+// operand mo are digits of its words jl, jl + 4, ...; the A operand of group
+// g is the query at the channels of g among them and zero elsewhere, so the
+// matrix op of (g, mo) contributes only where one of those channels falls
+// in g.  need[g][mo] marks those; idx numbers them (the A operands kept).
+template <class DK, int KW, int NV, int KM, int G>
+struct KeyGroupOps {
+  static constexpr int NG = kD / G;
+  struct Tab {
+    bool need[kD / 32][8];
+    int idx[kD / 32][8];
+    int g_of[32], mo_of[32];
+    int n;
+  };
+  static constexpr Tab make() {
+    Tab t{};
+    for (int g = 0; g < kD / 32; ++g)
+      for (int mo = 0; mo < 8; ++mo) {
+        t.need[g][mo] = false;
+        t.idx[g][mo] = -1;
+      }
+    for (int mo = 0; mo < KM; ++mo)
+      for (int jl = 0; jl < 4; ++jl) {
+        const int nw = (KW - jl + 3) / 4;
+        for (int i = 0; i < 8; ++i) {
+          const int tt = 8 * mo + i;
+          const int wi = DK::word_of(tt);
+          if (wi < 0 || wi >= nw) continue;
+          const int d = (jl + 4 * wi) * NV + DK::digit_of(tt);
+          if (d < kD) t.need[d / G][mo] = true;
+        }
+      }
+    t.n = 0;
+    for (int g = 0; g < NG; ++g)
+      for (int mo = 0; mo < KM; ++mo)
+        if (t.need[g][mo]) {
+          t.g_of[t.n] = g;
+          t.mo_of[t.n] = mo;
+          t.idx[g][mo] = t.n++;
+        }
+    return t;
+  }
+  static constexpr Tab kTab = make();
+  static_assert(KM <= 8 && kTab.n <= 32, "key operand table");
+};
+
+// f(integral_constant<int, i>) for i = B .. E-1, unrolled at compile time
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Waves per SIMD the register allocation aims at: two, except the 5-level
+// grid with 64-channel groups, whose two waves would need about 270
+// registers (it spills at 256) and which takes one.
+__host__ __device__ constexpr int mq_min_waves(int L, int G) { return (L == 5 && G == 64) ? 1 : 2; }
 
 template <int L, int G>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k_decode_pool_mq(PoolMqArgs a) {
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(mq_min_waves(L, G)))) void k_decode_pool_mq(
+    PoolMqArgs a) {
   using T = Tiling<L>;
   constexpr int NV = T::NV, KW = T::KW, KWL = T::KWL, R = T::R, RUN = T::RUN, MT = T::MT,
                 KT = T::KT;
@@ -51,9 +115,11 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
   constexpr int VK = VM * 8;                 // padded slot run per lane group
   constexpr int META = KT * NG * 16;         // (scale, zero) words per macro tile
   constexpr int META_PER_LANE = (META + 63) / 64;
+  using KG = KeyGroupOps<DK, KW, NV, KM, G>;
+  constexpr int NA = KG::kTab.n;             // key A operands (group, operand) kept
 
   __shared__ float qf[kMqR][kD];
-  __shared__ h8 aq_lds[NS][KM][64];          // key A operand per sub-group, lane order
+  __shared__ h8 aq_lds[NA][64];              // key A operands, lane order
   __shared__ uint32_t km_lds[META_PER_LANE * 64];   // key (scale, zero) of the macro tile
   __shared__ __attribute__((aligned(16))) _Float16 pw_lds[2][kMqR][4 * VK];  // 2^6 p, operand order
   __shared__ float al_lds[2][kMqR];          // rescale factor per row
@@ -105,10 +171,12 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
     for (int g = 0; g < NG; ++g) { vs_lds[g][i] = (_Float16)0.0f; vz_lds[g][i] = (_Float16)0.0f; }
   }
   __syncthreads();
-  // key A operands: lane (row n, k-block jl) of sub-group sg holds the query
-  // of row n at the channels its operand positions carry, zero elsewhere
-  for (int e = threadIdx.x; e < NS * KM * 64; e += 128) {
-    const int sg = e / (KM * 64), mo = (e / 64) % KM, l = e % 64;
+  // key A operands: lane (row n, k-block jl) of operand (g, mo) holds the
+  // query of row n at the channels of group g its operand positions carry,
+  // zero elsewhere
+  for (int e = threadIdx.x; e < NA * 64; e += 128) {
+    const int ai = e / 64, l = e % 64;
+    const int gq = KG::kTab.g_of[ai], mo = KG::kTab.mo_of[ai];
     const int rn = l & 15, jl = l >> 4;
     const int nw = (KW - jl + 3) / 4;        // words lane group jl owns
     h8 v;
@@ -117,10 +185,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
       const int t = 8 * mo + i;
       const int wi = DK::word_of(t);
       const int d = (jl + 4 * wi) * NV + DK::digit_of(t);
-      const bool ok = wi >= 0 && wi < nw && d < kD && (d >> 5) == sg;
+      const bool ok = wi >= 0 && wi < nw && d < kD && d / G == gq;
       v[i] = (_Float16)(ok ? qf[rn][min(max(d, 0), kD - 1)] : 0.0f);   // q is fp16: exact
     }
-    aq_lds[sg][mo][l] = v;
+    aq_lds[ai][l] = v;
   }
   __syncthreads();
 
@@ -152,27 +220,25 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
     };
     KBuf nxt;
     load_k(nxt, s_begin);
-    float qc[NS][kGqa];                      // c * sum over sub-group sg of row (j, h)
+    float qc[NG][kGqa];                      // c * sum over group g of row (j, h)
 #pragma unroll
-    for (int sg = 0; sg < NS; ++sg)
+    for (int g = 0; g < NG; ++g)
 #pragma unroll
       for (int h = 0; h < kGqa; ++h) {
         float sum = 0.f;
 #pragma unroll
-        for (int d = 0; d < 32; ++d) sum += qf[4 * j + h][32 * sg + d];
-        qc[sg][h] = sum * a.c;
+        for (int d = 0; d < G; ++d) sum += qf[4 * j + h][G * g + d];
+        qc[g][h] = sum * a.c;
       }
     int spos[KT];
 #pragma unroll
     for (int t = 0; t < KT; ++t) spos[t] = ppos_lds[16 * t + n];
     // the A operands stay in registers when they fit beside the rest
-    constexpr bool kAqRegs = KM <= 5;
-    h8 aqr[kAqRegs ? NS : 1][kAqRegs ? KM : 1];
+    constexpr bool kAqRegs = NA <= kMqAqRegsMax;
+    h8 aqr[kAqRegs ? NA : 1];
     if (kAqRegs)
 #pragma unroll
-      for (int sg = 0; sg < NS; ++sg)
-#pragma unroll
-        for (int mo = 0; mo < KM; ++mo) aqr[kAqRegs ? sg : 0][kAqRegs ? mo : 0] = aq_lds[sg][mo][lane];
+      for (int ai = 0; ai < NA; ++ai) aqr[kAqRegs ? ai : 0] = aq_lds[ai][lane];
     float m_run[kGqa], l_run[kGqa];
 #pragma unroll
     for (int h = 0; h < kGqa; ++h) { m_run[h] = -INFINITY; l_run[h] = 0.f; }
@@ -196,19 +262,22 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
           h8 bk[KM];
           DK::run(cur.kw[t], ctab, bk);
           float x[kGqa] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int sg = 0; sg < NS; ++sg) {
+          static_for<0, NG>([&](auto gc) {
+            constexpr int g = decltype(gc)::value;
             f4 pr = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int mo = 0; mo < KM; ++mo)
-              pr = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                  kAqRegs ? aqr[kAqRegs ? sg : 0][kAqRegs ? mo : 0] : aq_lds[sg][mo][lane], bk[mo], pr, 0, 0, 0);
-            const uint32_t meta = km_lds[(t * NG + sg / SUB) * 16 + n];
+            static_for<0, KM>([&](auto mc) {
+              constexpr int mo = decltype(mc)::value;
+              constexpr int ai = KG::kTab.idx[g][mo];
+              if constexpr (ai >= 0)
+                pr = __builtin_amdgcn_mfma_f32_16x16x32_f16(kAqRegs ? aqr[kAqRegs ? ai : 0] : aq_lds[ai][lane],
+                                                            bk[mo], pr, 0, 0, 0);
+            });
+            const uint32_t meta = km_lds[(t * NG + g) * 16 + n];
             const float sgf = h2f(meta & 0xFFFFu) * MUL;
             const float ssc = sgf * a.c, zz = AFF ? h2f(meta >> 16) - sgf : h2f(meta >> 16);
 #pragma unroll
-            for (int h = 0; h < kGqa; ++h) x[h] = __builtin_fmaf(ssc, pr[h], __builtin_fmaf(zz, qc[sg][h], x[h]));
-          }
+            for (int h = 0; h < kGqa; ++h) x[h] = __builtin_fmaf(ssc, pr[h], __builtin_fmaf(zz, qc[g][h], x[h]));
+          });
           const bool ok = s0 + 16 * t + n < s_end;
 #pragma unroll
           for (int h = 0; h < kGqa; ++h) {
