@@ -118,10 +118,24 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(mq_min_wave
   using KG = KeyGroupOps<DK, KW, NV, KM, G>;
   constexpr int NA = KG::kTab.n;             // key A operands (group, operand) kept
 
-  __shared__ float qf[kMqR][kD];
-  __shared__ h8 aq_lds[NA][64];              // key A operands, lane order
+  // the key A operands stay in registers when they fit beside the rest
+  constexpr bool kAqRegs = NA <= kMqAqRegsMax;
+  // The query rows (and the key A operands when they go to registers) are
+  // read only during set-up and the weights only after it, so they share
+  // LDS: this keeps a 5-level workgroup under 40 KB (four per CU).
+  union SetupOrPw {
+    struct {
+      float qf[kMqR][kD];
+      h8 aq[kAqRegs ? NA : 1][64];           // key A operands, lane order
+    } s;
+    _Float16 pw[2][kMqR][4 * VK];            // 2^6 p, operand order
+    uint4 raw[2 * kMqR * 4 * VK * 2 / 16];   // the weights as 16-byte words
+  };
+  __shared__ __attribute__((aligned(16))) SetupOrPw sp;
+  __shared__ h8 aq_keep[kAqRegs ? 1 : NA][64];   // key A operands kept in LDS
+  __shared__ float qcs[NG][kMqR];            // c * sum of row r's query over group g
+  constexpr int kPwBytes = 2 * kMqR * 4 * VK * 2;
   __shared__ uint32_t km_lds[META_PER_LANE * 64];   // key (scale, zero) of the macro tile
-  __shared__ __attribute__((aligned(16))) _Float16 pw_lds[2][kMqR][4 * VK];  // 2^6 p, operand order
   __shared__ float al_lds[2][kMqR];          // rescale factor per row
   __shared__ __attribute__((aligned(16))) _Float16 vs_lds[NG][4 * VK];  // value scale
   __shared__ __attribute__((aligned(16))) _Float16 vz_lds[NG][4 * VK];  // value zero
@@ -153,7 +167,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(mq_min_wave
   for (int i = threadIdx.x; i < kMqR * kD; i += 128) {
     const int r = i / kD, d = i % kD, m = qg * kMqQ + (r >> 2);
     const int src = a.korder ? (int)(a.korder[(size_t)hk * kD + d] & 0x7F) : d;   // stored order
-    qf[r][d] = m < a.M ? h2f(a.q[(((size_t)b * a.M + m) * Hq + hk * kGqa + (r & 3)) * kD + src]) : 0.f;
+    sp.s.qf[r][d] = m < a.M ? h2f(a.q[(((size_t)b * a.M + m) * Hq + hk * kGqa + (r & 3)) * kD + src]) : 0.f;
   }
   for (int sl = threadIdx.x; sl < MT; sl += 128) {
     const int jj = sl / RUN, rem = sl % RUN;
@@ -166,10 +180,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(mq_min_wave
     mpos_lds[e] = jj * VK + DV::pos_of(rem / NV, rem % NV);
   }
   DK::fill(ctab, threadIdx.x, 128);
-  for (int i = threadIdx.x; i < 4 * VK; i += 128) {
-    for (int r = 0; r < kMqR; ++r) { pw_lds[0][r][i] = (_Float16)0.0f; pw_lds[1][r][i] = (_Float16)0.0f; }
+  for (int i = threadIdx.x; i < 4 * VK; i += 128)
     for (int g = 0; g < NG; ++g) { vs_lds[g][i] = (_Float16)0.0f; vz_lds[g][i] = (_Float16)0.0f; }
-  }
   __syncthreads();
   // key A operands: lane (row n, k-block jl) of operand (g, mo) holds the
   // query of row n at the channels of group g its operand positions carry,
@@ -186,9 +198,18 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(mq_min_wave
       const int wi = DK::word_of(t);
       const int d = (jl + 4 * wi) * NV + DK::digit_of(t);
       const bool ok = wi >= 0 && wi < nw && d < kD && d / G == gq;
-      v[i] = (_Float16)(ok ? qf[rn][min(max(d, 0), kD - 1)] : 0.0f);   // q is fp16: exact
+      v[i] = (_Float16)(ok ? sp.s.qf[rn][min(max(d, 0), kD - 1)] : 0.0f);   // q is fp16: exact
     }
-    aq_lds[ai][l] = v;
+    if constexpr (kAqRegs)
+      sp.s.aq[ai][l] = v;
+    else
+      aq_keep[ai][l] = v;
+  }
+  for (int e = threadIdx.x; e < NG * kMqR; e += 128) {
+    const int g = e / kMqR, r = e % kMqR;
+    float sum = 0.f;
+    for (int d = 0; d < G; ++d) sum += sp.s.qf[r][G * g + d];
+    qcs[g][r] = sum * a.c;
   }
   __syncthreads();
 
@@ -224,21 +245,19 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(mq_min_wave
 #pragma unroll
     for (int g = 0; g < NG; ++g)
 #pragma unroll
-      for (int h = 0; h < kGqa; ++h) {
-        float sum = 0.f;
-#pragma unroll
-        for (int d = 0; d < G; ++d) sum += qf[4 * j + h][G * g + d];
-        qc[g][h] = sum * a.c;
-      }
+      for (int h = 0; h < kGqa; ++h) qc[g][h] = qcs[g][4 * j + h];
     int spos[KT];
 #pragma unroll
     for (int t = 0; t < KT; ++t) spos[t] = ppos_lds[16 * t + n];
-    // the A operands stay in registers when they fit beside the rest
-    constexpr bool kAqRegs = NA <= kMqAqRegsMax;
     h8 aqr[kAqRegs ? NA : 1];
     if (kAqRegs)
 #pragma unroll
-      for (int ai = 0; ai < NA; ++ai) aqr[kAqRegs ? ai : 0] = aq_lds[ai][lane];
+      for (int ai = 0; ai < NA; ++ai) aqr[kAqRegs ? ai : 0] = sp.s.aq[kAqRegs ? ai : 0][lane];
+    // set-up data read: clear the weight buffers that share its LDS (operand
+    // positions no slot fills stay zero); the other wave reads them only
+    // after the first macro tile's barrier
+    wave_lds_fence();
+    for (int i = lane; i < kPwBytes / 16; i += 64) sp.raw[i] = make_uint4(0u, 0u, 0u, 0u);
     float m_run[kGqa], l_run[kGqa];
 #pragma unroll
     for (int h = 0; h < kGqa; ++h) { m_run[h] = -INFINITY; l_run[h] = 0.f; }
@@ -262,14 +281,14 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(mq_min_wave
           h8 bk[KM];
           DK::run(cur.kw[t], ctab, bk);
           float x[kGqa] = {0.f, 0.f, 0.f, 0.f};
-          static_for<0, NG>([&](auto gc) {
+          static_for<0, NG>([&](auto gc) __attribute__((always_inline)) {
             constexpr int g = decltype(gc)::value;
             f4 pr = {0.f, 0.f, 0.f, 0.f};
-            static_for<0, KM>([&](auto mc) {
+            static_for<0, KM>([&](auto mc) __attribute__((always_inline)) {
               constexpr int mo = decltype(mc)::value;
               constexpr int ai = KG::kTab.idx[g][mo];
               if constexpr (ai >= 0)
-                pr = __builtin_amdgcn_mfma_f32_16x16x32_f16(kAqRegs ? aqr[kAqRegs ? ai : 0] : aq_lds[ai][lane],
+                pr = __builtin_amdgcn_mfma_f32_16x16x32_f16(kAqRegs ? aqr[kAqRegs ? ai : 0] : aq_keep[kAqRegs ? 0 : ai][lane],
                                                             bk[mo], pr, 0, 0, 0);
             });
             const uint32_t meta = km_lds[(t * NG + g) * 16 + n];
@@ -292,7 +311,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(mq_min_wave
           const float m_new = fmaxf(m_run[h], row_max16(mx[h]));
           const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
           const float alpha = __builtin_amdgcn_exp2f(m_run[h] - m_use);
-          _Float16* pb = &pw_lds[it & 1][4 * j + h][0];
+          _Float16* pb = &sp.pw[it & 1][4 * j + h][0];
           float ls = 0.f;
 #pragma unroll
           for (int t = 0; t < KT; ++t) {
@@ -395,7 +414,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(mq_min_wave
 #pragma unroll
         for (int m = 0; m < VM; ++m) {
           const int pos = j * VK + 8 * m;
-          const h8 p16 = *reinterpret_cast<const h8*>(&pw_lds[i & 1][n][pos]);
+          const h8 p16 = *reinterpret_cast<const h8*>(&sp.pw[i & 1][n][pos]);
 #pragma unroll
           for (int g = 0; g < NG; ++g) {
             const h8 zv = *reinterpret_cast<const h8*>(&vz_lds[g][pos]);
@@ -412,7 +431,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(mq_min_wave
 #pragma unroll
           for (int m = 0; m < VM; ++m) {
             const int pos = j * VK + 8 * m;
-            const h8 p16 = *reinterpret_cast<const h8*>(&pw_lds[i & 1][n][pos]);
+            const h8 p16 = *reinterpret_cast<const h8*>(&sp.pw[i & 1][n][pos]);
             const h8 sv = *reinterpret_cast<const h8*>(&vs_lds[g][pos]);
             av[m] = p16 * sv;                // fp16 products, rounded to nearest
           }
