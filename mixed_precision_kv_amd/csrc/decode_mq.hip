@@ -120,13 +120,13 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(mq_min_wave
 
   // the key A operands stay in registers when they fit beside the rest
   constexpr bool kAqRegs = NA <= kMqAqRegsMax;
-  // The query rows (and the key A operands when they go to registers) are
-  // read only during set-up and the weights only after it, so they share
-  // LDS: this keeps a 5-level workgroup under 40 KB (four per CU).
+  // The query rows are read only during set-up and the weights only after
+  // it, so they share LDS; the key wave builds its A operands in registers
+  // straight from the rows (a 5-level workgroup takes 33 KB, four per CU; a
+  // 6-level one 22 KB, six).
   union SetupOrPw {
     struct {
-      float qf[kMqR][kD];
-      h8 aq[kAqRegs ? NA : 1][64];           // key A operands, lane order
+      _Float16 qh[kMqR][kD];                 // query rows (fp16, as given)
     } s;
     _Float16 pw[2][kMqR][4 * VK];            // 2^6 p, operand order
     uint4 raw[2 * kMqR * 4 * VK * 2 / 16];   // the weights as 16-byte words
@@ -167,7 +167,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(mq_min_wave
   for (int i = threadIdx.x; i < kMqR * kD; i += 128) {
     const int r = i / kD, d = i % kD, m = qg * kMqQ + (r >> 2);
     const int src = a.korder ? (int)(a.korder[(size_t)hk * kD + d] & 0x7F) : d;   // stored order
-    sp.s.qf[r][d] = m < a.M ? h2f(a.q[(((size_t)b * a.M + m) * Hq + hk * kGqa + (r & 3)) * kD + src]) : 0.f;
+    sp.s.qh[r][d] = __builtin_bit_cast(
+        _Float16, (uint16_t)(m < a.M ? a.q[(((size_t)b * a.M + m) * Hq + hk * kGqa + (r & 3)) * kD + src] : 0));
   }
   for (int sl = threadIdx.x; sl < MT; sl += 128) {
     const int jj = sl / RUN, rem = sl % RUN;
@@ -185,7 +186,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(mq_min_wave
   __syncthreads();
   // key A operands: lane (row n, k-block jl) of operand (g, mo) holds the
   // query of row n at the channels of group g its operand positions carry,
-  // zero elsewhere
+  // zero elsewhere (here only when they stay in LDS)
+  if constexpr (!kAqRegs)
   for (int e = threadIdx.x; e < NA * 64; e += 128) {
     const int ai = e / 64, l = e % 64;
     const int gq = KG::kTab.g_of[ai], mo = KG::kTab.mo_of[ai];
@@ -198,17 +200,14 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(mq_min_wave
       const int wi = DK::word_of(t);
       const int d = (jl + 4 * wi) * NV + DK::digit_of(t);
       const bool ok = wi >= 0 && wi < nw && d < kD && d / G == gq;
-      v[i] = (_Float16)(ok ? sp.s.qf[rn][min(max(d, 0), kD - 1)] : 0.0f);   // q is fp16: exact
+      v[i] = ok ? sp.s.qh[rn][min(max(d, 0), kD - 1)] : (_Float16)0.0f;
     }
-    if constexpr (kAqRegs)
-      sp.s.aq[ai][l] = v;
-    else
-      aq_keep[ai][l] = v;
+    aq_keep[ai][l] = v;
   }
   for (int e = threadIdx.x; e < NG * kMqR; e += 128) {
     const int g = e / kMqR, r = e % kMqR;
     float sum = 0.f;
-    for (int d = 0; d < G; ++d) sum += sp.s.qf[r][G * g + d];
+    for (int d = 0; d < G; ++d) sum += (float)sp.s.qh[r][G * g + d];
     qcs[g][r] = sum * a.c;
   }
   __syncthreads();
@@ -250,9 +249,23 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(mq_min_wave
 #pragma unroll
     for (int t = 0; t < KT; ++t) spos[t] = ppos_lds[16 * t + n];
     h8 aqr[kAqRegs ? NA : 1];
-    if (kAqRegs)
+    if constexpr (kAqRegs) {
+      const int nwj = (KW - j + 3) / 4;      // words lane group j owns
+      static_for<0, NA>([&](auto ac) __attribute__((always_inline)) {
+        constexpr int ai = decltype(ac)::value;
+        constexpr int gq = KG::kTab.g_of[ai], mo = KG::kTab.mo_of[ai];
+        h8 v;
 #pragma unroll
-      for (int ai = 0; ai < NA; ++ai) aqr[kAqRegs ? ai : 0] = sp.s.aq[kAqRegs ? ai : 0][lane];
+        for (int i = 0; i < 8; ++i) {
+          const int t = 8 * mo + i;
+          const int wi = DK::word_of(t);
+          const int d = (j + 4 * wi) * NV + DK::digit_of(t);
+          const bool ok = wi >= 0 && wi < nwj && d < kD && d / G == gq;
+          v[i] = ok ? sp.s.qh[n][min(max(d, 0), kD - 1)] : (_Float16)0.0f;
+        }
+        aqr[ai] = v;
+      });
+    }
     // set-up data read: clear the weight buffers that share its LDS (operand
     // positions no slot fills stay zero); the other wave reads them only
     // after the first macro tile's barrier
