@@ -9,14 +9,16 @@
 // one-query decode kernel; the difference is what fills the 16 rows of the
 // matrix instruction: four query tokens x four heads, r = 4 m + h, instead of
 // four 32-channel sub-groups x four heads.  The digits of a key tile are
-// expanded once and multiplied by four A operands (one per sub-group, zero
-// outside it; held in registers where they fit, else read from LDS); the
-// value digits of a channel tile once, against A = p * s of that tile's
-// sub-group.  So the expansion work, the part that bounds one
-// query, is shared by four query tokens.
+// expanded once; each scale group g multiplies them by the A operands (the
+// query at g's channels, zero elsewhere) of just those operand positions
+// that carry a channel of g (a compile-time table), built by the key wave in
+// registers (read from LDS where there are too many); the value digits of a
+// channel tile once, against A = p * s of that tile's sub-group.  So the
+// expansion work, the part that bounds one query, is shared by four query
+// tokens.
 //   keys wave:   lane (n, j) gets rows (j, 0..3) of column n: query j, four
-//                heads, slot n; per sub-group it adds s_g * P + z_g * Q_g
-//                (Q_g = sum of the query over the sub-group) in fp32;
+//                heads, slot n; per group it adds s_g * P + z_g * Q_g
+//                (Q_g = sum of the query over the group) in fp32;
 //                online softmax per row; weights 2^6 p as fp16 into an LDS
 //                double buffer, rescale factors alongside.
 //   values wave: per macro tile A = p * s per sub-group, column-word digits,
@@ -213,6 +215,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(mq_min_wave
   __syncthreads();
 
   if (wave == 0) {
+    // the key chain sets the pace of the pair: it issues first on its SIMD
+    __builtin_amdgcn_s_setprio(3);
     // ================= keys: scores, softmax, weights =================
     const BufRes rK = make_res(a.kwords + (size_t)u * a.tiles * KW * 16, a.tiles * KW * 16 * 4);
     const BufRes rKM = make_res(a.kmeta + (size_t)u * a.tiles * NG * 16, a.tiles * NG * 16 * 4);
