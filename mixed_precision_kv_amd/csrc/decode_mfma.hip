@@ -480,31 +480,42 @@ constexpr int kMaxDevices = 64;
 static std::atomic<int> g_cus[kMaxDevices];
 static std::atomic<int> g_occ[kMaxDevices][9][3];
 
-int decode_pool_chunk(int L, int G, int U, int slots_per_unit) {
-  const int gi = G == 32 ? 0 : G == 64 ? 1 : 2;
-  const int mt = macro_tile_slots(L);
+int device_cu_count() {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
-  const bool cached = dev >= 0 && dev < kMaxDevices && L >= 0 && L <= 8;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  const bool cached = dev >= 0 && dev < kMaxDevices;
   int cus = cached ? g_cus[dev].load(std::memory_order_relaxed) - 1 : -1;
   if (cus < 0) {
     int n = 0;
-    cus = (dev >= 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) ? n : 0;
+    cus = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess ? n : 0;
     if (cached) g_cus[dev].store(cus + 1, std::memory_order_relaxed);
   }
-  int occ = cached ? g_occ[dev][L][gi].load(std::memory_order_relaxed) - 1 : -1;
-  if (occ < 0) {
-    occ = occupancy(L, G);
-    if (cached) g_occ[dev][L][gi].store(occ + 1, std::memory_order_relaxed);
-  }
-  const long waves = (long)cus * occ;
+  return cus;
+}
+
+int chunk_for_one_round(int L, int U, int slots_per_unit, int blocks_per_cu) {
+  const int mt = macro_tile_slots(L);
+  const long waves = (long)device_cu_count() * blocks_per_cu;
   if (waves <= 0 || slots_per_unit <= 0) return 8 * mt;
-  // macro tiles per wave so that U * chunks ~ waves (one round of the chip)
+  // macro tiles per workgroup so that U * chunks ~ the resident workgroups
   const long tiles_per_unit = (slots_per_unit + mt - 1) / mt;
   long m = (tiles_per_unit * U + waves - 1) / waves;
   if (m < 1) m = 1;
   if (m > tiles_per_unit) m = tiles_per_unit;
   return (int)(m * mt);
+}
+
+int decode_pool_chunk(int L, int G, int U, int slots_per_unit) {
+  const int gi = G == 32 ? 0 : G == 64 ? 1 : 2;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  const bool cached = dev >= 0 && dev < kMaxDevices && L >= 0 && L <= 8;
+  int occ = cached ? g_occ[dev][L][gi].load(std::memory_order_relaxed) - 1 : -1;
+  if (occ < 0) {
+    occ = occupancy(L, G);
+    if (cached) g_occ[dev][L][gi].store(occ + 1, std::memory_order_relaxed);
+  }
+  return chunk_for_one_round(L, U, slots_per_unit, occ);
 }
 
 bool launch_decode_pool(int L, const PoolArgs& a, int G, int nch, int U, void* stream) {

@@ -26,6 +26,7 @@
 //                VALU.
 // Partials (m, l, acc) per (unit, query group, chunk, row) are merged by
 // k_merge_mq, which also writes the log-sum-exp.
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -556,6 +557,43 @@ static bool launch_mq_L(const PoolMqArgs& a, int G, int nch, int U, hipStream_t 
   return false;
 }
 
+template <int L>
+static int mq_occupancy_L(int G) {
+  int blocks = 0;
+  hipError_t e = hipErrorInvalidValue;
+  switch (G) {
+    case 32: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_decode_pool_mq<L, 32>, 128, 0); break;
+    case 64: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_decode_pool_mq<L, 64>, 128, 0); break;
+    case 128: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_decode_pool_mq<L, 128>, 128, 0); break;
+  }
+  return e == hipSuccess ? blocks : 0;
+}
+
+// Workgroups per CU of the multi-query pool kernel, cached per device (value
+// + 1; 0: not read yet; threads racing on a first read store the same value).
+constexpr int kMqMaxDevices = 64;
+static std::atomic<int> g_mq_occ[kMqMaxDevices][9][3];
+
+static int mq_occupancy(int L, int G) {
+  const int gi = G == 32 ? 0 : G == 64 ? 1 : 2;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  const bool cached = dev >= 0 && dev < kMqMaxDevices && L >= 0 && L <= 8;
+  int occ = cached ? g_mq_occ[dev][L][gi].load(std::memory_order_relaxed) - 1 : -1;
+  if (occ >= 0) return occ;
+  switch (L) {
+    case 3: occ = mq_occupancy_L<3>(G); break;
+    case 4: occ = mq_occupancy_L<4>(G); break;
+    case 5: occ = mq_occupancy_L<5>(G); break;
+    case 6: occ = mq_occupancy_L<6>(G); break;
+    case 7: occ = mq_occupancy_L<7>(G); break;
+    case 8: occ = mq_occupancy_L<8>(G); break;
+    default: occ = 0;
+  }
+  if (cached) g_mq_occ[dev][L][gi].store(occ + 1, std::memory_order_relaxed);
+  return occ;
+}
+
 static bool launch_mq_pool(int L, const PoolMqArgs& a, int G, int nch, int U, hipStream_t s) {
   switch (L) {
     case 3: return launch_mq_L<3>(a, G, nch, U, s);
@@ -580,7 +618,7 @@ kvq_status launch_decode_mq(const kvq_layout* L, const uint8_t* cache, const voi
   int chunk[2], nchp[2];
   for (int p = 0; p < 2; ++p) {
     const int slots = L->cap[p] < max_len ? L->cap[p] : max_len;
-    chunk[p] = decode_pool_chunk(lv[p], c.group, U * nqg, slots);
+    chunk[p] = chunk_for_one_round(lv[p], U * nqg, slots, mq_occupancy(lv[p], c.group));
     nchp[p] = ceil_div(slots, chunk[p]);
   }
   const int nch_used = nchp[0] + nchp[1];

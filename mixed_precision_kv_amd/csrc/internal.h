@@ -84,6 +84,11 @@ struct PoolArgs {
 // Slots per workgroup for one pool so that the grid fills the chip about once
 // (uses the kernel's occupancy; falls back to 8 macro tiles).
 int decode_pool_chunk(int L, int G, int U, int slots_per_unit);
+// The device's CU count (cached per device).
+int device_cu_count();
+// Slots per chunk (whole macro tiles) so that U units' chunks make about one
+// round of a kernel resident at blocks_per_cu workgroups per CU.
+int chunk_for_one_round(int L, int U, int slots_per_unit, int blocks_per_cu);
 bool launch_decode_pool(int L, const PoolArgs& a, int G, int nch, int U, void* stream);
 // One tier pool of the multi-query kernel: four query tokens per workgroup.
 struct PoolMqArgs {
