@@ -322,21 +322,22 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(mq_min_wave
             mx[h] = fmaxf(mx[h], scs[t][h]);
           }
         }
-        // online softmax of rows (j, h); weights as fp16 2^6 p rounded half up
-        // (as in the one-query kernel)
+        // online softmax of rows (j, h); weights as fp16 2^6 p, formed by one
+        // exp2 with the 2^6 folded into the max and rounded to nearest even
+        // (unbiased, as the one-query kernel's half-up rounding)
 #pragma unroll
         for (int h = 0; h < kGqa; ++h) {
           const float m_new = fmaxf(m_run[h], row_max16(mx[h]));
           const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
           const float alpha = __builtin_amdgcn_exp2f(m_run[h] - m_use);
+          const float m6 = m_use - 6.0f;     // 2^6 p = exp2(s - (m - 6))
           _Float16* pb = &sp.pw[it & 1][4 * j + h][0];
-          float ls = 0.f;
+          float ls = 0.f;                    // in units of 2^-6
 #pragma unroll
           for (int t = 0; t < KT; ++t) {
-            const float p = __builtin_amdgcn_exp2f(scs[t][h] - m_use);
-            ls += p;
-            const float xq = __uint_as_float(__float_as_uint(p * kAScale) + 0x1000u);
-            pb[spos[t]] = __builtin_bit_cast(h2v, __builtin_amdgcn_cvt_pkrtz(xq, xq))[0];
+            const float p6 = __builtin_amdgcn_exp2f(scs[t][h] - m6);
+            ls += p6;
+            pb[spos[t]] = (_Float16)p6;     // round to nearest even
           }
           l_run[h] = __builtin_fmaf(l_run[h], alpha, ls);
           m_run[h] = m_new;
@@ -350,7 +351,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(mq_min_wave
       const float l_tot = row_sum16(l_run[h]);
       if (n == 0) {
         part[(4 * j + h) * kPartF + 0] = m_run[h];
-        part[(4 * j + h) * kPartF + 1] = l_tot;
+        part[(4 * j + h) * kPartF + 1] = l_tot * (1.0f / kAScale);
       }
     }
   } else {
