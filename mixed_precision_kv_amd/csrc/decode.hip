@@ -370,6 +370,48 @@ __global__ __launch_bounds__(THREADS) void k_merge(const float* __restrict__ par
   }
 }
 
+// Many chunks over few units: the same merge with each head's 128 channels
+// split over four workgroups of 256 threads (32 slices x 8 lanes of four
+// channels), so that four times as many CUs share the partial reads.
+__global__ __launch_bounds__(256) void k_merge_q(const float* __restrict__ part, uint16_t* __restrict__ out,
+                                                 int nch_total, int Hkv, float2* __restrict__ stats,
+                                                 const uint8_t* __restrict__ vorder) {
+  constexpr int S = 32;                      // slices
+  __shared__ float smax[S];
+  __shared__ float4 racc[S][8];
+  __shared__ float rl[S];
+  const int u = blockIdx.x, hh = blockIdx.y, cq = blockIdx.z, t = threadIdx.x;
+  const int b = u / Hkv, hk = u % Hkv;
+  const float* pu = part + (size_t)u * nch_total * kGqa * kPartStride + hh * kPartStride;
+  const size_t cs = (size_t)kGqa * kPartStride;
+  const int ql = t & 7, sl = t >> 3, q = 8 * cq + ql;   // q: quad of channels 4q .. 4q + 3
+  float M = -INFINITY, lsum = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  merge_accumulate(pu, cs, sl, S, nch_total, q, M, lsum, o);
+  if (ql == 0) smax[sl] = M;
+  __syncthreads();
+  float Mg = smax[0];
+#pragma unroll
+  for (int k = 1; k < S; ++k) Mg = fmaxf(Mg, smax[k]);
+  const float f = (M == -INFINITY) ? 0.f : exp2f(M - Mg);
+  racc[sl][ql] = make_float4(o.x * f, o.y * f, o.z * f, o.w * f);
+  if (ql == 0) rl[sl] = lsum * f;
+  __syncthreads();
+  if (t < 8) {
+    float4 r = racc[0][t];
+    float l = rl[0];
+#pragma unroll
+    for (int k = 1; k < S; ++k) {
+      const float4 x = racc[k][t];
+      r.x += x.x; r.y += x.y; r.z += x.z; r.w += x.w;
+      l += rl[k];
+    }
+    uint16_t* po = out + ((size_t)b * Hkv * kGqa + hk * kGqa + hh) * kD;
+    if (stats && cq == 0 && t == 0) stats[u * kGqa + hh] = make_float2(Mg, l);   // (max, sum) of the head
+    merge_write(po, vorder ? vorder + (size_t)hk * kD : nullptr, q, r, l);
+  }
+}
+
 // Few chunks per unit: one workgroup of 128 threads per unit; lane (head
 // t / 32, quad t % 32) merges every chunk of its head by itself (one slice,
 // no LDS combine), so a unit costs two waves instead of four workgroups.
@@ -396,7 +438,7 @@ static void launch_merge(const float* part, uint16_t* out, int U, int nch, int H
   else if (nch <= 8 * kMergeBatch)
     k_merge<256><<<dim3(U, kGqa), 256, 0, s>>>(part, out, nch, Hkv, stats, vorder);
   else
-    k_merge<1024><<<dim3(U, kGqa), 1024, 0, s>>>(part, out, nch, Hkv, stats, vorder);
+    k_merge_q<<<dim3(U, kGqa, 4), 256, 0, s>>>(part, out, nch, Hkv, stats, vorder);
 }
 
 // Attention mass of every cached token of sequence b: the softmax weight it
