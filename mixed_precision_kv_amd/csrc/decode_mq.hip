@@ -190,22 +190,23 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(mq_min_wave
   // key A operands: lane (row n, k-block jl) of operand (g, mo) holds the
   // query of row n at the channels of group g its operand positions carry,
   // zero elsewhere (here only when they stay in LDS)
-  if constexpr (!kAqRegs)
-  for (int e = threadIdx.x; e < NA * 64; e += 128) {
-    const int ai = e / 64, l = e % 64;
-    const int gq = KG::kTab.g_of[ai], mo = KG::kTab.mo_of[ai];
-    const int rn = l & 15, jl = l >> 4;
-    const int nw = (KW - jl + 3) / 4;        // words lane group jl owns
-    h8 v;
+  if constexpr (!kAqRegs) {
+    for (int e = threadIdx.x; e < NA * 64; e += 128) {
+      const int ai = e / 64, l = e % 64;
+      const int gq = KG::kTab.g_of[ai], mo = KG::kTab.mo_of[ai];
+      const int rn = l & 15, jl = l >> 4;
+      const int nw = (KW - jl + 3) / 4;        // words lane group jl owns
+      h8 v;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int t = 8 * mo + i;
-      const int wi = DK::word_of(t);
-      const int d = (jl + 4 * wi) * NV + DK::digit_of(t);
-      const bool ok = wi >= 0 && wi < nw && d < kD && d / G == gq;
-      v[i] = ok ? sp.s.qh[rn][min(max(d, 0), kD - 1)] : (_Float16)0.0f;
+      for (int i = 0; i < 8; ++i) {
+        const int t = 8 * mo + i;
+        const int wi = DK::word_of(t);
+        const int d = (jl + 4 * wi) * NV + DK::digit_of(t);
+        const bool ok = wi >= 0 && wi < nw && d < kD && d / G == gq;
+        v[i] = ok ? sp.s.qh[rn][min(max(d, 0), kD - 1)] : (_Float16)0.0f;
+      }
+      aq_keep[ai][l] = v;
     }
-    aq_keep[ai][l] = v;
   }
   for (int e = threadIdx.x; e < NG * kMqR; e += 128) {
     const int g = e / kMqR, r = e % kMqR;
