@@ -486,7 +486,7 @@ size_t decode_ws_used(const kvq_layout* L, int max_len) {
     nch = 0;
     for (int p = 0; p < 2; ++p) {
       const int slots = L->cap[p] < max_len ? L->cap[p] : max_len;
-      nch += ceil_div(slots, decode_pool_chunk(lv[p], c.group, (int)U, slots));
+      nch += ceil_div(slots, decode_pool_chunk(lv[p], c.group, (int)U, slots, L->slot_pos[p] != 0));
     }
   }
   return U * nch * kGqa * kPartStride * 4;
@@ -522,7 +522,7 @@ kvq_status launch_decode(const kvq_layout* L, const uint8_t* cache, const void* 
     int chunk[2], nchp[2];
     for (int p = 0; p < 2; ++p) {
       const int slots = L->cap[p] < max_len ? L->cap[p] : max_len;
-      chunk[p] = decode_pool_chunk(lv[p], c.group, U, slots);
+      chunk[p] = decode_pool_chunk(lv[p], c.group, U, slots, L->slot_pos[p] != 0);
       nchp[p] = ceil_div(slots, chunk[p]);
     }
     const int nch_used = nchp[0] + nchp[1];

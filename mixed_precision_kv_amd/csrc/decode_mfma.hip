@@ -425,20 +425,46 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
   }
 }
 
+// At three waves per SIMD (six workgroups per CU: the 6-level pool with
+// 32-channel groups) the two waves of a workgroup land on two SIMDs so that
+// half the SIMDs hold two key waves and a value wave and half one key wave
+// and two value waves; the key waves of the latter run about 15 % slower and
+// set the launch's end.  This instance therefore takes extra dynamic LDS
+// (unused) up to 38 KB per workgroup, so that four fit a CU: one key and
+// one value wave on every SIMD.  With pre-RoPE keys the rotation needs the
+// third wave, so that instance keeps it.
+constexpr int kFourPerCuLds = 38 * 1024;
+template <int L, int G>
+static size_t pad_lds() {
+  if (!(L == 6 && G == 32)) return 0;
+  static std::atomic<int> pad{-1};
+  int v = pad.load(std::memory_order_relaxed);
+  if (v < 0) {
+    hipFuncAttributes at;
+    v = (hipFuncGetAttributes(&at, reinterpret_cast<const void*>(&k_decode_pool<L, G, false>)) == hipSuccess &&
+         (int)at.sharedSizeBytes < kFourPerCuLds)
+            ? kFourPerCuLds - (int)at.sharedSizeBytes
+            : 0;
+    pad.store(v, std::memory_order_relaxed);
+  }
+  return (size_t)v;
+}
+
 template <int L, int G>
 static void launch_one(const PoolArgs& a, int nch, int U, hipStream_t s) {
   if (a.spos)
     k_decode_pool<L, G, true><<<dim3(nch, U), 128, 0, s>>>(a);
   else
-    k_decode_pool<L, G, false><<<dim3(nch, U), 128, 0, s>>>(a);
+    k_decode_pool<L, G, false><<<dim3(nch, U), 128, pad_lds<L, G>(), s>>>(a);
 }
 
 template <int L, int G>
-static int occupancy_one() {
+static int occupancy_one(bool rope) {
   int blocks = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_decode_pool<L, G, false>, 128, 0) != hipSuccess)
-    return 0;
-  return blocks;
+  const hipError_t e =
+      rope ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_decode_pool<L, G, true>, 128, 0)
+           : hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_decode_pool<L, G, false>, 128, pad_lds<L, G>());
+  return e == hipSuccess ? blocks : 0;
 }
 
 template <int L>
@@ -452,23 +478,23 @@ static bool launch_L(const PoolArgs& a, int G, int nch, int U, hipStream_t s) {
 }
 
 template <int L>
-static int occupancy_L(int G) {
+static int occupancy_L(int G, bool rope) {
   switch (G) {
-    case 32: return occupancy_one<L, 32>();
-    case 64: return occupancy_one<L, 64>();
-    case 128: return occupancy_one<L, 128>();
+    case 32: return occupancy_one<L, 32>(rope);
+    case 64: return occupancy_one<L, 64>(rope);
+    case 128: return occupancy_one<L, 128>(rope);
   }
   return 0;
 }
 
-static int occupancy(int L, int G) {
+static int occupancy(int L, int G, bool rope) {
   switch (L) {
-    case 3: return occupancy_L<3>(G);
-    case 4: return occupancy_L<4>(G);
-    case 5: return occupancy_L<5>(G);
-    case 6: return occupancy_L<6>(G);
-    case 7: return occupancy_L<7>(G);
-    case 8: return occupancy_L<8>(G);
+    case 3: return occupancy_L<3>(G, rope);
+    case 4: return occupancy_L<4>(G, rope);
+    case 5: return occupancy_L<5>(G, rope);
+    case 6: return occupancy_L<6>(G, rope);
+    case 7: return occupancy_L<7>(G, rope);
+    case 8: return occupancy_L<8>(G, rope);
   }
   return 0;
 }
@@ -478,7 +504,7 @@ static int occupancy(int L, int G) {
 // the same value, so relaxed atomics suffice.
 constexpr int kMaxDevices = 64;
 static std::atomic<int> g_cus[kMaxDevices];
-static std::atomic<int> g_occ[kMaxDevices][9][3];
+static std::atomic<int> g_occ[kMaxDevices][9][3][2];
 
 int device_cu_count() {
   int dev = 0;
@@ -505,15 +531,15 @@ int chunk_for_one_round(int L, int U, int slots_per_unit, int blocks_per_cu) {
   return (int)(m * mt);
 }
 
-int decode_pool_chunk(int L, int G, int U, int slots_per_unit) {
+int decode_pool_chunk(int L, int G, int U, int slots_per_unit, bool rope) {
   const int gi = G == 32 ? 0 : G == 64 ? 1 : 2;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = -1;
   const bool cached = dev >= 0 && dev < kMaxDevices && L >= 0 && L <= 8;
-  int occ = cached ? g_occ[dev][L][gi].load(std::memory_order_relaxed) - 1 : -1;
+  int occ = cached ? g_occ[dev][L][gi][rope].load(std::memory_order_relaxed) - 1 : -1;
   if (occ < 0) {
-    occ = occupancy(L, G);
-    if (cached) g_occ[dev][L][gi].store(occ + 1, std::memory_order_relaxed);
+    occ = occupancy(L, G, rope);
+    if (cached) g_occ[dev][L][gi][rope].store(occ + 1, std::memory_order_relaxed);
   }
   return chunk_for_one_round(L, U, slots_per_unit, occ);
 }

@@ -83,7 +83,7 @@ struct PoolArgs {
 };
 // Slots per workgroup for one pool so that the grid fills the chip about once
 // (uses the kernel's occupancy; falls back to 8 macro tiles).
-int decode_pool_chunk(int L, int G, int U, int slots_per_unit);
+int decode_pool_chunk(int L, int G, int U, int slots_per_unit, bool rope = false);
 // The device's CU count (cached per device).
 int device_cu_count();
 // Slots per chunk (whole macro tiles) so that U units' chunks make about one
