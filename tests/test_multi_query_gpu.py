@@ -83,7 +83,8 @@ def test_multi_query_skvq(M):
 
 
 @pytest.mark.parametrize("lh,ll,g,T", [(8, 6, 64, 3001), (4, 3, 128, 1201), (8, 7, 32, 777),
-                                       (7, 5, 64, 1500), (5, 3, 32, 900), (6, 5, 128, 1400)])
+                                       (7, 5, 64, 1500), (5, 3, 32, 900), (6, 5, 128, 1400),
+                                       (8, 4, 32, 700), (7, 3, 128, 900), (4, 3, 64, 800)])
 def test_multi_query_level_pairs(lh, ll, g, T):
     """Every grid 3..8 (table and power-of-two digit paths) and group size."""
     w = synth.W_LLAMA.shrink(name=f"mq_levels_{lh}_{ll}_g{g}", batch=1, kv_heads=2, q_heads=8, tokens=T,
