@@ -476,19 +476,37 @@ __global__ __launch_bounds__(256) void k_token_mass(const int32_t* __restrict__ 
 
 // Partial bytes a decode of sequences of at most max_len tokens writes with
 // the chunk split launch_decode chooses (decode_ws_bytes bounds every split).
+// The tiered decode's split: both pools in one launch of npair chunks per
+// unit (npair > 0), else nchp[p] chunks of chunk[p] slots per pool.
+struct TieredSplit {
+  int npair, chunk[2], nchp[2];
+  int used() const { return npair > 0 ? npair : nchp[0] + nchp[1]; }
+};
+static TieredSplit tiered_split(const kvq_layout* L, int max_len) {
+  const kvq_config& c = L->cfg;
+  const int U = c.batch * c.kv_heads;
+  const int lv[2] = {c.levels_hi, c.levels_lo};
+  int slots[2];
+  for (int p = 0; p < 2; ++p) slots[p] = L->cap[p] < max_len ? L->cap[p] : max_len;
+  TieredSplit t;
+  memset(&t, 0, sizeof(t));
+  // pre-RoPE keys keep one launch per pool (the pair kernel has no rotation)
+  if (!L->slot_pos[0] && !L->slot_pos[1])
+    t.npair = decode_pair_chunks(lv[0], lv[1], c.group, U, slots[0], slots[1]);
+  if (t.npair == 0)
+    for (int p = 0; p < 2; ++p) {
+      t.chunk[p] = decode_pool_chunk(lv[p], c.group, U, slots[p], L->slot_pos[p] != 0);
+      t.nchp[p] = ceil_div(slots[p], t.chunk[p]);
+    }
+  return t;
+}
+
 size_t decode_ws_used(const kvq_layout* L, int max_len) {
   const kvq_config& c = L->cfg;
   const size_t U = (size_t)c.batch * c.kv_heads;
   int nch0, nch1;
   int nch = decode_chunks(L, max_len, &nch0, &nch1);
-  if (c.mode == KVQ_MODE_TIERED) {
-    const int lv[2] = {c.levels_hi, c.levels_lo};
-    nch = 0;
-    for (int p = 0; p < 2; ++p) {
-      const int slots = L->cap[p] < max_len ? L->cap[p] : max_len;
-      nch += ceil_div(slots, decode_pool_chunk(lv[p], c.group, (int)U, slots, L->slot_pos[p] != 0));
-    }
-  }
+  if (c.mode == KVQ_MODE_TIERED) nch = tiered_split(L, max_len).used();
   return U * nch * kGqa * kPartStride * 4;
 }
 
@@ -519,13 +537,8 @@ kvq_status launch_decode(const kvq_layout* L, const uint8_t* cache, const void* 
   a.scale_log2 = scale * kLog2e;
   if (c.mode == KVQ_MODE_TIERED) {
     const int lv[2] = {c.levels_hi, c.levels_lo};
-    int chunk[2], nchp[2];
-    for (int p = 0; p < 2; ++p) {
-      const int slots = L->cap[p] < max_len ? L->cap[p] : max_len;
-      chunk[p] = decode_pool_chunk(lv[p], c.group, U, slots, L->slot_pos[p] != 0);
-      nchp[p] = ceil_div(slots, chunk[p]);
-    }
-    const int nch_used = nchp[0] + nchp[1];
+    const TieredSplit sp = tiered_split(L, max_len);
+    const int nch_used = sp.used();
     if (nch_used > nch) return KVQ_ERR_WORKSPACE;   // the workspace holds the finest split
     // with the token mass: raw scores of both pools, then per-head (max, sum)
     float* raw[2];
@@ -534,8 +547,9 @@ kvq_status launch_decode(const kvq_layout* L, const uint8_t* cache, const void* 
     float2* stats = (float2*)(raw[1] + (size_t)U * kGqa * L->cap[1]);
     const uint8_t* korder = c.reorder ? cache + L->chan_order : nullptr;
     const uint8_t* vorder = c.reorder ? korder + (size_t)c.kv_heads * kD : nullptr;
+    PoolArgs pargs[2];
     for (int p = 0; p < 2; ++p) {
-      PoolArgs pa;
+      PoolArgs& pa = pargs[p];
       pa.counters = a.counters;
       pa.q = a.q;
       pa.part = a.part;
@@ -548,16 +562,19 @@ kvq_status launch_decode(const kvq_layout* L, const uint8_t* cache, const void* 
       pa.tiles = L->tiles[p];
       pa.vrows = L->vrows[p];
       pa.nch_total = nch_used;
-      pa.part_off = p ? nchp[0] : 0;
-      pa.chunk = chunk[p];
+      pa.part_off = sp.npair > 0 ? 0 : p ? sp.nchp[0] : 0;
+      pa.chunk = sp.chunk[p];
       pa.c = a.scale_log2;
       pa.raw = mass ? raw[p] : nullptr;
       pa.cap_p = L->cap[p];
       pa.korder = korder;
       pa.spos = L->slot_pos[p] ? (const int32_t*)(cache + L->slot_pos[p]) : nullptr;
       pa.rope_theta = c.rope_theta;
-      if (nchp[p] > 0 && !launch_decode_pool(lv[p], pa, c.group, nchp[p], U, stream)) return KVQ_ERR_LAUNCH;
+      if (sp.npair == 0 && sp.nchp[p] > 0 && !launch_decode_pool(lv[p], pa, c.group, sp.nchp[p], U, stream))
+        return KVQ_ERR_LAUNCH;
     }
+    if (sp.npair > 0 && !launch_decode_pair(lv[0], lv[1], c.group, pargs[0], pargs[1], sp.npair, U, stream))
+      return KVQ_ERR_LAUNCH;
     launch_merge((const float*)ws, (uint16_t*)out, U, nch_used, c.kv_heads, s, mass ? stats : nullptr,
                  vorder);
     if (mass)

@@ -46,8 +46,34 @@ namespace kvq {
 // theta_i / 2 pi, then the hardware sine and cosine), and hands
 // the rotated key to the matrix cores as fp16 high and low parts against A
 // rows 4h .. 4h + 3 = query head h, so lane (n, j) receives head j's score.
+// Softmax and value sums a workgroup carries from one pool's pass to the
+// next (lane (n, h) of the key wave; the value wave's accumulator rows).
+// The value sums are in units of `mul`, the digit multiplier of the pass
+// that formed them: the output is (acc - asum) mul + zacc.
+struct PassCarry {
+  float m_run, l_run;
+  f4 acc[8];
+  f4 asum;
+  float zacc;
+  float mul;
+};
+
+__device__ __forceinline__ void carry_init(PassCarry& cr, float mul) {
+  cr.m_run = -INFINITY;
+  cr.l_run = 0.f;
+#pragma unroll
+  for (int v = 0; v < 8; ++v) cr.acc[v] = (f4){0.f, 0.f, 0.f, 0.f};
+  cr.asum = (f4){0.f, 0.f, 0.f, 0.f};
+  cr.zacc = 0.f;
+  cr.mul = mul;
+}
+
+// One pool's slots [s_begin, s_end) of unit blockIdx.y (s_begin < s_end),
+// added to the carried softmax and sums.  Every thread of the workgroup
+// calls it; each wave takes its own branch, with the same number of
+// workgroup barriers in both.
 template <int L, int G, bool ROPE>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k_decode_pool(PoolArgs a) {
+__device__ __forceinline__ void pool_pass(const PoolArgs& a, int s_begin, int s_end, PassCarry& cr) {
   using T = Tiling<L>;
   constexpr int NV = T::NV, KW = T::KW, KWL = T::KWL, R = T::R, RUN = T::RUN, MT = T::MT,
                 KT = T::KT;
@@ -69,27 +95,14 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
   __shared__ __attribute__((aligned(16))) _Float16 vz_lds[NG][4 * VK];  // value zero, same order
   __shared__ int ppos_lds[MT];               // slot -> position in that order
   __shared__ int mpos_lds[64 * META_PER_LANE];
-  __shared__ float zred[16];
   __shared__ uint2 ctab[DK::kTableEntries];   // chunk -> four fp16 digits
   __shared__ uint2 rev_lds[ROPE ? kD / 2 : 1];    // theta_i / 2 pi as a 64-bit binary fraction (hi, lo)
   __shared__ __attribute__((aligned(16))) _Float16 kc_lds[ROPE ? 16 : 1][ROPE ? kD + 8 : 1];  // a key tile, channel order
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, j = lane >> 4;    // B/C-operand view: slot/channel n, group j
-  const int c = blockIdx.x, u = blockIdx.y;
+  const int u = blockIdx.y;
   const int b = u / a.Hkv, hk = u % a.Hkv;
-  float* part = a.part + ((size_t)u * a.nch_total + a.part_off + c) * kGqa * kPartF;
-  const int n_valid = a.counters[b * 4 + 1 + a.pool];
-  // the unit's filled slots split evenly over the launch's chunks, in whole
-  // macro tiles (the grid is sized for the pool's capacity, which can exceed
-  // the filled slots by a whole chunk's share)
-  const int span = ((n_valid + MT - 1) / MT + (int)gridDim.x - 1) / (int)gridDim.x * MT;
-  const int s_begin = c * span;
-  const int s_end = min(n_valid, s_begin + span);
-  if (s_begin >= s_end) {
-    for (int i = threadIdx.x; i < kGqa * kPartF; i += 128) part[i] = (i % kPartF == 0) ? -INFINITY : 0.f;
-    return;
-  }
   const int nmt = (s_end - s_begin + MT - 1) / MT;
 
   // ---- shared set-up
@@ -234,7 +247,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
       }
       return pr[0];
     };
-    float m_run = -INFINITY, l_run = 0.f;
+    float m_run = cr.m_run, l_run = cr.l_run;
     for (int it = 0; it <= nmt; ++it) {
       if (it < nmt) {
         const int s0 = s_begin + it * MT;
@@ -298,11 +311,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
       }
       __syncthreads();
     }
-    const float l_tot = row_sum16(l_run);
-    if (n == 0) {
-      part[j * kPartF + 0] = m_run;
-      part[j * kPartF + 1] = l_tot;
-    }
+    cr.m_run = m_run;
+    cr.l_run = l_run;
   } else {
     // ================= values: A = p * s, matrix ops =================
     const BufRes rVM = make_res(a.vmeta + (size_t)u * a.tiles * NG * 16, a.tiles * NG * 16 * 4);
@@ -337,11 +347,20 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
     // A-operand view: lane (r, j) holds row r = (sub-group sg, head h) over
     // the operand positions of lane group j
     const int h = n & 3, g = (n >> 2) / SUB;
-    float zacc = 0.f;                        // 2^6 sum p z (row r)
+    float zacc = cr.zacc;                    // 2^6 sum p z (row r)
     f4 acc[8];
+    f4 asum = cr.asum;                       // power-of-two grids: sum of A per row
+    // sums carried from a pass on another grid: into this grid's units
+    // (both multipliers are powers of two, so the rescale is exact)
+    const float cfac = cr.mul / MUL;
 #pragma unroll
-    for (int v = 0; v < 8; ++v) acc[v] = (f4){0.f, 0.f, 0.f, 0.f};
-    f4 asum = {0.f, 0.f, 0.f, 0.f};          // power-of-two grids: sum of A per row
+    for (int v = 0; v < 8; ++v) {
+      acc[v] = cr.acc[v];
+      if (cfac != 1.0f)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[v][e] = (acc[v][e] - asum[e]) * cfac;
+    }
+    if (cfac != 1.0f) asum = (f4){0.f, 0.f, 0.f, 0.f};
     for (int it = 0; it <= nmt; ++it) {
       if (it >= 1) {
         const int i = it - 1;
@@ -403,26 +422,101 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
       }
       __syncthreads();
     }
-    // partials.  zacc: lanes (r, j) -> sum over j per row r = 4 sg + h.
-    float zs = zacc;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) cr.acc[v] = acc[v];
+    cr.asum = asum;
+    cr.zacc = zacc;
+    cr.mul = MUL;
+  }
+}
+
+// A chunk's partial (m, l, acc) per head from the carried state.
+__device__ __forceinline__ void write_partial(const PoolArgs& a, float* part, const PassCarry& cr) {
+  __shared__ float zred[16];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, j = lane >> 4;
+  if (wave == 0) {
+    const float l_tot = row_sum16(cr.l_run);
+    if (n == 0) {
+      part[j * kPartF + 0] = cr.m_run;
+      part[j * kPartF + 1] = l_tot;
+    }
+  } else {
+    const int b = (int)blockIdx.y / a.Hkv;
+    const bool vbig = (a.counters[b * 4 + 3] & kFlagBigValueScale) != 0;
+    // zacc: lanes (r, j) -> sum over j per row r = 4 sg + h
+    float zs = cr.zacc;
     zs += __shfl_xor(zs, 16);
     zs += __shfl_xor(zs, 32);
     if (lane < 16) zred[lane] = zs;
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
     // acc rows (sg = j, h) hold channels of sub-group j
-    const float vfac = MUL * (vbig ? kBigValueShift : 1.0f);
+    const float vfac = cr.mul * (vbig ? kBigValueShift : 1.0f);
 #pragma unroll
     for (int v = 0; v < 8; ++v) {
       if ((v >> 1) != j) continue;           // channels 16v..16v+15 belong to sub-group v/2
       const int d = 16 * v + n;
 #pragma unroll
       for (int hh = 0; hh < 4; ++hh) {
-        const float t = (acc[v][hh] - (AFF ? asum[hh] : 0.f)) * vfac + zred[4 * j + hh];
+        const float t = (cr.acc[v][hh] - cr.asum[hh]) * vfac + zred[4 * j + hh];
         part[hh * kPartF + 4 + d] = t * (1.0f / kAScale);
       }
     }
   }
+}
+
+__device__ __forceinline__ void write_empty_partial(float* part) {
+  for (int i = threadIdx.x; i < kGqa * kPartF; i += 128) part[i] = (i % kPartF == 0) ? -INFINITY : 0.f;
+}
+
+// Slots [begin, end) of chunk c of gridDim.x over one pool: the unit's filled
+// slots split evenly over the launch's chunks, in whole macro tiles (the grid
+// is sized for the pool's capacity, which can exceed the filled slots by a
+// whole chunk's share).
+template <int L>
+__device__ __forceinline__ int2 chunk_span(const PoolArgs& a, int c) {
+  constexpr int MT = Tiling<L>::MT;
+  const int b = (int)blockIdx.y / a.Hkv;
+  const int n_valid = a.counters[b * 4 + 1 + a.pool];
+  const int span = ((n_valid + MT - 1) / MT + (int)gridDim.x - 1) / (int)gridDim.x * MT;
+  const int s_begin = c * span;
+  return make_int2(s_begin, min(n_valid, s_begin + span));
+}
+
+template <int L, int G, bool ROPE>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k_decode_pool(PoolArgs a) {
+  const int c = blockIdx.x, u = blockIdx.y;
+  float* part = a.part + ((size_t)u * a.nch_total + a.part_off + c) * kGqa * kPartF;
+  const int2 sp = chunk_span<L>(a, c);
+  if (sp.x >= sp.y) {
+    write_empty_partial(part);
+    return;
+  }
+  PassCarry cr;
+  carry_init(cr, (float)Unpack<L, Tiling<L>::KWL>::kMul);
+  pool_pass<L, G, ROPE>(a, sp.x, sp.y, cr);
+  write_partial(a, part, cr);
+}
+
+// Both tier pools of a unit in one launch: chunk c of the launch takes chunk
+// c of each pool's even split, the high pool first, and carries its softmax
+// and value sums into the low pool's pass, so a workgroup does its set-up and
+// its partial once per pool pair and the merge reads one partial per chunk.
+template <int L0, int L1, int G>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k_decode_pair(PoolArgs a0, PoolArgs a1) {
+  const int c = blockIdx.x, u = blockIdx.y;
+  float* part = a0.part + ((size_t)u * a0.nch_total + c) * kGqa * kPartF;
+  const int2 s0 = chunk_span<L0>(a0, c), s1 = chunk_span<L1>(a1, c);
+  if (s0.x >= s0.y && s1.x >= s1.y) {
+    write_empty_partial(part);
+    return;
+  }
+  PassCarry cr;
+  carry_init(cr, (float)Unpack<L0, Tiling<L0>::KWL>::kMul);
+  if (s0.x < s0.y) pool_pass<L0, G, false>(a0, s0.x, s0.y, cr);
+  if (s1.x < s1.y) pool_pass<L1, G, false>(a1, s1.x, s1.y, cr);
+  write_partial(a0, part, cr);
 }
 
 // At three waves per SIMD (six workgroups per CU: the 6-level pool with
@@ -542,6 +636,50 @@ int decode_pool_chunk(int L, int G, int U, int slots_per_unit, bool rope) {
     if (cached) g_occ[dev][L][gi][rope].store(occ + 1, std::memory_order_relaxed);
   }
   return chunk_for_one_round(L, U, slots_per_unit, occ);
+}
+
+// ---- both tier pools in one launch (k_decode_pair) for the level pairs the
+// workloads use; other pairs launch one kernel per pool
+static int pair_index(int L0, int L1, int G) {
+  if (L0 == 6 && L1 == 5 && G == 32) return 0;
+  if (L0 == 8 && L1 == 6 && G == 64) return 1;
+  return -1;
+}
+static std::atomic<int> g_occ_pair[kMaxDevices][2];
+
+int decode_pair_chunks(int L0, int L1, int G, int U, int slots0, int slots1) {
+  const int k = pair_index(L0, L1, G);
+  if (k < 0 || U <= 0) return 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  int occ = cached ? g_occ_pair[dev][k].load(std::memory_order_relaxed) - 1 : -1;
+  if (occ < 0) {
+    int blocks = 0;
+    const hipError_t e = k == 0 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_decode_pair<6, 5, 32>, 128, 0)
+                                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_decode_pair<8, 6, 64>, 128, 0);
+    occ = e == hipSuccess ? blocks : 0;
+    if (cached) g_occ_pair[dev][k].store(occ + 1, std::memory_order_relaxed);
+  }
+  const long resident = (long)device_cu_count() * occ;
+  if (resident <= 0) return 0;
+  // one round of resident workgroups, at most one chunk per macro tile of the
+  // larger pool
+  const long t0 = (slots0 + macro_tile_slots(L0) - 1) / macro_tile_slots(L0);
+  const long t1 = (slots1 + macro_tile_slots(L1) - 1) / macro_tile_slots(L1);
+  long nch = resident / U;
+  if (nch > (t0 > t1 ? t0 : t1)) nch = t0 > t1 ? t0 : t1;
+  return nch < 1 ? 1 : (int)nch;
+}
+
+bool launch_decode_pair(int L0, int L1, int G, const PoolArgs& a0, const PoolArgs& a1, int nch, int U,
+                        void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  switch (pair_index(L0, L1, G)) {
+    case 0: k_decode_pair<6, 5, 32><<<dim3(nch, U), 128, 0, s>>>(a0, a1); return true;
+    case 1: k_decode_pair<8, 6, 64><<<dim3(nch, U), 128, 0, s>>>(a0, a1); return true;
+  }
+  return false;
 }
 
 bool launch_decode_pool(int L, const PoolArgs& a, int G, int nch, int U, void* stream) {

@@ -90,6 +90,12 @@ int device_cu_count();
 // round of a kernel resident at blocks_per_cu workgroups per CU.
 int chunk_for_one_round(int L, int U, int slots_per_unit, int blocks_per_cu);
 bool launch_decode_pool(int L, const PoolArgs& a, int G, int nch, int U, void* stream);
+// Both tier pools in one launch: chunks per unit for a level pair that has a
+// one-launch kernel (0: none, launch one kernel per pool), and the launch
+// (a0.part, a0.nch_total and a0.counters serve both; partial c per chunk).
+int decode_pair_chunks(int L0, int L1, int G, int U, int slots0, int slots1);
+bool launch_decode_pair(int L0, int L1, int G, const PoolArgs& a0, const PoolArgs& a1, int nch, int U,
+                        void* stream);
 // One tier pool of the multi-query kernel: four query tokens per workgroup.
 struct PoolMqArgs {
   const int32_t* counters;
