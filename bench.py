@@ -622,7 +622,7 @@ def main():
     roof = dict(bound="hbm", achieved=round(dec_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=round(dec_gbs / HBM_PEAK_GBS, 4),
                 traffic=measured_traffic("decode", khash, w.name),
-                kernel="kvq_decode_attn (two tier-pool kernels + merge)",
+                kernel="kvq_decode_attn (both tier pools in one kernel + merge)",
                 bytes_per_launch=round(dec_total_bytes / n_dec), launch_ms=round(dec_mean_ms, 5))
     read_gbs = stream_read_gbs(torch, kvq, dev, stream)
     roof["achievable_read_gbs"] = round(read_gbs, 1)
