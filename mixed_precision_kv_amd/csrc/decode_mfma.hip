@@ -49,7 +49,8 @@ namespace kvq {
 // Softmax and value sums a workgroup carries from one pool's pass to the
 // next (lane (n, h) of the key wave; the value wave's accumulator rows).
 // The value sums are in units of `mul`, the digit multiplier of the pass
-// that formed them: the output is (acc - asum) mul + zacc.
+// that formed them: the output row is ((acc - asum) mul + zacc) / 2^6 (times
+// 2^6 again for a sequence flagged for large value scales).
 struct PassCarry {
   float m_run, l_run;
   f4 acc[8];
@@ -501,8 +502,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
 
 // Both tier pools of a unit in one launch: chunk c of the launch takes chunk
 // c of each pool's even split, the high pool first, and carries its softmax
-// and value sums into the low pool's pass, so a workgroup does its set-up and
-// its partial once per pool pair and the merge reads one partial per chunk.
+// and value sums into the low pool's pass, so the workgroup writes one
+// partial for both pools and the merge reads one partial per chunk.  Each
+// pass keeps its own LDS arrays and does its own set-up.
 template <int L0, int L1, int G>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k_decode_pair(PoolArgs a0, PoolArgs a1) {
   const int c = blockIdx.x, u = blockIdx.y;
