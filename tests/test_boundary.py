@@ -131,6 +131,19 @@ def test_quantize_validation(over, status):
     assert e.value.status == status
 
 
+def test_quantize_longest_ranked_sequence():
+    """The rank kernels take sequences of up to 262144 tokens; one more is
+    refused before any launch, whatever the capacity."""
+    lay = kvq.layout_init(_cfg(capacity=262145, cap_hi=0, cap_lo=0))
+    strides = (262145 * 128, 128, 128)
+    with pytest.raises(kvq.KvqError) as e:
+        _quant(lay, T=262145, n_hi=131072, strides=strides)
+    assert e.value.status == 2
+    with pytest.raises(kvq.KvqError) as e:            # the limit itself passes validation
+        _quant(lay, T=262144, n_hi=131072, strides=strides, ws=0)
+    assert e.value.status == 4                        # (stopped at the missing workspace)
+
+
 def test_quantize_capacity_per_pool():
     c = _cfg(capacity=4096, cap_hi=2048, cap_lo=2048)
     lay = kvq.layout_init(c)

@@ -115,6 +115,20 @@ def test_tiered_long_sequences_with_ties(T):
     _check_tiered(w, inp, run)
 
 
+def test_tiered_longest_sequence():
+    """The longest sequence the rank kernels take (262144 tokens: eight
+    groups of eight 4096-token blocks), with long runs of equal scores, at
+    the long-context workload's 8/6 levels and 64-channel groups; every
+    rank, slot, word and scale, and the attention, against the oracle."""
+    w = synth.W_LONG.shrink(name="longest_T262144", batch=1, kv_heads=1, q_heads=4, tokens=262144)
+    log(f"case {w.name}")
+    inp = synth.make_inputs(w)
+    inp.scores[0, ::3] = np.round(inp.scores[0, ::3] * 8) / 8   # tie runs in every block and group
+    run = GpuRun(w, inp)
+    run.quantize()
+    _check_tiered(w, inp, run)
+
+
 def test_tiered_ties_zeros_and_constant_groups():
     """Equal scores (stable order decides), -0/+0 scores, constant groups
     (scale 0), signed zeros in the data."""
