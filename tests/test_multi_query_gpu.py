@@ -70,6 +70,19 @@ def test_multi_query_c2_shape(M):
     _check_multi(w, inp, run, synth.make_queries(w, M))
 
 
+@pytest.mark.parametrize("M", [4096, 4093])
+def test_multi_query_most_queries(M):
+    """The largest block of query tokens the entry point takes (4096, 1024
+    query groups of four) and a ragged last group, over a short two-sequence
+    cache: every row's output and log-sum-exp."""
+    w = synth.W_LLAMA.shrink(name="c2_tiny_mq", batch=2, kv_heads=1, q_heads=4, tokens=613)
+    log(f"case {w.name} M{M}")
+    inp = synth.make_inputs(w)
+    run = GpuRun(w, inp, want_ranks=False)
+    run.quantize()
+    _check_multi(w, inp, run, synth.make_queries(w, M))
+
+
 @pytest.mark.parametrize("M", [1, 6])
 def test_multi_query_skvq(M):
     """Queries gathered through the stored key order, outputs written back
