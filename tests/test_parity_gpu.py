@@ -129,6 +129,18 @@ def test_tiered_longest_sequence():
     _check_tiered(w, inp, run)
 
 
+def test_tiered_many_short_units():
+    """More (sequence, KV head) units than workgroups resident on the chip
+    (256 x 8 = 2048 units of 45 tokens: one chunk per unit, several rounds
+    of workgroups, a one-partial merge), ragged tiers (22 / 23 slots)."""
+    w = synth.W_LLAMA.shrink(name="many_units_T45", batch=256, kv_heads=8, q_heads=32, tokens=45)
+    log(f"case {w.name}")
+    inp = synth.make_inputs(w)
+    run = GpuRun(w, inp)
+    run.quantize()
+    _check_tiered(w, inp, run)
+
+
 def test_tiered_ties_zeros_and_constant_groups():
     """Equal scores (stable order decides), -0/+0 scores, constant groups
     (scale 0), signed zeros in the data."""
