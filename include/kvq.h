@@ -103,11 +103,11 @@ enum { KVQ_OP_QUANTIZE = 0, KVQ_OP_DECODE = 1, KVQ_OP_DECODE_MASS = 2 };
 /* Caller-filled description of one cache (host memory, plain data). */
 typedef struct kvq_config {
   int32_t mode;           /* KVQ_MODE_TIERED or KVQ_MODE_KCHAN */
-  int32_t batch;          /* sequences B >= 1 */
+  int32_t batch;          /* sequences B >= 1; B * kv_heads <= 65536 (else KVQ_ERR_UNSUPPORTED) */
   int32_t kv_heads;       /* Hkv >= 1 */
   int32_t q_heads;        /* Hq = 4 * Hkv */
   int32_t head_dim;       /* D = 128 */
-  int32_t capacity;       /* max tokens per sequence */
+  int32_t capacity;       /* max tokens per sequence, <= 2^24 (else KVQ_ERR_UNSUPPORTED) */
   /* tiered mode */
   int32_t levels_hi;      /* L_hi in [3, 8]: the decode kernels expand digits through */
   int32_t levels_lo;      /* L_lo in [3, 8]   per-level tables (else KVQ_ERR_UNSUPPORTED) */

@@ -70,7 +70,9 @@ extern "C" kvq_status kvq_layout_init(const kvq_config* cfg, kvq_layout* out) {
   if (c.batch < 1 || c.kv_heads < 1 || c.q_heads < 1 || c.head_dim < 1 || c.capacity < 1)
     return KVQ_ERR_ARG;
   if (c.head_dim != kD || c.q_heads != kGqa * c.kv_heads) return KVQ_ERR_UNSUPPORTED;
-  if ((int64_t)c.batch * c.kv_heads > (1 << 20) || c.capacity > (1 << 24)) return KVQ_ERR_UNSUPPORTED;
+  // kernels take the (sequence, KV head) unit as the grid's second dimension,
+  // which holds at most 65536 workgroups
+  if ((int64_t)c.batch * c.kv_heads > 65536 || c.capacity > (1 << 24)) return KVQ_ERR_UNSUPPORTED;
   kvq_layout L;
   memset(&L, 0, sizeof(L));
   L.cfg = c;

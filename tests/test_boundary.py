@@ -131,6 +131,18 @@ def test_quantize_validation(over, status):
     assert e.value.status == status
 
 
+def test_layout_unit_count_limit():
+    """(sequence, KV head) units index the kernels' second grid dimension,
+    which holds 65536 workgroups: one unit more is refused by the layout."""
+    kvq.layout_init(_cfg(batch=65536))
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.layout_init(_cfg(batch=65537))
+    assert e.value.status == 2
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.layout_init(_cfg(batch=16385, kv_heads=4, q_heads=16))
+    assert e.value.status == 2
+
+
 def test_quantize_longest_ranked_sequence():
     """The rank kernels take sequences of up to 262144 tokens; one more is
     refused before any launch, whatever the capacity."""
